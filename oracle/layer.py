@@ -1,0 +1,130 @@
+"""One paged MoE layer and a stack of them, float64.
+
+[PE] "What does Paged Experts actually do?": per step, the routed experts that
+are missing are copied from the pinned host store into slots (least recently
+used out), then the MoE math runs over the slots. [PE] "Can paging change the
+model's outputs?": the paged layer must return what the unpaged layer returns,
+and a paged-in expert must never run with another expert's bytes.
+
+The oracle therefore keeps a CPU copy of the slot store, copies whole records
+into it exactly as the planner says, and computes every expert FROM ITS SLOT,
+so that a planner or copy mistake shows up in the output. ``unpaged_forward``
+computes from the store directly; the two agree bitwise.
+
+Stack reading (no attention, no norm): x_next = bf16_rne(x + moe(x)).
+"""
+import numpy as np
+
+from . import formats
+from .expert import swiglu_expert
+from .lru import SlotTable
+from .router import route
+
+
+def bf16_rne(v):
+    """float64 -> nearest bfloat16 value (ties to even), returned as float64.
+
+    With v = m * 2^e, 0.5 <= |m| < 1, a bfloat16 keeps 8 significant bits, so
+    the result is rint(m * 2^8) * 2^(e-8) with rint rounding half to even.
+    Normal-range inputs only (the hidden states here are O(1)).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def bf16_bits(v):
+    """float64 values that are exact bf16 -> uint16 bit patterns."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+class PagedLayer:
+    """host_store: uint8 [E][stride]. Keeps its own CPU slot store [K][stride]."""
+
+    def __init__(self, host_store, fmt, E, top_k, H, I, K, initial_fill=False, max_cached=48):
+        self.store = np.asarray(host_store, dtype=np.uint8)
+        self.max_cached = max_cached
+        self.fmt, self.E, self.top_k, self.H, self.I, self.K = fmt, E, top_k, H, I, K
+        self.stride = formats.record_stride(fmt, H, I)
+        assert self.store.shape == (E, self.stride)
+        self.table = SlotTable(E, K, initial_fill)
+        self.slots = np.zeros((K, self.stride), dtype=np.uint8)
+        self._cache = {}
+        self.reset()
+
+    def reset(self):
+        self.table.reset()
+        self.slots[:] = 0
+        if self.table.initial_fill:
+            self.slots[:] = self.store[:self.K]
+        self._cache = {}
+
+    def _page_in(self, e, s):
+        self.slots[s] = self.store[e]
+        self._cache.pop(s, None)
+
+    def _slot_weights(self, s):
+        # decoded from the slot's bytes; invalidated on every page-in into s
+        if s not in self._cache:
+            if len(self._cache) >= self.max_cached:
+                self._cache.pop(next(iter(self._cache)))
+            self._cache[s] = formats.decode_record(self.slots[s], self.fmt, self.H, self.I)
+        return self._cache[s]
+
+    def step(self, logits, x):
+        """logits float32 [B,E], x [B,H] (values) -> (out float64 [B,H], ids, w, plan)."""
+        ids, w = route(logits, self.top_k)
+        plan = self.table.plan(ids, on_page_in=None)
+        # replay the page-ins in wave order: a later wave may reuse a slot that
+        # an earlier wave of the same step computed from
+        x = np.asarray(x, dtype=np.float64)
+        B = x.shape[0]
+        out = np.zeros((B, self.H), dtype=np.float64)
+        for wave_i, wave in enumerate(plan.waves):
+            for e, s in wave.misses:
+                self._page_in(e, s)
+            for b in range(B):
+                for j in range(self.top_k):
+                    if plan.wave_of[b, j] != wave_i:
+                        continue
+                    wg, wu, wd = self._slot_weights(int(plan.slot_ids[b, j]))
+                    out[b] += w[b, j] * swiglu_expert(wg, wu, wd, x[b])
+        return out, ids, w, plan
+
+    def unpaged_forward(self, logits, x):
+        """The same layer computed straight from the host store (no slots)."""
+        ids, w = route(logits, self.top_k)
+        x = np.asarray(x, dtype=np.float64)
+        B = x.shape[0]
+        out = np.zeros((B, self.H), dtype=np.float64)
+        # same summation order as step(): by wave, then token, then j. The wave
+        # of each (b, j) only depends on the table, so take it from a dry run.
+        dry = SlotTable(self.E, self.K, self.table.initial_fill)
+        dry.slot_expert, dry.expert_slot = self.table.slot_expert.copy(), self.table.expert_slot.copy()
+        dry.stamp, dry.clock = self.table.stamp.copy(), self.table.clock
+        plan = dry.plan(ids)
+        for wave_i in range(plan.n_waves):
+            for b in range(B):
+                for j in range(self.top_k):
+                    if plan.wave_of[b, j] != wave_i:
+                        continue
+                    wg, wu, wd = formats.decode_record(self.store[ids[b, j]], self.fmt, self.H, self.I)
+                    out[b] += w[b, j] * swiglu_expert(wg, wu, wd, x[b])
+        return out
+
+
+def run_stack(layers, logits_per_layer, x0):
+    """Stack of paged layers: x_{l+1} = bf16_rne(x_l + out_l).
+
+    logits_per_layer: list of float32 [B,E]; x0: values [B,H] (bf16-exact).
+    Returns (x_final, per-layer outputs, per-layer plans).
+    """
+    x = np.asarray(x0, dtype=np.float64)
+    outs, plans = [], []
+    for layer, logits in zip(layers, logits_per_layer):
+        out, _, _, plan = layer.step(logits, x)
+        outs.append(out)
+        plans.append(plan)
+        x = bf16_rne(x + out)
+    return x, outs, plans
