@@ -1,0 +1,724 @@
+// C ABI of libmoepage: layer and plan handles, the plan readback, the copy
+// engine and the wave sequencing around the kernels.
+//
+// [PE] = "Running an MoE Model Larger Than Your VRAM: SGLang Paged Experts, the
+// PCIe Math, and the 4-Request Cliff".
+#include <immintrin.h>
+
+#include <chrono>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+using namespace moepage;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(MOE_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));     \
+  } while (0)
+
+struct TimerRec {
+  hipEvent_t a, b;
+  int cls;
+  double bytes, flops;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+struct moe_layer {
+  int E, k, H, I, K, fmt;
+  RecLayout rl;
+  size_t stride;
+  const uint8_t* host_store;
+  uint8_t* slots;
+  uint8_t* state;
+  hipStream_t compute, copy, route;
+  hipEvent_t ev_fwd_done, ev_copied, ev_routed;
+  bool fwd_recorded, copy_recorded;
+  int initial_fill;
+  moe_stats stats;
+  // sequencing of the current step
+  const moe_plan* cur_plan;
+  int next_page, next_fwd, n_waves;
+  // timing
+  bool timing;
+  std::vector<TimerRec> pending;
+  std::vector<hipEvent_t> pool;
+  moe_timing acc;
+};
+
+struct moe_plan {
+  const moe_layer* layer;
+  int max_tokens, max_pairs;
+  void* dev_block;
+  PlanDev dev;
+  PlanHdr* hdr;       // host pointer
+  PlanHdr* hdr_dev;   // device alias of the same pinned memory
+  int32_t seq;
+  float* h;           // GEMV scratch
+  uint16_t* hb;       // GEMM scratch
+  float* y;           // GEMM scratch
+  int gemv_pairs;     // capacity of h in pairs
+  hipEvent_t ev_consumed;
+  bool consumed_recorded;
+  moe_plan_info info;
+  bool valid;
+};
+
+namespace {
+
+moe_status get_event(moe_layer* L, hipEvent_t* ev) {
+  if (!L->pool.empty()) {
+    *ev = L->pool.back();
+    L->pool.pop_back();
+    return MOE_OK;
+  }
+  HIP_TRY(hipEventCreate(ev));
+  return MOE_OK;
+}
+
+moe_status timer_begin(moe_layer* L, hipStream_t s, TimerRec* t) {
+  if (!L->timing) return MOE_OK;
+  moe_status st = get_event(L, &t->a);
+  if (st) return st;
+  st = get_event(L, &t->b);
+  if (st) return st;
+  HIP_TRY(hipEventRecord(t->a, s));
+  return MOE_OK;
+}
+
+moe_status timer_end(moe_layer* L, hipStream_t s, TimerRec* t, int cls, double bytes,
+                     double flops) {
+  if (!L->timing) return MOE_OK;
+  HIP_TRY(hipEventRecord(t->b, s));
+  t->cls = cls;
+  t->bytes = bytes;
+  t->flops = flops;
+  L->pending.push_back(*t);
+  return MOE_OK;
+}
+
+void init_state_host(const moe_layer* L, std::vector<uint8_t>& buf) {
+  const StateLayout sl = state_layout(L->E, L->K);
+  buf.assign(sl.total, 0);
+  int32_t* se = (int32_t*)(buf.data() + sl.slot_expert);
+  int32_t* es = (int32_t*)(buf.data() + sl.expert_slot);
+  int64_t* st = (int64_t*)(buf.data() + sl.stamp);
+  int64_t* clk = (int64_t*)(buf.data() + sl.clock);
+  for (int e = 0; e < L->E; ++e) es[e] = -1;
+  for (int s = 0; s < L->K; ++s) {
+    se[s] = L->initial_fill ? s : -1;
+    st[s] = L->initial_fill ? 0 : -1;
+    if (L->initial_fill) es[s] = s;
+  }
+  *clk = 0;
+}
+
+moe_status restore_initial(moe_layer* L) {
+  std::vector<uint8_t> buf;
+  init_state_host(L, buf);
+  HIP_TRY(hipMemcpy(L->state, buf.data(), buf.size(), hipMemcpyHostToDevice));
+  if (L->initial_fill)
+    HIP_TRY(hipMemcpy(L->slots, L->host_store, (size_t)L->K * L->stride, hipMemcpyHostToDevice));
+  L->cur_plan = nullptr;
+  L->next_page = L->next_fwd = L->n_waves = 0;
+  return MOE_OK;
+}
+
+bool is_pinned(const void* p) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+
+// Weight bytes of the gate/up and the down part of one record.
+double up_weight_bytes(const moe_layer* L) {
+  const RecLayout& r = L->rl;
+  double b = (double)(r.wd - r.w13);
+  if (L->fmt == MOE_FMT_FP8_E4M3_B128) b += (double)(r.sd - r.s13);
+  if (L->fmt == MOE_FMT_INT4_ASYM_G128) b += (double)(r.sd - r.s13) + (double)(r.zd - r.z13);
+  return b;
+}
+double down_weight_bytes(const moe_layer* L) {
+  const RecLayout& r = L->rl;
+  double b = (double)(r.s13 - r.wd);
+  if (L->fmt == MOE_FMT_FP8_E4M3_B128) b += (double)(r.payload - r.sd);
+  if (L->fmt == MOE_FMT_INT4_ASYM_G128) b += (double)(r.z13 - r.sd) + (double)(r.payload - r.zd);
+  return b;
+}
+
+moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, float* y,
+                   int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out, int accumulate,
+                   const int32_t* wave_of, int wave, int max_rows);
+
+moe_status self_check(moe_layer* L);
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+size_t moe_record_bytes(int32_t format, int32_t hidden, int32_t intermediate) {
+  if (format < MOE_FMT_F32 || format > MOE_FMT_INT4_ASYM_G128) return 0;
+  if (hidden <= 0 || intermediate <= 0) return 0;
+  if (!ffn_shape_supported(format, hidden, intermediate)) return 0;
+  return rec_layout(format, hidden, intermediate).stride;
+}
+
+size_t moe_state_bytes(int32_t num_experts, int32_t num_slots) {
+  if (num_experts <= 0 || num_slots <= 0) return 0;
+  return state_layout(num_experts, num_slots).total;
+}
+
+void* moe_host_alloc(size_t bytes) {
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    g_err = std::string("hipHostMalloc: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  return p;
+}
+
+void moe_host_free(void* p) {
+  if (p) (void)hipHostFree(p);
+}
+
+moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* copy_stream,
+                          void* route_stream, moe_layer** out) {
+  if (!d || !out) return fail(MOE_ERR_INVALID_ARG, "null descriptor or output");
+  *out = nullptr;
+  if (d->num_experts < 1 || d->num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts must be in 1..1024");
+  if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > MOE_MAX_TOP_K)
+    return fail(MOE_ERR_INVALID_ARG, "top_k must be in 1..min(E, 32)");
+  if (d->num_slots < 1 || d->num_slots > d->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "num_slots K must be in 1..E");
+  if (d->format < MOE_FMT_F32 || d->format > MOE_FMT_INT4_ASYM_G128)
+    return fail(MOE_ERR_FORMAT, "unknown expert format");
+  if (!ffn_shape_supported(d->format, d->hidden, d->intermediate))
+    return fail(MOE_ERR_FORMAT, "hidden/intermediate not supported for this format");
+  const RecLayout rl = rec_layout(d->format, d->hidden, d->intermediate);
+  if (d->record_bytes != rl.stride)
+    return fail(MOE_ERR_FORMAT, "record_bytes does not match the format's record stride (" +
+                                    std::to_string(rl.stride) + ")");
+  if (!d->host_store || !d->slot_store || !d->state)
+    return fail(MOE_ERR_INVALID_ARG, "null host_store, slot_store or state");
+  if (((uintptr_t)d->slot_store & 255) || ((uintptr_t)d->state & 7))
+    return fail(MOE_ERR_INVALID_ARG, "slot_store must be 256-byte and state 8-byte aligned");
+  const uint8_t* hs = (const uint8_t*)d->host_store;
+  if (!is_pinned(hs) || !is_pinned(hs + (size_t)d->num_experts * rl.stride - 1))
+    return fail(MOE_ERR_NOT_PINNED, "host_store is not page-locked host memory over its whole range");
+
+  moe_layer* L = new (std::nothrow) moe_layer();
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  L->E = d->num_experts;
+  L->k = d->top_k;
+  L->H = d->hidden;
+  L->I = d->intermediate;
+  L->K = d->num_slots;
+  L->fmt = d->format;
+  L->rl = rl;
+  L->stride = rl.stride;
+  L->host_store = hs;
+  L->slots = (uint8_t*)d->slot_store;
+  L->state = (uint8_t*)d->state;
+  L->compute = (hipStream_t)compute_stream;
+  L->copy = (hipStream_t)copy_stream;
+  L->route = (hipStream_t)route_stream;
+  L->initial_fill = d->initial_fill ? 1 : 0;
+  L->fwd_recorded = L->copy_recorded = false;
+  std::memset(&L->stats, 0, sizeof(L->stats));
+  std::memset(&L->acc, 0, sizeof(L->acc));
+  L->timing = false;
+  moe_status st = MOE_OK;
+  auto bail = [&](moe_status s) {
+    moe_layer_destroy(L);
+    return s;
+  };
+  if (hipEventCreateWithFlags(&L->ev_fwd_done, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->ev_copied, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->ev_routed, hipEventDisableTiming) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "hipEventCreate failed"));
+  if (d->self_check) {
+    st = self_check(L);
+    if (st) return bail(st);
+  }
+  st = restore_initial(L);
+  if (st) return bail(st);
+  *out = L;
+  return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer* L) {
+  if (!L) return;
+  (void)hipStreamSynchronize(L->compute);
+  (void)hipStreamSynchronize(L->copy);
+  (void)hipStreamSynchronize(L->route);
+  if (L->ev_fwd_done) (void)hipEventDestroy(L->ev_fwd_done);
+  if (L->ev_copied) (void)hipEventDestroy(L->ev_copied);
+  if (L->ev_routed) (void)hipEventDestroy(L->ev_routed);
+  for (auto& t : L->pending) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  for (auto e : L->pool) (void)hipEventDestroy(e);
+  delete L;
+}
+
+moe_status moe_layer_reset(moe_layer* L) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer");
+  HIP_TRY(hipStreamSynchronize(L->compute));
+  HIP_TRY(hipStreamSynchronize(L->copy));
+  HIP_TRY(hipStreamSynchronize(L->route));
+  return restore_initial(L);
+}
+
+moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** out) {
+  if (!L || !out) return fail(MOE_ERR_INVALID_ARG, "null layer or output");
+  *out = nullptr;
+  if (max_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "max_tokens must be >= 1");
+  const bool gemm = max_tokens > MOE_MAX_GEMV_TOKENS;
+  if (gemm && (L->fmt != MOE_FMT_BF16 || !gemm_shape_supported(L->H, L->I)))
+    return fail(MOE_ERR_INVALID_ARG,
+                "more than 64 tokens per forward needs a bf16 layer with H and I multiples of 128");
+  moe_plan* p = new (std::nothrow) moe_plan();
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  std::memset(p, 0, sizeof(*p));
+  p->layer = L;
+  p->max_tokens = max_tokens;
+  p->max_pairs = max_tokens * L->k;
+  const size_t P = (size_t)p->max_pairs, E = (size_t)L->E;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_ids = take(4 * P), o_w = take(4 * P), o_sid = take(4 * P), o_wo = take(4 * P),
+               o_oe = take(4 * E), o_os = take(4 * E), o_po = take(4 * (E + 1)),
+               o_pl = take(4 * P), o_cnt = take(16);
+  p->gemv_pairs = (int)std::min<size_t>(P, (size_t)MOE_MAX_GEMV_TOKENS * L->k);
+  const size_t o_h = take(sizeof(float) * (size_t)p->gemv_pairs * L->I);
+  size_t o_hb = 0, o_y = 0;
+  if (gemm) {
+    o_hb = take(2 * P * L->I);
+    o_y = take(4 * P * L->H);
+  }
+  auto cleanup = [&](moe_status s) {
+    moe_plan_destroy(p);
+    return s;
+  };
+  if (hipMalloc(&p->dev_block, off) != hipSuccess) return cleanup(fail(MOE_ERR_HIP, "hipMalloc plan"));
+  uint8_t* b = (uint8_t*)p->dev_block;
+  p->dev.ids = (int32_t*)(b + o_ids);
+  p->dev.weights = (float*)(b + o_w);
+  p->dev.slot_ids = (int32_t*)(b + o_sid);
+  p->dev.wave_of = (int32_t*)(b + o_wo);
+  p->dev.order_expert = (int32_t*)(b + o_oe);
+  p->dev.order_slot = (int32_t*)(b + o_os);
+  p->dev.pair_off = (int32_t*)(b + o_po);
+  p->dev.pair_list = (int32_t*)(b + o_pl);
+  p->dev.counts = (int32_t*)(b + o_cnt);
+  p->h = (float*)(b + o_h);
+  p->hb = gemm ? (uint16_t*)(b + o_hb) : nullptr;
+  p->y = gemm ? (float*)(b + o_y) : nullptr;
+  const size_t hbytes = sizeof(PlanHdr) + 2 * sizeof(int32_t) * E;
+  if (hipHostMalloc((void**)&p->hdr, hbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
+    return cleanup(fail(MOE_ERR_HIP, "hipHostMalloc plan header"));
+  std::memset(p->hdr, 0, hbytes);
+  if (hipHostGetDevicePointer((void**)&p->hdr_dev, p->hdr, 0) != hipSuccess)
+    return cleanup(fail(MOE_ERR_HIP, "hipHostGetDevicePointer"));
+  if (hipEventCreateWithFlags(&p->ev_consumed, hipEventDisableTiming) != hipSuccess)
+    return cleanup(fail(MOE_ERR_HIP, "hipEventCreate"));
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan* p) {
+  if (!p) return;
+  if (p->consumed_recorded) (void)hipEventSynchronize(p->ev_consumed);
+  if (p->ev_consumed) (void)hipEventDestroy(p->ev_consumed);
+  if (p->dev_block) (void)hipFree(p->dev_block);
+  if (p->hdr) (void)hipHostFree(p->hdr);
+  delete p;
+}
+
+moe_status moe_route(moe_layer* L, const float* logits, int32_t T, moe_plan* p) {
+  if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
+  if (p->layer != L) return fail(MOE_ERR_INVALID_ARG, "plan was created for another layer");
+  if (T < 0 || T > p->max_tokens) return fail(MOE_ERR_INVALID_ARG, "num_tokens out of 0..max_tokens");
+  if (T > 0 && !logits) return fail(MOE_ERR_INVALID_ARG, "null logits");
+  if (L->cur_plan && L->next_fwd < L->n_waves)
+    return fail(MOE_ERR_STATE, "previous step of this layer has waves not yet forwarded");
+  if (p->consumed_recorded) HIP_TRY(hipStreamWaitEvent(L->route, p->ev_consumed, 0));
+  TimerRec tr{};
+  moe_status st = timer_begin(L, L->route, &tr);
+  if (st) return st;
+  HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, L->route));
+  const int32_t seq = ++p->seq;
+  HIP_TRY(launch_plan(p->dev.ids, T, L->k, L->E, L->K, L->state, p->dev, p->hdr_dev, seq, L->route));
+  HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, L->route));
+  st = timer_end(L, L->route, &tr, MOE_T_ROUTE, 0.0, 0.0);
+  if (st) return st;
+  HIP_TRY(hipEventRecord(L->ev_routed, L->route));
+  // The one host synchronisation of a layer-step: wait until the slot-plan
+  // kernel has published the plan into pinned host memory.
+  volatile int32_t* flag = &p->hdr->seq;
+  auto t0 = std::chrono::steady_clock::now();
+  long spins = 0;
+  while (__atomic_load_n(flag, __ATOMIC_ACQUIRE) != seq) {
+    _mm_pause();
+    if (++spins % 4096 == 0) {
+      hipError_t q = hipStreamQuery(L->route);
+      if (q != hipSuccess && q != hipErrorNotReady)
+        return fail(MOE_ERR_HIP, std::string("route kernels failed: ") + hipGetErrorString(q));
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60))
+        return fail(MOE_ERR_TIMEOUT, "slot plan did not become host-visible within 60 s");
+      if (spins > (1L << 20)) std::this_thread::yield();
+    }
+  }
+  const PlanHdr& h = *p->hdr;
+  p->info.num_tokens = h.num_tokens;
+  p->info.num_distinct = h.num_distinct;
+  p->info.num_hits = h.num_hits;
+  p->info.num_misses = h.num_distinct - h.num_hits;
+  p->info.num_waves = h.num_waves;
+  p->valid = true;
+  if (T > 0) {
+    L->stats.steps += 1;
+    L->stats.refs += h.num_distinct;
+    L->stats.activations += (int64_t)T * L->k;
+    L->stats.hits += h.num_hits;
+    L->stats.misses += h.num_distinct - h.num_hits;
+    L->stats.waves += h.num_waves;
+    L->stats.bytes_paged += (int64_t)(h.num_distinct - h.num_hits) * (int64_t)L->stride;
+  }
+  L->n_waves = h.num_waves;
+  L->next_page = L->next_fwd = 0;
+  L->cur_plan = h.num_waves > 0 ? p : nullptr;
+  return MOE_OK;
+}
+
+moe_status moe_plan_get_info(const moe_plan* p, moe_plan_info* out) {
+  if (!p || !out) return fail(MOE_ERR_INVALID_ARG, "null plan or output");
+  if (!p->valid) return fail(MOE_ERR_STATE, "plan has not been routed");
+  *out = p->info;
+  return MOE_OK;
+}
+
+moe_status moe_plan_get_wave(const moe_plan* p, int32_t w, moe_wave_info* out) {
+  if (!p || !out) return fail(MOE_ERR_INVALID_ARG, "null plan or output");
+  if (!p->valid) return fail(MOE_ERR_STATE, "plan has not been routed");
+  if (w < 0 || w >= p->info.num_waves) return fail(MOE_ERR_INVALID_ARG, "wave out of range");
+  const int K = p->layer->K, D = p->info.num_distinct, nH = p->info.num_hits;
+  const int lo = w * K, hi = std::min(lo + K, D), mlo = std::max(lo, nH);
+  const int32_t* oe = (const int32_t*)(p->hdr + 1);
+  const int32_t* os = oe + p->layer->E;
+  out->num_experts = hi - lo;
+  out->num_misses = hi - mlo;
+  out->experts = oe + lo;
+  out->slots = os + lo;
+  out->miss_experts = oe + mlo;
+  out->miss_slots = os + mlo;
+  return MOE_OK;
+}
+
+moe_status moe_plan_read(const moe_plan* p, int32_t* ids, float* weights, int32_t* slot_ids,
+                         int32_t* wave_of) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "null plan");
+  if (!p->valid) return fail(MOE_ERR_STATE, "plan has not been routed");
+  const moe_layer* L = p->layer;
+  HIP_TRY(hipStreamSynchronize(L->route));
+  const size_t n = (size_t)p->info.num_tokens * L->k;
+  if (n == 0) return MOE_OK;
+  if (ids) HIP_TRY(hipMemcpy(ids, p->dev.ids, 4 * n, hipMemcpyDeviceToHost));
+  if (weights) HIP_TRY(hipMemcpy(weights, p->dev.weights, 4 * n, hipMemcpyDeviceToHost));
+  if (slot_ids) HIP_TRY(hipMemcpy(slot_ids, p->dev.slot_ids, 4 * n, hipMemcpyDeviceToHost));
+  if (wave_of) HIP_TRY(hipMemcpy(wave_of, p->dev.wave_of, 4 * n, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
+moe_status moe_page_in(moe_layer* L, const moe_plan* p, int32_t w) {
+  if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
+  if (L->cur_plan != p) return fail(MOE_ERR_STATE, "plan is not this layer's current step");
+  if (w != L->next_page || w != L->next_fwd)
+    return fail(MOE_ERR_STATE, "waves must be paged in in order, each after the previous forward");
+  moe_wave_info wi;
+  moe_status st = moe_plan_get_wave(p, w, &wi);
+  if (st) return st;
+  // a victim slot may still be read by the previous forward of this layer
+  if (L->fwd_recorded) HIP_TRY(hipStreamWaitEvent(L->copy, L->ev_fwd_done, 0));
+  TimerRec tr{};
+  st = timer_begin(L, L->copy, &tr);
+  if (st) return st;
+  for (int i = 0; i < wi.num_misses; ++i) {
+    const int e = wi.miss_experts[i], s = wi.miss_slots[i];
+    if (e < 0 || e >= L->E || s < 0 || s >= L->K)
+      return fail(MOE_ERR_STATE, "corrupt miss list");
+    HIP_TRY(hipMemcpyAsync(L->slots + (size_t)s * L->stride, L->host_store + (size_t)e * L->stride,
+                           L->stride, hipMemcpyHostToDevice, L->copy));
+  }
+  st = timer_end(L, L->copy, &tr, MOE_T_PAGE_IN, (double)wi.num_misses * L->stride, 0.0);
+  if (st) return st;
+  HIP_TRY(hipEventRecord(L->ev_copied, L->copy));
+  L->copy_recorded = true;
+  L->next_page = w + 1;
+  return MOE_OK;
+}
+
+moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out) {
+  if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
+  if (L->cur_plan != p) return fail(MOE_ERR_STATE, "plan is not this layer's current step");
+  if (w != L->next_fwd || L->next_page != w + 1)
+    return fail(MOE_ERR_STATE, "forward(w) must follow page_in(w)");
+  const int T = p->info.num_tokens;
+  if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "null x or out");
+  if (((uintptr_t)x & 15) || ((uintptr_t)out & 15))
+    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_routed, 0));
+  if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
+  const int K = L->K, D = p->info.num_distinct;
+  const int o_lo = w * K, n_exp = std::min(K, D - o_lo);
+  moe_plan* pm = const_cast<moe_plan*>(p);
+  moe_status st = run_ffn(L, p->dev, p->h, p->hb, p->y, o_lo, n_exp, T * L->k, T, x, out, w > 0,
+                          p->dev.wave_of, w, T);
+  if (st) return st;
+  HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
+  L->fwd_recorded = true;
+  HIP_TRY(hipEventRecord(pm->ev_consumed, L->compute));
+  pm->consumed_recorded = true;
+  L->next_fwd = w + 1;
+  if (L->next_fwd == L->n_waves) L->cur_plan = nullptr;
+  return MOE_OK;
+}
+
+moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out, int64_t n,
+                             void* stream) {
+  if (n < 0 || (n > 0 && (!x_in || !out || !x_out)))
+    return fail(MOE_ERR_INVALID_ARG, "bad residual arguments");
+  if (((uintptr_t)x_in & 7) || ((uintptr_t)x_out & 7) || ((uintptr_t)out & 15))
+    return fail(MOE_ERR_INVALID_ARG, "x must be 8-byte and out 16-byte aligned");
+  HIP_TRY(launch_residual((const uint16_t*)x_in, out, (uint16_t*)x_out, n, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_layer_stats(const moe_layer* L, moe_stats* out) {
+  if (!L || !out) return fail(MOE_ERR_INVALID_ARG, "null layer or output");
+  *out = L->stats;
+  return MOE_OK;
+}
+
+moe_status moe_layer_get_state(moe_layer* L, int32_t* slot_expert, int32_t* expert_slot,
+                               int64_t* stamp, int64_t* clock) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer");
+  HIP_TRY(hipStreamSynchronize(L->route));
+  const StateLayout sl = state_layout(L->E, L->K);
+  std::vector<uint8_t> buf(sl.total);
+  HIP_TRY(hipMemcpy(buf.data(), L->state, sl.total, hipMemcpyDeviceToHost));
+  if (slot_expert) std::memcpy(slot_expert, buf.data() + sl.slot_expert, 4 * (size_t)L->K);
+  if (expert_slot) std::memcpy(expert_slot, buf.data() + sl.expert_slot, 4 * (size_t)L->E);
+  if (stamp) std::memcpy(stamp, buf.data() + sl.stamp, 8 * (size_t)L->K);
+  if (clock) std::memcpy(clock, buf.data() + sl.clock, 8);
+  return MOE_OK;
+}
+
+moe_status moe_timing_enable(moe_layer* L, int32_t enable) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer");
+  L->timing = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(moe_layer* L, moe_timing* out) {
+  if (!L || !out) return fail(MOE_ERR_INVALID_ARG, "null layer or output");
+  for (auto& t : L->pending) {
+    HIP_TRY(hipEventSynchronize(t.b));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, t.a, t.b));
+    L->acc.count[t.cls] += 1;
+    L->acc.ms[t.cls] += ms;
+    L->acc.bytes[t.cls] += t.bytes;
+    L->acc.flops[t.cls] += t.flops;
+    L->pool.push_back(t.a);
+    L->pool.push_back(t.b);
+  }
+  L->pending.clear();
+  *out = L->acc;
+  std::memset(&L->acc, 0, sizeof(L->acc));
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, float* y, int o_lo,
+                   int n_exp, int n_pairs, int T, const void* x, float* out, int accumulate,
+                   const int32_t* wave_of, int wave, int max_rows) {
+  FfnArgs a{};
+  a.fmt = L->fmt;
+  a.E = L->E;
+  a.k = L->k;
+  a.H = L->H;
+  a.I = L->I;
+  a.K = L->K;
+  a.stride = L->stride;
+  a.slots = L->slots;
+  a.order_slot = dev.order_slot;
+  a.pair_off = dev.pair_off;
+  a.pair_list = dev.pair_list;
+  a.weights = dev.weights;
+  a.o_lo = o_lo;
+  a.n_exp = n_exp;
+  a.T = T;
+  a.x = x;
+  a.out = out;
+  a.accumulate = accumulate;
+  a.h = h;
+  a.hb = hb;
+  a.y = y;
+  a.max_rows = max_rows;
+  const double xb = (L->fmt == MOE_FMT_F32 ? 4.0 : 2.0);
+  // pairs of this wave are not known on the host; count the weight bytes
+  // (exact) and bound the activation bytes by all pairs of the step
+  const double up_b = n_exp * up_weight_bytes(L);
+  const double dn_b = n_exp * down_weight_bytes(L);
+  const double flop_up = 2.0 * 2.0 * L->I * (double)L->H * n_pairs;
+  const double flop_dn = 2.0 * (double)L->H * L->I * n_pairs;
+  (void)xb;
+  moe_status st;
+  if (T <= MOE_MAX_GEMV_TOKENS) {
+    TimerRec t1{}, t2{};
+    if ((st = timer_begin(L, L->compute, &t1))) return st;
+    HIP_TRY(launch_ffn_up(a, L->compute));
+    if ((st = timer_end(L, L->compute, &t1, MOE_T_FFN_UP, up_b, flop_up))) return st;
+    if ((st = timer_begin(L, L->compute, &t2))) return st;
+    HIP_TRY(launch_ffn_down(a, L->compute));
+    if ((st = timer_end(L, L->compute, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn))) return st;
+  } else {
+    TimerRec t1{}, t2{}, t3{};
+    if ((st = timer_begin(L, L->compute, &t1))) return st;
+    HIP_TRY(launch_gemm_up(a, L->compute));
+    if ((st = timer_end(L, L->compute, &t1, MOE_T_GEMM_UP, up_b, flop_up))) return st;
+    if ((st = timer_begin(L, L->compute, &t2))) return st;
+    HIP_TRY(launch_gemm_down(a, L->compute));
+    if ((st = timer_end(L, L->compute, &t2, MOE_T_GEMM_DOWN, dn_b, flop_dn))) return st;
+    if ((st = timer_begin(L, L->compute, &t3))) return st;
+    HIP_TRY(launch_combine(a, wave_of, wave, L->compute));
+    if ((st = timer_end(L, L->compute, &t3, MOE_T_COMBINE, 0.0, 0.0))) return st;
+  }
+  return MOE_OK;
+}
+
+// Startup independence check ([PE] "Can paging change the model's outputs?":
+// at startup one more chunk of experts is re-run and the check fails if
+// experts got mixed). Pages up to four experts into two different slot
+// permutations and requires each expert's output to be bitwise identical in
+// both and different from every other expert's output.
+moe_status self_check(moe_layer* L) {
+  const int n = std::min(std::min(L->K, L->E), 4);
+  const int H = L->H, I = L->I;
+  const size_t xsz = (L->fmt == MOE_FMT_F32 ? 4 : 2) * (size_t)H;
+  std::vector<uint8_t> xh(xsz);
+  for (int i = 0; i < H; ++i) {
+    const float v = 0.5f * (float)((i * 37) % 17 - 8) / 8.f;
+    if (L->fmt == MOE_FMT_F32) std::memcpy(&xh[4 * i], &v, 4);
+    else {
+      uint32_t b;
+      std::memcpy(&b, &v, 4);
+      const uint16_t hbits = (uint16_t)(b >> 16);
+      std::memcpy(&xh[2 * i], &hbits, 2);
+    }
+  }
+  // scratch: x, out[2][n][H], h[I], and a one-pair plan per launch
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    size_t o = off;
+    off = align_up(off + b, 256);
+    return o;
+  };
+  const size_t o_x = take(xsz), o_out = take(sizeof(float) * 2 * n * H), o_h = take(sizeof(float) * I),
+               o_os = take(4), o_po = take(8), o_pl = take(4), o_w = take(4);
+  void* blk = nullptr;
+  HIP_TRY(hipMalloc(&blk, off));
+  uint8_t* b = (uint8_t*)blk;
+  moe_status result = MOE_OK;
+  std::vector<float> outs(2 * (size_t)n * H);
+  do {
+    const int32_t po[2] = {0, 1}, pl = 0;
+    const float one = 1.f;
+    if (hipMemcpy(b + o_x, xh.data(), xsz, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(b + o_po, po, 8, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(b + o_pl, &pl, 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(b + o_w, &one, 4, hipMemcpyHostToDevice) != hipSuccess) {
+      result = fail(MOE_ERR_HIP, "self-check setup copy failed");
+      break;
+    }
+    PlanDev dev{};
+    dev.order_slot = (int32_t*)(b + o_os);
+    dev.pair_off = (int32_t*)(b + o_po);
+    dev.pair_list = (int32_t*)(b + o_pl);
+    dev.weights = (float*)(b + o_w);
+    const bool timing = L->timing;
+    L->timing = false;
+    for (int perm = 0; perm < 2 && !result; ++perm) {
+      for (int i = 0; i < n && !result; ++i) {
+        const int slot = perm == 0 ? i : (L->K - 1 - i);
+        if (hipMemcpy(L->slots + (size_t)slot * L->stride, L->host_store + (size_t)i * L->stride,
+                      L->stride, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(b + o_os, &slot, 4, hipMemcpyHostToDevice) != hipSuccess) {
+          result = fail(MOE_ERR_HIP, "self-check page-in failed");
+          break;
+        }
+        float* o = (float*)(b + o_out) + ((size_t)perm * n + i) * H;
+        // the one-pair plan addresses token 0 as pair 0 (k may exceed 1: pair 0 / k == 0)
+        result = run_ffn(L, dev, (float*)(b + o_h), nullptr, nullptr, 0, 1, 1, 1, b + o_x, o, 0,
+                         nullptr, 0, 1);
+        if (!result && hipStreamSynchronize(L->compute) != hipSuccess)
+          result = fail(MOE_ERR_HIP, "self-check forward failed");
+      }
+    }
+    L->timing = timing;
+    if (result) break;
+    if (hipMemcpy(outs.data(), b + o_out, sizeof(float) * outs.size(), hipMemcpyDeviceToHost) != hipSuccess) {
+      result = fail(MOE_ERR_HIP, "self-check readback failed");
+      break;
+    }
+    for (int i = 0; i < n && !result; ++i) {
+      if (std::memcmp(&outs[(size_t)i * H], &outs[((size_t)n + i) * H], sizeof(float) * H) != 0)
+        result = fail(MOE_ERR_SELFCHECK, "expert " + std::to_string(i) +
+                                             " gives different outputs from two different slots");
+      for (int j = 0; j < i && !result; ++j)
+        if (std::memcmp(&outs[(size_t)i * H], &outs[(size_t)j * H], sizeof(float) * H) == 0)
+          result = fail(MOE_ERR_SELFCHECK, "experts " + std::to_string(j) + " and " +
+                                               std::to_string(i) + " give identical outputs");
+    }
+  } while (0);
+  (void)hipFree(blk);
+  return result;
+}
+
+}  // namespace

@@ -1,0 +1,471 @@
+// Decode-path expert FFN (few tokens per expert): weight streaming GEMVs.
+//
+// [PE] "What does Paged Experts actually do?": once a wave's experts are in
+// their slots, the expert math runs on the GPU over the slots. [SRV]
+// ("Mastering the LLM Inference Serving Engine SGLang", the prefill/decode
+// discussion): batch-1 decode does about one flop per weight byte, so it is
+// bound by reading the weights, and smaller weight formats read less.
+//
+// Two launches per wave:
+//   up   : one workgroup per (expert of the wave, block of h rows). Every
+//          wavefront streams RPW gate rows and RPW up rows of its expert once
+//          (16-byte loads, all issued before any arithmetic), dots them with
+//          the tokens routed to that expert, reduces across the wavefront and
+//          writes h = SiLU(g) * u (fp32) for each (token, expert) pair.
+//   down : one wavefront per RW output rows; it walks the wave's experts,
+//          streaming the RW rows of each W_d (next expert's rows prefetched
+//          while the current ones are used), dots them with h and adds
+//          w_tj * y into the accumulator of token t held by lane t.
+// Every weight byte of the wave is read from HBM exactly once; the summation
+// order is fixed, so results are bitwise reproducible.
+#include "internal.h"
+
+namespace moepage {
+
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// e4m3fn pair -> two floats (gfx950 converts OCP e4m3 in hardware); HI selects
+// bytes 2..3 of the word instead of bytes 0..1.
+template <bool HI>
+__device__ inline f32x2 fp8x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+__device__ inline float half_to_float(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, 2);
+  return (float)v;
+}
+
+// ------------------------------------------------------------------ formats
+// Per format: values per 16-byte chunk of a W13 row (CV1), bytes and values
+// per chunk of a W_d row (CB2, CV2).
+template <int F> struct Fmt;
+template <> struct Fmt<MOE_FMT_F32> { static constexpr int CV1 = 4, CB2 = 16, CV2 = 4; };
+template <> struct Fmt<MOE_FMT_BF16> { static constexpr int CV1 = 8, CB2 = 8, CV2 = 4; };
+template <> struct Fmt<MOE_FMT_FP8_E4M3_B128> { static constexpr int CV1 = 16, CB2 = 4, CV2 = 4; };
+template <> struct Fmt<MOE_FMT_INT4_ASYM_G128> { static constexpr int CV1 = 32, CB2 = 4, CV2 = 8; };
+
+// Load CV1 activations starting at column col, as float.
+template <int F, typename XT>
+__device__ inline void load_x(const XT* x, int col, float* v) {
+  constexpr int CV1 = Fmt<F>::CV1;
+  if constexpr (sizeof(XT) == 4) {
+#pragma unroll
+    for (int i = 0; i < CV1; i += 4) {
+      const float4 q = *(const float4*)((const float*)x + col + i);
+      v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CV1; i += 8) {
+      const uint4 q = *(const uint4*)((const uint16_t*)x + col + i);
+      v[i] = bf16lo(q.x); v[i + 1] = bf16hi(q.x);
+      v[i + 2] = bf16lo(q.y); v[i + 3] = bf16hi(q.y);
+      v[i + 4] = bf16lo(q.z); v[i + 5] = bf16hi(q.z);
+      v[i + 6] = bf16lo(q.w); v[i + 7] = bf16hi(q.w);
+    }
+  }
+}
+
+// Raw dot of one 16-byte W13 chunk with CV1 activations (no scale/zero).
+// For int4 also returns the activation sum (for the zero point).
+template <int F>
+__device__ inline float dot1(const uint4 w, const float* x, float* xsum) {
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  float acc = 0.f;
+  if constexpr (F == MOE_FMT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(wv[i]), x[i], acc);
+  } else if constexpr (F == MOE_FMT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16lo(wv[i]), x[2 * i], acc);
+      acc = fmaf(bf16hi(wv[i]), x[2 * i + 1], acc);
+    }
+  } else if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 a = fp8x2<false>(wv[i]), b = fp8x2<true>(wv[i]);
+      acc = fmaf(a.x, x[4 * i], acc);
+      acc = fmaf(a.y, x[4 * i + 1], acc);
+      acc = fmaf(b.x, x[4 * i + 2], acc);
+      acc = fmaf(b.y, x[4 * i + 3], acc);
+    }
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        acc = fmaf((float)((wv[i] >> (4 * n)) & 0xFu), x[8 * i + n], acc);
+        s += x[8 * i + n];
+      }
+    }
+    *xsum = s;
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------------ up
+template <int F, int NJ, int RPW, typename XT>
+__global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
+  constexpr int CV1 = Fmt<F>::CV1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int H = a.H, I = a.I;
+  const int i0 = (blockIdx.x * 4 + wid) * RPW;
+  if (i0 >= I) return;
+  const int o = a.o_lo + blockIdx.y;
+  const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
+  const RecLayout L = rec_layout(F, H, I);
+  const int nch = H / CV1;
+  const size_t row_bytes = (size_t)H * fmt_elem_bits(F) / 8;
+  const uint8_t* w13 = rec + L.w13;
+
+  uint4 wg[RPW][NJ], wu[RPW][NJ];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int i = min(i0 + r, I - 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = lane + kWave * j;
+      if (c < nch) {
+        wg[r][j] = *(const uint4*)(w13 + (size_t)i * row_bytes + (size_t)c * 16);
+        wu[r][j] = *(const uint4*)(w13 + (size_t)(I + i) * row_bytes + (size_t)c * 16);
+      } else {
+        wg[r][j] = make_uint4(0, 0, 0, 0);
+        wu[r][j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  // per-chunk scale (fp8: 128x128 tiles; int4: per row and group of 128)
+  float sg[RPW][NJ], su[RPW][NJ], zg[RPW][NJ], zu[RPW][NJ];
+  if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+    const float* s13 = (const float*)(rec + L.s13);
+    const int nb = H / 128;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int i = min(i0 + r, I - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = min(lane + kWave * j, nch - 1);
+        sg[r][j] = s13[(i / 128) * nb + (c * CV1) / 128];
+        su[r][j] = s13[((I + i) / 128) * nb + (c * CV1) / 128];
+      }
+    }
+  } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+    const uint16_t* s13 = (const uint16_t*)(rec + L.s13);
+    const uint16_t* z13 = (const uint16_t*)(rec + L.z13);
+    const int ng = H / 128;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int i = min(i0 + r, I - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int g = min(lane + kWave * j, nch - 1) * CV1 / 128;
+        sg[r][j] = half_to_float(s13[(size_t)i * ng + g]);
+        zg[r][j] = half_to_float(z13[(size_t)i * ng + g]);
+        su[r][j] = half_to_float(s13[(size_t)(I + i) * ng + g]);
+        zu[r][j] = half_to_float(z13[(size_t)(I + i) * ng + g]);
+      }
+    }
+  }
+
+  const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
+  const XT* xbase = (const XT*)a.x;
+  for (int q = p0; q < p1; ++q) {
+    const int t = a.pair_list[q] / a.k;
+    float xv[NJ][CV1];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = lane + kWave * j;
+      if (c < nch) load_x<F, XT>(xbase + (size_t)t * H, c * CV1, xv[j]);
+      else {
+#pragma unroll
+        for (int v = 0; v < CV1; ++v) xv[j][v] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float xs = 0.f;
+        const float dg = dot1<F>(wg[r][j], xv[j], &xs);
+        const float du = dot1<F>(wu[r][j], xv[j], &xs);
+        if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+          g = fmaf(dg, sg[r][j], g);
+          u = fmaf(du, su[r][j], u);
+        } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+          g = fmaf(sg[r][j], dg - zg[r][j] * xs, g);
+          u = fmaf(su[r][j], du - zu[r][j] * xs, u);
+        } else {
+          g += dg;
+          u += du;
+        }
+      }
+      g = wave_sum(g);
+      u = wave_sum(u);
+      if (lane == 0 && i0 + r < I) {
+        const float h = g / (1.f + __expf(-g)) * u;
+        a.h[(size_t)q * I + i0 + r] = h;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down
+template <int F>
+__device__ inline void load_w2(const uint8_t* p, uint32_t* w) {
+  if constexpr (Fmt<F>::CB2 == 16) {
+    const uint4 v = *(const uint4*)p;
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (Fmt<F>::CB2 == 8) {
+    const uint2 v = *(const uint2*)p;
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *(const uint32_t*)p;
+  }
+}
+
+template <int F>
+__device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
+  float acc = 0.f;
+  if constexpr (F == MOE_FMT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(w[i]), h[i], acc);
+  } else if constexpr (F == MOE_FMT_BF16) {
+    acc = fmaf(bf16lo(w[0]), h[0], acc);
+    acc = fmaf(bf16hi(w[0]), h[1], acc);
+    acc = fmaf(bf16lo(w[1]), h[2], acc);
+    acc = fmaf(bf16hi(w[1]), h[3], acc);
+  } else if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+    const f32x2 a = fp8x2<false>(w[0]), b = fp8x2<true>(w[0]);
+    acc = fmaf(a.x, h[0], acc);
+    acc = fmaf(a.y, h[1], acc);
+    acc = fmaf(b.x, h[2], acc);
+    acc = fmaf(b.y, h[3], acc);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      acc = fmaf((float)((w[0] >> (4 * n)) & 0xFu), h[n], acc);
+      s += h[n];
+    }
+    *hsum = s;
+  }
+  return acc;
+}
+
+template <int F, int NJ, int RW>
+__global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
+  constexpr int CB2 = Fmt<F>::CB2, CV2 = Fmt<F>::CV2, NW = CB2 / 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int H = a.H, I = a.I;
+  const int r0 = (blockIdx.x * 4 + wid) * RW;
+  if (r0 >= H) return;
+  const RecLayout L = rec_layout(F, H, I);
+  const int nch = I / CV2;
+  const size_t row_bytes = (size_t)I * fmt_elem_bits(F) / 8;
+
+  float acc[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+
+  uint32_t cur[RW][NJ][NW], nxt[RW][NJ][NW];
+  auto load_expert = [&](int e, uint32_t (&dst)[RW][NJ][NW]) {
+    const uint8_t* wd = a.slots + (size_t)a.order_slot[a.o_lo + e] * a.stride + L.wd;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int row = min(r0 + r, H - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) load_w2<F>(wd + (size_t)row * row_bytes + (size_t)c * CB2, dst[r][j]);
+        else {
+#pragma unroll
+          for (int n = 0; n < NW; ++n) dst[r][j][n] = 0u;
+        }
+      }
+    }
+  };
+
+  if (a.n_exp > 0) load_expert(0, cur);
+  for (int e = 0; e < a.n_exp; ++e) {
+    if (e + 1 < a.n_exp) load_expert(e + 1, nxt);
+    const int o = a.o_lo + e;
+    const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
+    float sc[RW][NJ], zc[RW][NJ];
+    if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+      const float* sd = (const float*)(rec + L.sd);
+      const int nb = I / 128;
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = min(lane + kWave * j, nch - 1);
+          sc[r][j] = sd[(min(r0 + r, H - 1) / 128) * nb + (c * CV2) / 128];
+        }
+    } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+      const uint16_t* sd = (const uint16_t*)(rec + L.sd);
+      const uint16_t* zd = (const uint16_t*)(rec + L.zd);
+      const int ng = I / 128;
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int g = min(lane + kWave * j, nch - 1) * CV2 / 128;
+          const size_t row = (size_t)min(r0 + r, H - 1);
+          sc[r][j] = half_to_float(sd[row * ng + g]);
+          zc[r][j] = half_to_float(zd[row * ng + g]);
+        }
+    }
+    const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
+    for (int q = p0; q < p1; ++q) {
+      const int pair = a.pair_list[q];
+      const int t = pair / a.k;
+      const float wq = a.weights[pair];
+      float hv[NJ][CV2];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) {
+#pragma unroll
+          for (int v = 0; v < CV2; v += 4) {
+            const float4 f = *(const float4*)(a.h + (size_t)q * I + c * CV2 + v);
+            hv[j][v] = f.x; hv[j][v + 1] = f.y; hv[j][v + 2] = f.z; hv[j][v + 3] = f.w;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < CV2; ++v) hv[j][v] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        float y = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          float hs = 0.f;
+          const float d = dot2<F>(cur[r][j], hv[j], &hs);
+          if constexpr (F == MOE_FMT_FP8_E4M3_B128) y = fmaf(d, sc[r][j], y);
+          else if constexpr (F == MOE_FMT_INT4_ASYM_G128) y = fmaf(sc[r][j], d - zc[r][j] * hs, y);
+          else y += d;
+        }
+        y = wave_sum(y);
+        if (lane == t) acc[r] = fmaf(wq, y, acc[r]);
+      }
+    }
+    if (e + 1 < a.n_exp) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int n = 0; n < NW; ++n) cur[r][j][n] = nxt[r][j][n];
+    }
+  }
+  if (lane < a.T) {
+    float* o = a.out + (size_t)lane * H;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      if (r0 + r < H) o[r0 + r] = (a.accumulate ? o[r0 + r] : 0.f) + acc[r];
+    }
+  }
+}
+
+constexpr int kRPW = 2;  // h rows per wavefront (up)
+constexpr int kRW = 2;   // output rows per wavefront (down)
+
+template <int F, typename XT>
+hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
+  const int nj = (a.H / Fmt<F>::CV1 + kWave - 1) / kWave;
+  const dim3 grid((a.I + 4 * kRPW - 1) / (4 * kRPW), a.n_exp), block(256);
+  switch (nj) {
+    case 1: ffn_up_kernel<F, 1, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    case 2: ffn_up_kernel<F, 2, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    case 3: ffn_up_kernel<F, 3, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    case 4: ffn_up_kernel<F, 4, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    case 6: ffn_up_kernel<F, 6, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    case 8: ffn_up_kernel<F, 8, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int F>
+hipError_t down_dispatch(const FfnArgs& a, hipStream_t s) {
+  const int nj = (a.I / Fmt<F>::CV2 + kWave - 1) / kWave;
+  const dim3 grid((a.H + 4 * kRW - 1) / (4 * kRW)), block(256);
+  switch (nj) {
+    case 1: ffn_down_kernel<F, 1, kRW><<<grid, block, 0, s>>>(a); break;
+    case 2: ffn_down_kernel<F, 2, kRW><<<grid, block, 0, s>>>(a); break;
+    case 3: ffn_down_kernel<F, 3, kRW><<<grid, block, 0, s>>>(a); break;
+    case 4: ffn_down_kernel<F, 4, kRW><<<grid, block, 0, s>>>(a); break;
+    case 6: ffn_down_kernel<F, 6, kRW><<<grid, block, 0, s>>>(a); break;
+    case 8: ffn_down_kernel<F, 8, kRW><<<grid, block, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int nj_of(int n) {
+  const int nj = (n + kWave - 1) / kWave;
+  return (nj == 1 || nj == 2 || nj == 3 || nj == 4 || nj == 6 || nj == 8) ? nj : 0;
+}
+
+}  // namespace
+
+bool ffn_shape_supported(int fmt, int H, int I) {
+  if (H <= 0 || I <= 0) return false;
+  int cv1 = 0, cv2 = 0;
+  switch (fmt) {
+    case MOE_FMT_F32: cv1 = 4; cv2 = 4; break;
+    case MOE_FMT_BF16: cv1 = 8; cv2 = 4; break;
+    case MOE_FMT_FP8_E4M3_B128: cv1 = 16; cv2 = 4; break;
+    case MOE_FMT_INT4_ASYM_G128: cv1 = 32; cv2 = 8; break;
+    default: return false;
+  }
+  if (fmt == MOE_FMT_FP8_E4M3_B128 || fmt == MOE_FMT_INT4_ASYM_G128) {
+    if (H % 128 || I % 128) return false;
+  }
+  if (H % cv1 || I % cv2) return false;
+  return nj_of(H / cv1) && nj_of(I / cv2);
+}
+
+hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s) {
+  if (a.n_exp <= 0) return hipSuccess;
+  switch (a.fmt) {
+    case MOE_FMT_F32: return up_dispatch<MOE_FMT_F32, float>(a, s);
+    case MOE_FMT_BF16: return up_dispatch<MOE_FMT_BF16, uint16_t>(a, s);
+    case MOE_FMT_FP8_E4M3_B128: return up_dispatch<MOE_FMT_FP8_E4M3_B128, uint16_t>(a, s);
+    case MOE_FMT_INT4_ASYM_G128: return up_dispatch<MOE_FMT_INT4_ASYM_G128, uint16_t>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) {
+  switch (a.fmt) {
+    case MOE_FMT_F32: return down_dispatch<MOE_FMT_F32>(a, s);
+    case MOE_FMT_BF16: return down_dispatch<MOE_FMT_BF16>(a, s);
+    case MOE_FMT_FP8_E4M3_B128: return down_dispatch<MOE_FMT_FP8_E4M3_B128>(a, s);
+    case MOE_FMT_INT4_ASYM_G128: return down_dispatch<MOE_FMT_INT4_ASYM_G128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moepage

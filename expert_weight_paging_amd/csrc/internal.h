@@ -1,0 +1,138 @@
+// Internal declarations of libmoepage (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "moepage.h"
+
+namespace moepage {
+
+// Byte offsets of the per-layer table state (see moe_state_bytes).
+struct StateLayout {
+  size_t slot_expert, expert_slot, stamp, clock, total;
+};
+
+inline size_t align8(size_t v) { return (v + 7) & ~size_t(7); }
+
+inline StateLayout state_layout(int E, int K) {
+  StateLayout s;
+  s.slot_expert = 0;
+  s.expert_slot = align8(s.slot_expert + sizeof(int32_t) * (size_t)K);
+  s.stamp = align8(s.expert_slot + sizeof(int32_t) * (size_t)E);
+  s.clock = s.stamp + sizeof(int64_t) * (size_t)K;
+  s.total = s.clock + sizeof(int64_t);
+  return s;
+}
+
+// Header of the host-visible plan (pinned, mapped, coherent). The slot-plan
+// kernel writes the header fields and the two order arrays that follow it,
+// then publishes `seq` with a system-scope release store; the host waits for
+// seq to reach the value it expects.
+struct PlanHdr {
+  int32_t seq;
+  int32_t num_tokens;
+  int32_t num_distinct;
+  int32_t num_hits;
+  int32_t num_waves;
+  int32_t pad[3];
+  // int32_t order_expert[E]; int32_t order_slot[E];
+};
+
+// Device-side arrays of a plan.
+struct PlanDev {
+  int32_t* ids;          // [T*k]
+  float* weights;        // [T*k]
+  int32_t* slot_ids;     // [T*k]
+  int32_t* wave_of;      // [T*k]
+  int32_t* order_expert; // [E] experts in wave order
+  int32_t* order_slot;   // [E] slot of each during its wave
+  int32_t* pair_off;     // [E+1] CSR offsets over wave order
+  int32_t* pair_list;    // [T*k] pair index t*k+j, grouped by expert, ascending
+  int32_t* counts;       // [4]: num_distinct, num_hits, num_waves, num_tokens
+};
+
+// Format traits shared by host validation and launch code.
+__host__ __device__ inline int fmt_elem_bits(int fmt) {
+  switch (fmt) {
+    case MOE_FMT_F32: return 32;
+    case MOE_FMT_BF16: return 16;
+    case MOE_FMT_FP8_E4M3_B128: return 8;
+    case MOE_FMT_INT4_ASYM_G128: return 4;
+  }
+  return 0;
+}
+
+// Byte offsets of the sections of one expert record.
+struct RecLayout {
+  size_t w13, wd, s13, sd, z13, zd, payload, stride;
+};
+
+__host__ __device__ inline RecLayout rec_layout(int fmt, int H, int I) {
+  RecLayout r{};
+  size_t n13 = (size_t)2 * I * H, nd = (size_t)H * I;
+  int bits = fmt_elem_bits(fmt);
+  r.w13 = 0;
+  r.wd = n13 * bits / 8;
+  size_t end = r.wd + nd * bits / 8;
+  r.s13 = r.sd = r.z13 = r.zd = end;
+  if (fmt == MOE_FMT_FP8_E4M3_B128) {
+    r.s13 = end;
+    r.sd = r.s13 + sizeof(float) * (size_t)(2 * I / 128) * (H / 128);
+    end = r.sd + sizeof(float) * (size_t)(H / 128) * (I / 128);
+  } else if (fmt == MOE_FMT_INT4_ASYM_G128) {
+    size_t g13 = (size_t)2 * I * (H / 128), gd = (size_t)H * (I / 128);
+    r.s13 = end;
+    r.sd = r.s13 + 2 * g13;
+    r.z13 = r.sd + 2 * gd;
+    r.zd = r.z13 + 2 * g13;
+    end = r.zd + 2 * gd;
+  }
+  r.payload = end;
+  r.stride = (end + 255) / 256 * 256;
+  return r;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
+                         hipStream_t s);
+
+hipError_t launch_plan(const int32_t* ids, int T, int k, int E, int K, void* state,
+                       PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s);
+
+hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s);
+
+struct FfnArgs {
+  int fmt, E, k, H, I, K;
+  size_t stride;
+  const uint8_t* slots;
+  const int32_t* order_slot;
+  const int32_t* pair_off;
+  const int32_t* pair_list;
+  const float* weights;
+  int o_lo, n_exp;     // wave's range in wave order
+  int T;
+  const void* x;       // [T][H]
+  float* out;          // [T][H]
+  int accumulate;      // 0: write out, 1: add to out
+  float* h;            // GEMV scratch fp32 [T*k][I], indexed by CSR position
+  uint16_t* hb;        // GEMM scratch bf16 [T*k][I]
+  float* y;            // GEMM scratch fp32 [T*k][H]
+  int max_rows;        // upper bound on pairs of one expert in this wave (GEMM)
+};
+
+hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);
+bool ffn_shape_supported(int fmt, int H, int I);
+
+hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const FfnArgs& a, const int32_t* wave_of, int wave, hipStream_t s);
+bool gemm_shape_supported(int H, int I);
+
+hipError_t launch_residual(const uint16_t* x_in, const float* out, uint16_t* x_out, int64_t n,
+                           hipStream_t s);
+
+}  // namespace moepage

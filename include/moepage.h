@@ -1,0 +1,265 @@
+/*
+ * moepage.h -- C ABI of the Paged Experts hot path on AMD MI355X (gfx950).
+ *
+ * Sources, cited by title and section:
+ *   [PE]  "Running an MoE Model Larger Than Your VRAM: SGLang Paged Experts,
+ *         the PCIe Math, and the 4-Request Cliff" (post on the sgl-project
+ *         feed page).
+ *   [LRU] "Locality of reference helped 94GB Qwen3.8-Flash-Next runs at 68
+ *         tok/s on one RTX 5090" (post on the same page).
+ *
+ * The scheme ([PE] "TL;DR", "What does Paged Experts actually do?"): every MoE
+ * layer keeps K of its E experts in a slot table in GPU memory and all E in
+ * pinned host memory; a step copies in only the routed experts that are not
+ * resident (least recently used out), then runs the expert math on the GPU.
+ *
+ * One layer-step is:
+ *   moe_route(layer, logits, T, plan)             router + slot plan; returns
+ *                                                  once the plan is host-visible
+ *   for w in 0 .. plan.num_waves-1:
+ *     moe_page_in(layer, plan, w)                  async copies, copy stream
+ *     moe_forward(layer, plan, w, x, out)          async expert FFN, compute stream
+ *
+ * Conventions for every call:
+ *   - Returns MOE_OK (0) or a negative moe_status; nothing throws or aborts
+ *     across the ABI. moe_last_error() gives a message for the calling thread.
+ *   - Pointers marked "device" are HIP device pointers (torch CUDA tensors);
+ *     "host" are CPU pointers. Streams are hipStream_t passed as void*;
+ *     NULL means the null stream.
+ *   - The caller owns every buffer it passes and both/all streams. The library
+ *     owns only the opaque handles and what moe_plan_create allocates.
+ *   - A layer handle and the plans used with it are used by one host thread
+ *     at a time.
+ *   - There is never a silent fallback: unsupported shapes or formats fail at
+ *     init ([PE] "A rollout checklist": rejection at startup is the good
+ *     failure).
+ */
+#ifndef MOEPAGE_H
+#define MOEPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad shape, pointer, wave index or size limit   */
+  MOE_ERR_NOT_PINNED = -2,  /* host store is not page-locked host memory       */
+  MOE_ERR_FORMAT = -3,      /* unknown format or record size mismatch          */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call failed                        */
+  MOE_ERR_SELFCHECK = -5,   /* slot-independence check at init failed           */
+  MOE_ERR_STATE = -6,       /* calls out of order (page-in/forward vs plan)     */
+  MOE_ERR_TIMEOUT = -7      /* the plan did not become host-visible in time     */
+} moe_status;
+
+/* Expert weight formats ([PE] "What does Paged Experts actually do?": bf16,
+ * block-FP8 and GPTQ-style int4 experts). Record layout of one expert, in this
+ * order (reduction dimension contiguous in every matrix):
+ *   W13 = [W_gate; W_up]  2I x H      W_d  H x I
+ *   MOE_FMT_F32            : float32 weights
+ *   MOE_FMT_BF16           : bfloat16 weights
+ *   MOE_FMT_FP8_E4M3_B128  : OCP e4m3fn codes, then float32 scales per 128x128
+ *                            tile: W13 [2I/128][H/128], W_d [H/128][I/128];
+ *                            w = decode(q) * scale (weight-only)
+ *   MOE_FMT_INT4_ASYM_G128 : 8 codes per uint32 along the reduction dim (low
+ *                            nibble = lower index), then float16 scales W13
+ *                            [2I][H/128], W_d [H][I/128], then float16 zeros
+ *                            in the same shapes; w = (q - z) * s
+ * All per-expert tensors live in the one record, so one page-in moves all of
+ * them ([PE] "Can paging change the model's outputs?": a tensor left unpaged
+ * makes a paged-in expert run with another expert's values). The record
+ * stride is the payload rounded up to 256 bytes. */
+typedef enum moe_format {
+  MOE_FMT_F32 = 0,
+  MOE_FMT_BF16 = 1,
+  MOE_FMT_FP8_E4M3_B128 = 2,
+  MOE_FMT_INT4_ASYM_G128 = 3
+} moe_format;
+
+/* Limits of this implementation (checked at init). */
+#define MOE_MAX_EXPERTS 1024        /* E                                      */
+#define MOE_MAX_TOP_K 32            /* top_k                                  */
+#define MOE_MAX_GEMV_TOKENS 64      /* tokens per forward for non-bf16 formats */
+
+/* Record stride in bytes for a format and shape, or 0 if unsupported. */
+size_t moe_record_bytes(int32_t format, int32_t hidden, int32_t intermediate);
+
+/* Bytes of the per-layer slot-table state buffer (device). Layout:
+ * int32 slot_expert[K], int32 expert_slot[E], int64 stamp[K], int64 clock,
+ * each array starting on an 8-byte boundary. */
+size_t moe_state_bytes(int32_t num_experts, int32_t num_slots);
+
+typedef struct moe_layer_desc {
+  int32_t num_experts;   /* E, 1..MOE_MAX_EXPERTS                              */
+  int32_t top_k;         /* k, 1..min(E, MOE_MAX_TOP_K)                        */
+  int32_t hidden;        /* H                                                  */
+  int32_t intermediate;  /* I                                                  */
+  int32_t num_slots;     /* K, 1..E ([PE] "What does Paged Experts actually do?")*/
+  int32_t format;        /* moe_format                                          */
+  size_t record_bytes;   /* must equal moe_record_bytes(format, H, I)          */
+  const void* host_store;/* host, pinned, [E][record_bytes]; caller-owned; must
+                            outlive the handle ([PE] "What does Paged Experts
+                            actually do?": the pinned store holds every expert) */
+  void* slot_store;      /* device, [K][record_bytes]; caller-owned              */
+  void* state;           /* device, moe_state_bytes(E, K); caller-owned          */
+  int32_t initial_fill;  /* 0: empty table; 1: experts 0..K-1 copied into slots
+                            0..K-1 (stamp 0) at init and at reset                */
+  int32_t self_check;    /* 1: run the slot-independence check at init           */
+} moe_layer_desc;
+
+typedef struct moe_layer moe_layer;
+typedef struct moe_plan moe_plan;
+
+/* Create a layer. Validates the descriptor; verifies with
+ * hipPointerGetAttributes that host_store is page-locked host memory
+ * (MOE_ERR_NOT_PINNED otherwise); initialises the state buffer (synchronously)
+ * and, with initial_fill, copies experts 0..K-1 into the slots.
+ *   compute_stream: expert FFN kernels
+ *   copy_stream:    page-in copies (hipMemcpyAsync, pinned host -> slot)
+ *   route_stream:   router and slot-plan kernels (may equal compute_stream)
+ * With self_check, pages a few experts into two different slot permutations
+ * and requires bitwise-identical per-expert outputs and distinct outputs
+ * across experts ([PE] "Can paging change the model's outputs?": the startup
+ * independence check); MOE_ERR_SELFCHECK on failure. */
+moe_status moe_layer_init(const moe_layer_desc* desc, void* compute_stream,
+                          void* copy_stream, void* route_stream, moe_layer** out);
+
+/* Restore the initial table (empty, or experts 0..K-1 when initial_fill),
+ * synchronously. Statistics are kept. */
+moe_status moe_layer_reset(moe_layer* layer);
+void moe_layer_destroy(moe_layer* layer);
+
+/* Create a plan for up to max_tokens tokens per route call with this layer.
+ * Allocates small device arrays (ids, weights, slot map, grouping), the
+ * pinned host-visible plan and the FFN workspace. */
+moe_status moe_plan_create(const moe_layer* layer, int32_t max_tokens, moe_plan** out);
+void moe_plan_destroy(moe_plan* plan);
+
+/* Route T tokens and plan the step.
+ *   logits: device, float32 [T][E], row-major
+ * Router: top_k largest logits compared as float32, equal logits to the
+ * smaller id, listed by descending logit; weights are the softmax renormalised
+ * over the selected k ([PE] "What does Paged Experts actually do?").
+ * Slot plan: distinct routed experts D; residents first, then missing ones,
+ * each ascending; waves are consecutive chunks of K of that order, so a step
+ * is one wave exactly when |D| <= K ([PE] "What happens with more than one
+ * request?"). Per wave the clock ticks; victims are slots whose expert is not
+ * in the wave, empty first, then oldest stamp, ties to the lower slot; the
+ * i-th missing expert (ascending id) takes the i-th victim ([PE] "TL;DR":
+ * least recently used out; [LRU] "The fix").
+ * Kernels run on route_stream; they wait for the plan's previous forward. The
+ * call returns once the plan is host-visible (the one host synchronisation of
+ * a layer-step). T may be 0 (no waves). T <= max_tokens. */
+moe_status moe_route(moe_layer* layer, const float* logits, int32_t num_tokens, moe_plan* plan);
+
+typedef struct moe_plan_info {
+  int32_t num_tokens;
+  int32_t num_distinct;   /* |D|                          */
+  int32_t num_hits;       /* resident at the start        */
+  int32_t num_misses;     /* experts paged in, all waves  */
+  int32_t num_waves;      /* ceil(|D| / K)                */
+} moe_plan_info;
+
+typedef struct moe_wave_info {
+  int32_t num_experts;             /* experts in this wave                   */
+  int32_t num_misses;              /* of which paged in                      */
+  const int32_t* experts;          /* host, [num_experts], wave order        */
+  const int32_t* slots;            /* host, [num_experts], slot of each      */
+  const int32_t* miss_experts;     /* host, [num_misses] = tail of experts   */
+  const int32_t* miss_slots;       /* host, [num_misses] = tail of slots     */
+} moe_wave_info;
+
+/* Host views of the last routed plan (valid until the next moe_route). */
+moe_status moe_plan_get_info(const moe_plan* plan, moe_plan_info* out);
+moe_status moe_plan_get_wave(const moe_plan* plan, int32_t wave, moe_wave_info* out);
+
+/* Copy the plan's per-(token, j) arrays to host buffers (synchronous; for
+ * checking): ids int32 [T][k], weights float32 [T][k], slot of each pair
+ * during its wave int32 [T][k], wave of each pair int32 [T][k]. Any pointer
+ * may be NULL. */
+moe_status moe_plan_read(const moe_plan* plan, int32_t* ids, float* weights,
+                         int32_t* slot_ids, int32_t* wave_of);
+
+/* Page in the misses of one wave: one hipMemcpyAsync per miss, host record ->
+ * its slot, on copy_stream, after the layer's previous forward has finished
+ * (a victim slot may still be read by it). Waves are paged in and computed in
+ * order: page_in(w) requires forward(w-1) to have been issued. */
+moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
+
+/* Expert math of one wave on compute_stream, after that wave's page-in:
+ *   x:   device, [T][H], float32 for MOE_FMT_F32 else bfloat16
+ *   out: device, float32 [T][H]; wave 0 writes it, later waves add to it
+ * out[t] = sum over (t, j) in this wave of w_tj * W_d (SiLU(W_gate x_t) *
+ * (W_up x_t)), reading each expert from its slot. For T <= MOE_MAX_GEMV_TOKENS
+ * the weights are streamed once per wave (GEMV path); bf16 layers with more
+ * tokens use the token-grouped MFMA GEMM. */
+moe_status moe_forward(moe_layer* layer, const moe_plan* plan, int32_t wave,
+                       const void* x, float* out);
+
+/* Residual of a stack of MoE layers (no attention, no norm):
+ * x_out[i] = bf16_rne(float(x_in[i]) + out[i]) for i < n; x_in and x_out are
+ * device bf16 (may alias), out device float32. Runs on the given stream. */
+moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out,
+                             int64_t n, void* stream);
+
+typedef struct moe_stats {
+  int64_t steps;        /* moe_route calls with T > 0                          */
+  int64_t refs;         /* sum of distinct experts per step                    */
+  int64_t activations;  /* sum of T * top_k                                    */
+  int64_t hits;         /* sum of resident-at-start distinct experts           */
+  int64_t misses;       /* experts paged in                                    */
+  int64_t waves;        /* sum of waves                                        */
+  int64_t bytes_paged;  /* misses * record_bytes                               */
+} moe_stats;
+
+/* Per-layer counters ([LRU] "The fix": the hit rate is reported at exit;
+ * [PE] "Why is it fast ...": only a counter inside the engine gives the real
+ * miss rate). */
+moe_status moe_layer_stats(const moe_layer* layer, moe_stats* out);
+
+/* Synchronous copy of the table state to host buffers (any may be NULL):
+ * slot_expert int32 [K], expert_slot int32 [E], stamp int64 [K], clock. */
+moe_status moe_layer_get_state(moe_layer* layer, int32_t* slot_expert, int32_t* expert_slot,
+                               int64_t* stamp, int64_t* clock);
+
+/* Kernel timing with HIP events on the streams the work runs on. */
+typedef enum moe_timer {
+  MOE_T_ROUTE = 0,     /* router + slot plan + grouping kernels              */
+  MOE_T_FFN_UP = 1,    /* GEMV path, gate/up + SiLU kernel                    */
+  MOE_T_FFN_DOWN = 2,  /* GEMV path, down projection + weighted combine       */
+  MOE_T_GEMM_UP = 3,   /* GEMM path, grouped gate/up GEMM + SiLU              */
+  MOE_T_GEMM_DOWN = 4, /* GEMM path, grouped down GEMM                        */
+  MOE_T_COMBINE = 5,   /* GEMM path, weighted top-k combine                   */
+  MOE_T_PAGE_IN = 6,   /* one wave's page-in copies                           */
+  MOE_T_COUNT = 7
+} moe_timer;
+
+typedef struct moe_timing {
+  int64_t count[MOE_T_COUNT];    /* timed launches                            */
+  double ms[MOE_T_COUNT];        /* summed event-measured duration            */
+  double bytes[MOE_T_COUNT];     /* summed algorithmic bytes (weights read for
+                                    the FFN/GEMM classes, bytes copied for
+                                    page-in)                                  */
+  double flops[MOE_T_COUNT];     /* summed algorithmic flops                  */
+} moe_timing;
+
+/* enable != 0 starts recording events around each timed launch (adds host
+ * overhead); moe_timing_read waits for them, returns the sums since the last
+ * read and clears them. */
+moe_status moe_timing_enable(moe_layer* layer, int32_t enable);
+moe_status moe_timing_read(moe_layer* layer, moe_timing* out);
+
+/* Page-locked host memory for expert stores (hipHostMalloc), and its release. */
+void* moe_host_alloc(size_t bytes);
+void moe_host_free(void* p);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEPAGE_H */

@@ -72,8 +72,12 @@ class PagedLayer:
             self._cache[s] = formats.decode_record(self.slots[s], self.fmt, self.H, self.I)
         return self._cache[s]
 
-    def step(self, logits, x):
-        """logits float32 [B,E], x [B,H] (values) -> (out float64 [B,H], ids, w, plan)."""
+    def step(self, logits, x, compute=True):
+        """logits float32 [B,E], x [B,H] (values) -> (out float64 [B,H], ids, w, plan).
+
+        compute=False plans and pages in exactly the same way but skips the
+        expert math (out is None), for long sequences checked on samples.
+        """
         ids, w = route(logits, self.top_k)
         plan = self.table.plan(ids, on_page_in=None)
         # replay the page-ins in wave order: a later wave may reuse a slot that
@@ -84,13 +88,15 @@ class PagedLayer:
         for wave_i, wave in enumerate(plan.waves):
             for e, s in wave.misses:
                 self._page_in(e, s)
+            if not compute:
+                continue
             for b in range(B):
                 for j in range(self.top_k):
                     if plan.wave_of[b, j] != wave_i:
                         continue
                     wg, wu, wd = self._slot_weights(int(plan.slot_ids[b, j]))
                     out[b] += w[b, j] * swiglu_expert(wg, wu, wd, x[b])
-        return out, ids, w, plan
+        return (out if compute else None), ids, w, plan
 
     def unpaged_forward(self, logits, x):
         """The same layer computed straight from the host store (no slots)."""
