@@ -73,7 +73,8 @@ struct moe_plan {
   PlanHdr* hdr_dev;   // device alias of the same pinned memory
   int32_t seq;
   float* h;           // GEMV scratch
-  uint16_t* hb;       // GEMM scratch
+  uint16_t* hb;       // GEMM scratch (h high part)
+  uint16_t* hb_lo;    // GEMM scratch (h low part)
   float* y;           // GEMM scratch
   int gemv_pairs;     // capacity of h in pairs
   hipEvent_t ev_consumed;
@@ -169,9 +170,10 @@ double down_weight_bytes(const moe_layer* L) {
   return b;
 }
 
-moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, float* y,
-                   int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out, int accumulate,
-                   const int32_t* wave_of, int wave, int max_rows);
+moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
+                   float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
+                   int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
+                   int max_rows);
 
 moe_status self_check(moe_layer* L);
 
@@ -320,12 +322,13 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   };
   const size_t o_ids = take(4 * P), o_w = take(4 * P), o_sid = take(4 * P), o_wo = take(4 * P),
                o_oe = take(4 * E), o_os = take(4 * E), o_po = take(4 * (E + 1)),
-               o_pl = take(4 * P), o_cnt = take(16);
+               o_pl = take(4 * P), o_pp = take(4 * P), o_cnt = take(16);
   p->gemv_pairs = (int)std::min<size_t>(P, (size_t)MOE_MAX_GEMV_TOKENS * L->k);
   const size_t o_h = take(sizeof(float) * (size_t)p->gemv_pairs * L->I);
-  size_t o_hb = 0, o_y = 0;
+  size_t o_hb = 0, o_hl = 0, o_y = 0;
   if (gemm) {
     o_hb = take(2 * P * L->I);
+    o_hl = take(2 * P * L->I);
     o_y = take(4 * P * L->H);
   }
   auto cleanup = [&](moe_status s) {
@@ -342,9 +345,11 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->dev.order_slot = (int32_t*)(b + o_os);
   p->dev.pair_off = (int32_t*)(b + o_po);
   p->dev.pair_list = (int32_t*)(b + o_pl);
+  p->dev.pair_pos = (int32_t*)(b + o_pp);
   p->dev.counts = (int32_t*)(b + o_cnt);
   p->h = (float*)(b + o_h);
   p->hb = gemm ? (uint16_t*)(b + o_hb) : nullptr;
+  p->hb_lo = gemm ? (uint16_t*)(b + o_hl) : nullptr;
   p->y = gemm ? (float*)(b + o_y) : nullptr;
   const size_t hbytes = sizeof(PlanHdr) + 2 * sizeof(int32_t) * E;
   if (hipHostMalloc((void**)&p->hdr, hbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
@@ -504,8 +509,8 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
   const int K = L->K, D = p->info.num_distinct;
   const int o_lo = w * K, n_exp = std::min(K, D - o_lo);
   moe_plan* pm = const_cast<moe_plan*>(p);
-  moe_status st = run_ffn(L, p->dev, p->h, p->hb, p->y, o_lo, n_exp, T * L->k, T, x, out, w > 0,
-                          p->dev.wave_of, w, T);
+  moe_status st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, T * L->k, T, x, out,
+                          w > 0, p->dev.pair_pos, p->dev.wave_of, w, T);
   if (st) return st;
   HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
   L->fwd_recorded = true;
@@ -575,9 +580,10 @@ moe_status moe_timing_read(moe_layer* L, moe_timing* out) {
 
 namespace {
 
-moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, float* y, int o_lo,
-                   int n_exp, int n_pairs, int T, const void* x, float* out, int accumulate,
-                   const int32_t* wave_of, int wave, int max_rows) {
+moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
+                   float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
+                   int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
+                   int max_rows) {
   FfnArgs a{};
   a.fmt = L->fmt;
   a.E = L->E;
@@ -599,6 +605,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, flo
   a.accumulate = accumulate;
   a.h = h;
   a.hb = hb;
+  a.hb_lo = hb_lo;
   a.y = y;
   a.max_rows = max_rows;
   const double xb = (L->fmt == MOE_FMT_F32 ? 4.0 : 2.0);
@@ -627,7 +634,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, flo
     HIP_TRY(launch_gemm_down(a, L->compute));
     if ((st = timer_end(L, L->compute, &t2, MOE_T_GEMM_DOWN, dn_b, flop_dn))) return st;
     if ((st = timer_begin(L, L->compute, &t3))) return st;
-    HIP_TRY(launch_combine(a, wave_of, wave, L->compute));
+    HIP_TRY(launch_combine(a, pair_pos, wave_of, wave, L->compute));
     if ((st = timer_end(L, L->compute, &t3, MOE_T_COMBINE, 0.0, 0.0))) return st;
   }
   return MOE_OK;
@@ -695,8 +702,8 @@ moe_status self_check(moe_layer* L) {
         }
         float* o = (float*)(b + o_out) + ((size_t)perm * n + i) * H;
         // the one-pair plan addresses token 0 as pair 0 (k may exceed 1: pair 0 / k == 0)
-        result = run_ffn(L, dev, (float*)(b + o_h), nullptr, nullptr, 0, 1, 1, 1, b + o_x, o, 0,
-                         nullptr, 0, 1);
+        result = run_ffn(L, dev, (float*)(b + o_h), nullptr, nullptr, nullptr, 0, 1, 1, 1, b + o_x,
+                         o, 0, nullptr, nullptr, 0, 1);
         if (!result && hipStreamSynchronize(L->compute) != hipSuccess)
           result = fail(MOE_ERR_HIP, "self-check forward failed");
       }

@@ -50,6 +50,7 @@ struct PlanDev {
   int32_t* order_slot;   // [E] slot of each during its wave
   int32_t* pair_off;     // [E+1] CSR offsets over wave order
   int32_t* pair_list;    // [T*k] pair index t*k+j, grouped by expert, ascending
+  int32_t* pair_pos;     // [T*k] inverse of pair_list: CSR position of pair t*k+j
   int32_t* counts;       // [4]: num_distinct, num_hits, num_waves, num_tokens
 };
 
@@ -118,7 +119,8 @@ struct FfnArgs {
   float* out;          // [T][H]
   int accumulate;      // 0: write out, 1: add to out
   float* h;            // GEMV scratch fp32 [T*k][I], indexed by CSR position
-  uint16_t* hb;        // GEMM scratch bf16 [T*k][I]
+  uint16_t* hb;        // GEMM scratch bf16 [T*k][I], high part of h
+  uint16_t* hb_lo;     // GEMM scratch bf16 [T*k][I], low part of h
   float* y;            // GEMM scratch fp32 [T*k][H]
   int max_rows;        // upper bound on pairs of one expert in this wave (GEMM)
 };
@@ -129,7 +131,8 @@ bool ffn_shape_supported(int fmt, int H, int I);
 
 hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s);
-hipError_t launch_combine(const FfnArgs& a, const int32_t* wave_of, int wave, hipStream_t s);
+hipError_t launch_combine(const FfnArgs& a, const int32_t* pair_pos, const int32_t* wave_of, int wave,
+                          hipStream_t s);
 bool gemm_shape_supported(int H, int I);
 
 hipError_t launch_residual(const uint16_t* x_in, const float* out, uint16_t* x_out, int64_t n,

@@ -276,7 +276,11 @@ __global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ 
     const int p = c + lane;
     const bool m = p < P && ids[p] == e;
     const unsigned long long mask = __ballot(m);
-    if (m) dev.pair_list[base + running + __popcll(mask & below)] = p;
+    if (m) {
+      const int q = base + running + __popcll(mask & below);
+      dev.pair_list[q] = p;
+      dev.pair_pos[p] = q;
+    }
     running += __popcll(mask);
   }
 }

@@ -75,48 +75,51 @@ class PagedLayer:
     def step(self, logits, x, compute=True):
         """logits float32 [B,E], x [B,H] (values) -> (out float64 [B,H], ids, w, plan).
 
-        compute=False plans and pages in exactly the same way but skips the
-        expert math (out is None), for long sequences checked on samples.
+        Per wave, the wave's experts are taken in wave order; each one is
+        decoded from ITS SLOT and applied to all tokens routed to it in this
+        wave, out[t] += w_tj * y. compute=False plans and pages in exactly the
+        same way but skips the expert math (out is None), for long sequences
+        checked on samples.
         """
         ids, w = route(logits, self.top_k)
         plan = self.table.plan(ids, on_page_in=None)
         # replay the page-ins in wave order: a later wave may reuse a slot that
         # an earlier wave of the same step computed from
         x = np.asarray(x, dtype=np.float64)
-        B = x.shape[0]
-        out = np.zeros((B, self.H), dtype=np.float64)
-        for wave_i, wave in enumerate(plan.waves):
+        out = np.zeros((x.shape[0], self.H), dtype=np.float64) if compute else None
+        for wave in plan.waves:
             for e, s in wave.misses:
                 self._page_in(e, s)
-            if not compute:
-                continue
-            for b in range(B):
-                for j in range(self.top_k):
-                    if plan.wave_of[b, j] != wave_i:
-                        continue
-                    wg, wu, wd = self._slot_weights(int(plan.slot_ids[b, j]))
-                    out[b] += w[b, j] * swiglu_expert(wg, wu, wd, x[b])
-        return (out if compute else None), ids, w, plan
+            if compute:
+                for e, s in zip(wave.experts, wave.slots):
+                    self._apply(self._slot_weights(s), e, ids, w, x, out)
+        return out, ids, w, plan
+
+    @staticmethod
+    def _apply(weights, e, ids, w, x, out):
+        """out[t] += w_tj * expert_e(x_t) for every (t, j) routed to expert e."""
+        rows, cols = np.nonzero(ids == e)          # each token routes to e at most once
+        if rows.size == 0:
+            return
+        wg, wu, wd = weights
+        y = swiglu_expert(wg, wu, wd, x[rows])
+        out[rows] += w[rows, cols][:, None] * y
 
     def unpaged_forward(self, logits, x):
-        """The same layer computed straight from the host store (no slots)."""
+        """The same layer computed straight from the host store (no slots),
+        in the same order as step(); the wave of each expert only depends on
+        the table, so it is taken from a dry run of the planner."""
         ids, w = route(logits, self.top_k)
         x = np.asarray(x, dtype=np.float64)
-        B = x.shape[0]
-        out = np.zeros((B, self.H), dtype=np.float64)
-        # same summation order as step(): by wave, then token, then j. The wave
-        # of each (b, j) only depends on the table, so take it from a dry run.
+        out = np.zeros((x.shape[0], self.H), dtype=np.float64)
         dry = SlotTable(self.E, self.K, self.table.initial_fill)
         dry.slot_expert, dry.expert_slot = self.table.slot_expert.copy(), self.table.expert_slot.copy()
         dry.stamp, dry.clock = self.table.stamp.copy(), self.table.clock
         plan = dry.plan(ids)
-        for wave_i in range(plan.n_waves):
-            for b in range(B):
-                for j in range(self.top_k):
-                    if plan.wave_of[b, j] != wave_i:
-                        continue
-                    wg, wu, wd = formats.decode_record(self.store[ids[b, j]], self.fmt, self.H, self.I)
-                    out[b] += w[b, j] * swiglu_expert(wg, wu, wd, x[b])
+        for wave in plan.waves:
+            for e in wave.experts:
+                self._apply(formats.decode_record(self.store[e], self.fmt, self.H, self.I),
+                            e, ids, w, x, out)
         return out
 
 

@@ -1,0 +1,189 @@
+"""GPU edge cases of the boundary: empty steps, K < top_k, K = E, the largest
+E and top_k, error codes, the startup self-check, ordering under separate
+streams (NaN canary in victim slots), and bitwise reproducibility."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_paging_amd as ewp
+import workloads as W
+from workloads import gen
+
+from gpu_harness import PairedLayer, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny_fill(E, H, I, fmt=gen.F32, seed=0):
+    rng = np.random.default_rng(seed)
+    recs = [gen.encode_record(fmt, (rng.standard_normal((2 * I, H)) * 0.05).astype(np.float32),
+                              (rng.standard_normal((H, I)) * 0.05).astype(np.float32)) for _ in range(E)]
+
+    def fill(a):
+        for e in range(E):
+            a[e] = recs[e]
+    return fill
+
+
+def _seq(E, B, steps, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((steps, B, E)).astype(np.float32)
+    x = rng.standard_normal((steps, B, 64)).astype(np.float32)
+    return logits, x
+
+
+def test_empty_step_then_normal():
+    say("case: T=0 route")
+    p = PairedLayer(8, 2, 64, 32, 4, gen.F32, _tiny_fill(8, 64, 32), max_tokens=4)
+    lg = torch.zeros(0, 8, dtype=torch.float32, device="cuda")
+    info = p.gpu.route(p.plan, lg, num_tokens=0)
+    assert info["num_waves"] == 0 and info["num_distinct"] == 0
+    logits, x = _seq(8, 3, 6, 1)
+    p.run(logits, x, check_state_every=1)
+    p.close()
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
+def test_small_and_full_tables(K):
+    say("case: E=8 k=3 K=%d B=2 (K < top_k gives multi-wave steps)" % K)
+    p = PairedLayer(8, 3, 64, 32, K, gen.F32, _tiny_fill(8, 64, 32, seed=K), max_tokens=2)
+    logits, x = _seq(8, 2, 20, K)
+    p.run(logits, x, check_state_every=1)
+    st = p.gpu.stats()
+    if K == 8:
+        # K = E: after every expert has been seen there are no more misses
+        assert st["misses"] <= 8
+    if K < 3:
+        assert st["waves"] > st["steps"]
+    p.close()
+
+
+def test_largest_e_and_top_k():
+    E, k = 1024, 32
+    say("case: E=1024 k=32 K=100 B=3")
+    p = PairedLayer(E, k, 64, 32, 100, gen.F32, _tiny_fill(E, 64, 32), max_tokens=3)
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((5, 3, E)).astype(np.float32)
+    logits[:, :, :50] = np.round(logits[:, :, :50])         # plenty of exact ties
+    x = rng.standard_normal((5, 3, 64)).astype(np.float32)
+    p.run(logits, x, check_state_every=1)
+    p.close()
+
+
+def test_separate_streams_and_nan_canary():
+    """Compute, copy and route on three streams; before each page-in the victim
+    slots are filled with NaN on the copy stream. A forward that read a slot
+    before its copy landed would produce NaN."""
+    cfg = W.CONFIGS[2]
+    say("case: bf16 layer on 3 streams with NaN-poisoned victims, 24 steps")
+    s = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+    p = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt,
+                    lambda a: gen.expert_store(cfg, out=a), max_tokens=1, streams=s)
+    logits, x = gen.decode_inputs(cfg, 1, steps=24)
+    rec = p.gpu.record_bytes
+    slots = p.slots.view(cfg.K, rec)
+
+    def poison(pl, t, info):
+        # after the previous forward (compute stream), before this page-in (copy stream)
+        ev = torch.cuda.Event()
+        ev.record(s[0])
+        s[1].wait_event(ev)
+        for w in range(info["num_waves"]):
+            _, _, misses = pl.plan.wave(w)
+            with torch.cuda.stream(s[1]):
+                for e, sl in misses:
+                    slots[sl].fill_(0xFF)
+    p.run(logits, x, on_step=poison, sample=lambda t: t % 6 == 5)
+    p.close()
+
+
+def test_bitwise_reproducible():
+    cfg = W.CONFIGS[3]
+    say("case: fp8 B=6 run twice -> identical bits")
+    outs = []
+    logits, x = gen.decode_inputs(cfg, 6, steps=6)
+    for _ in range(2):
+        p = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt,
+                        lambda a: gen.expert_store(cfg, out=a), max_tokens=6)
+        lg = torch.from_numpy(logits).cuda()
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        out = torch.empty(6, cfg.H, dtype=torch.float32, device="cuda")
+        res = []
+        for t in range(6):
+            p.gpu.step(p.plan, lg[t], xd[t], out)
+            res.append(out.cpu().numpy().copy())
+        outs.append(np.stack(res))
+        p.close()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+def test_self_check_pass_and_fail():
+    say("case: startup independence check")
+    E, H, I = 8, 64, 32
+    fill = _tiny_fill(E, H, I)
+    p = PairedLayer(E, 2, H, I, 4, gen.F32, fill, max_tokens=1, self_check=True)
+    p.close()
+
+    def aliased(a):                       # expert 1's record is a copy of expert 0's
+        fill(a)
+        a[1] = a[0]
+    with pytest.raises(ewp.MoeError) as ei:
+        PairedLayer(E, 2, H, I, 4, gen.F32, aliased, max_tokens=1, self_check=True)
+    assert ei.value.name == "MOE_ERR_SELFCHECK"
+
+
+def _desc(E=8, k=2, H=64, I=32, K=4, fmt=0, rb=None, host=None, slots=None, state=None):
+    rb = ewp.record_bytes(fmt, H, I) if rb is None else rb
+    return ewp._Desc(E, k, H, I, K, fmt, rb, ctypes.c_void_p(host), ctypes.c_void_p(slots),
+                     ctypes.c_void_p(state), 0, 0)
+
+
+def _init(d):
+    h = ctypes.c_void_p()
+    return ewp.lib().moe_layer_init(ctypes.byref(d), None, None, None, ctypes.byref(h)), h
+
+
+def test_error_codes():
+    say("case: error codes")
+    E, H, I, K = 8, 64, 32, 4
+    rb = ewp.record_bytes(0, H, I)
+    host = ewp.HostStore(E, rb)
+    slots, state = ewp.alloc_layer_buffers(E, K, rb, "cuda")
+    args = dict(host=host.ptr, slots=slots.data_ptr(), state=state.data_ptr())
+    assert _init(_desc(K=0, **args))[0] == -1
+    assert _init(_desc(K=9, **args))[0] == -1
+    assert _init(_desc(k=9, **args))[0] == -1
+    assert _init(_desc(rb=rb + 256, **args))[0] == -3
+    assert _init(_desc(fmt=7, **args))[0] == -3
+    assert _init(_desc(fmt=2, **args))[0] == -3          # FP8 needs multiples of 128
+    pageable = np.zeros(E * rb, dtype=np.uint8)
+    a2 = dict(args, host=pageable.ctypes.data)
+    assert _init(_desc(**a2))[0] == -2
+    st, h = _init(_desc(**args))
+    assert st == 0
+    layer = ewp.Layer.__new__(ewp.Layer)
+    layer.handle, layer.top_k, layer.E, layer.K = h, 2, E, K
+    plan = ewp.Plan(layer, 2)
+    x = torch.zeros(2, H, device="cuda")
+    out = torch.zeros(2, H, device="cuda")
+    lg = torch.randn(2, E, device="cuda")
+    with pytest.raises(ewp.MoeError) as ei:
+        ewp._check(ewp.lib().moe_forward(h, plan.handle, 0, ctypes.c_void_p(x.data_ptr()),
+                                         ctypes.c_void_p(out.data_ptr())))
+    assert ei.value.name == "MOE_ERR_STATE"
+    ewp._check(ewp.lib().moe_route(h, ctypes.c_void_p(lg.data_ptr()), 2, plan.handle))
+    with pytest.raises(ewp.MoeError) as ei:       # route again before the waves ran
+        ewp._check(ewp.lib().moe_route(h, ctypes.c_void_p(lg.data_ptr()), 2, plan.handle))
+    assert ei.value.name == "MOE_ERR_STATE"
+    with pytest.raises(ewp.MoeError) as ei:       # forward before page-in
+        ewp._check(ewp.lib().moe_forward(h, plan.handle, 0, ctypes.c_void_p(x.data_ptr()),
+                                         ctypes.c_void_p(out.data_ptr())))
+    assert ei.value.name == "MOE_ERR_STATE"
+    with pytest.raises(ewp.MoeError) as ei:       # more tokens than the plan holds
+        ewp._check(ewp.lib().moe_route(h, ctypes.c_void_p(lg.data_ptr()), 3, plan.handle))
+    assert ei.value.name in ("MOE_ERR_INVALID_ARG", "MOE_ERR_STATE")
+    plan.close()
+    layer.close()                                  # destroys h exactly once
+    host.free()

@@ -1,0 +1,138 @@
+"""GPU parity of the prefill path (token-grouped MFMA GEMMs + combine) against
+the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_paging_amd as ewp
+import workloads as W
+from oracle.layer import PagedLayer, bf16_rne, run_stack
+from workloads import gen
+
+from gpu_harness import PairedLayer, rel_err, say, x_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_layer_check(p, logits, x, tol=2e-2):
+    T = logits.shape[0]
+    dev = p.dev
+    lg = torch.from_numpy(np.ascontiguousarray(logits)).to(dev)
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    out = torch.empty(T, p.H, dtype=torch.float32, device=dev)
+    info = p.gpu.route(p.plan, lg)
+    for w in range(info["num_waves"]):
+        p.gpu.page_in(p.plan, w)
+        p.gpu.forward(p.plan, w, xd, out)
+    o_ref, ids_ref, w_ref, p_ref = p.ref.step(logits, x_values(x, p.fmt))
+    p.check_plan(ids_ref, w_ref, p_ref, T)
+    torch.cuda.synchronize()
+    e = rel_err(out.cpu().numpy(), o_ref)
+    say("prefill T=%d waves=%d misses=%d rel err %.3g" % (T, info["num_waves"], info["num_misses"], e))
+    assert e <= tol
+    p.check_state()
+    return info
+
+
+def test_prefill_qwen_layer_2048_tokens():
+    cfg = W.CONFIGS[5]
+    say("case: prefill bf16 layer E=128 k=8 H=2048 I=768 K=92 warm, 2048 tokens")
+    p = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt,
+                    lambda a: gen.expert_store(cfg, out=a), max_tokens=2048, initial_fill=True)
+    logits, x0 = gen.prefill_inputs(cfg, layers=1)
+    info = _prefill_layer_check(p, logits[0], x0)
+    assert info["num_waves"] == 2 and info["num_misses"] == 36
+    p.close()
+
+
+@pytest.mark.parametrize("T,E,k,H,I,K", [(1000, 64, 4, 512, 256, 20), (65, 32, 8, 256, 128, 12),
+                                         (300, 16, 2, 768, 384, 16)])
+def test_prefill_ragged(T, E, k, H, I, K):
+    say("case: prefill ragged T=%d E=%d k=%d H=%d I=%d K=%d" % (T, E, k, H, I, K))
+    rng = np.random.default_rng(T + E)
+    recs = [gen.encode_record(gen.BF16, (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32),
+                              (rng.standard_normal((H, I)) * 0.02).astype(np.float32)) for _ in range(E)]
+
+    def fill(a):
+        for e in range(E):
+            a[e] = recs[e]
+    p = PairedLayer(E, k, H, I, K, gen.BF16, fill, max_tokens=T)
+    for step in range(2):
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        x = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        _prefill_layer_check(p, logits, x)
+    p.close()
+
+
+def test_prefill_stack_residual():
+    """Three bf16 layers at full shape with the device residual, against the
+    oracle's stack run from the same x0. Each layer's MoE output must meet the
+    bf16 output tolerance. The hidden state is bf16, so where the two sides'
+    sums straddle a rounding boundary they differ by one bf16 ulp; element-wise
+    the final hidden state may differ by the last layer's output tolerance plus
+    one ulp of each intermediate hidden value, and such flips must be rare."""
+    cfg = W.CONFIGS[5]
+    L, T = 3, 512
+    say("case: prefill stack of %d bf16 layers, %d tokens" % (L, T))
+    logits, x0 = gen.prefill_inputs(cfg, layers=L, tokens=T, salt=7)
+    pool = gen.expert_store(cfg)
+    layers, refs = [], []
+    for l in range(L):
+        perm = gen.layer_permutation(cfg, l)
+        p = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt,
+                        lambda a, perm=perm: a.__setitem__(slice(None), pool[perm]),
+                        max_tokens=T, initial_fill=True)
+        layers.append(p)
+        refs.append(p.ref)
+    dev = "cuda:0"
+    x = torch.from_numpy(np.ascontiguousarray(x0).view(np.int16)).to(dev)
+    out = torch.empty(T, cfg.H, dtype=torch.float32, device=dev)
+    lg = torch.from_numpy(logits).to(dev)
+    outs = []
+    for l, p in enumerate(layers):
+        info = p.gpu.route(p.plan, lg[l])
+        for w in range(info["num_waves"]):
+            p.gpu.page_in(p.plan, w)
+            p.gpu.forward(p.plan, w, x, out)
+        outs.append(out.cpu().numpy().copy())
+        ewp.residual_bf16(x, out, x)
+    torch.cuda.synchronize()
+    xf_ref, outs_ref, plans = run_stack(refs, [logits[l] for l in range(L)], x_values(x0, cfg.fmt))
+    for l in range(L):
+        e = rel_err(outs[l], outs_ref[l])
+        say("layer %d MoE output rel err %.3g" % (l, e))
+        assert e <= 2e-2
+    got = gen.bf16_bits_to_f32(x.cpu().numpy().view(np.uint16)).astype(np.float64)
+    # bound per element: the output tolerance of the last layer plus one bf16
+    # ulp of every intermediate hidden value the rounding may have flipped
+    xl, bound = x_values(x0, cfg.fmt), 2e-2 * np.sqrt(np.mean(outs_ref[-1] ** 2))
+    for o in outs_ref:
+        xl = bf16_rne(xl + o)
+        bound = bound + np.exp2(np.floor(np.log2(np.maximum(np.abs(xl), 2.0 ** -126))) - 7)
+    d = np.abs(got - xf_ref)
+    say("hidden: max diff / bound %.3g, %.2e of elements differ" % ((d / bound).max(), (d > 0).mean()))
+    assert np.all(d <= bound)
+    assert (d > 0).mean() < 2e-2
+    for p in layers:
+        p.check_state()
+        p.close()
+
+
+def test_residual_kernel_exact():
+    rng = np.random.default_rng(3)
+    n = 4096 * 3 + 2                                   # ragged tail
+
+    def mag(v):                                        # |v| in [1/16, 8): sums of two stay exact in fp32
+        return np.where(np.abs(v) < 1 / 16, np.sign(v + 1e-30) / 16, v)
+    xb = gen.f32_to_bf16_bits(mag(rng.uniform(-8, 8, n)).astype(np.float32))
+    # out values whose fp32 sum with x is exact, so both sides round the same value
+    o = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(mag(rng.uniform(-8, 8, n)).astype(np.float32)))
+    dev = "cuda:0"
+    xd = torch.from_numpy(xb.view(np.int16)).to(dev)
+    od = torch.from_numpy(o.astype(np.float32)).to(dev)
+    yd = torch.empty_like(xd)
+    ewp.residual_bf16(xd, od, yd)
+    torch.cuda.synchronize()
+    ref = bf16_rne(gen.bf16_bits_to_f32(xb).astype(np.float64) + o.astype(np.float64))
+    got = gen.bf16_bits_to_f32(yd.cpu().numpy().view(np.uint16)).astype(np.float64)
+    assert np.array_equal(got, ref)

@@ -230,10 +230,9 @@ def correlated_sets(rng, steps, E, k, p):
 
 
 def uniform_sets(rng, steps, E, k):
-    sets = np.zeros((steps, k), dtype=np.int32)
-    for t in range(steps):
-        sets[t] = np.sort(rng.choice(E, size=k, replace=False))
-    return sets
+    """[steps][k] sorted uniform k-subsets of E (first k of a random permutation)."""
+    perm = np.argsort(rng.random((steps, E)), axis=1)[:, :k]
+    return np.sort(perm, axis=1).astype(np.int32)
 
 
 def logits_from_sets(rng, sets, E):
@@ -243,10 +242,12 @@ def logits_from_sets(rng, sets, E):
     z = rng.standard_normal(shape + (E,)).astype(np.float32)
     flat = z.reshape(-1, E)
     fs = sets.reshape(-1, sets.shape[-1])
-    for r in range(flat.shape[0]):
-        flat[r, fs[r]] += ROUTE_SHIFT
-        others = np.setdiff1d(np.arange(E), fs[r])
-        assert flat[r, fs[r]].min() > flat[r, others].max()
+    member = np.zeros(flat.shape, dtype=bool)
+    np.put_along_axis(member, fs, True, axis=1)
+    flat[member] += ROUTE_SHIFT
+    lo_in = np.where(member, flat, np.inf).min(axis=1)
+    hi_out = np.where(member, -np.inf, flat).max(axis=1)
+    assert np.all(lo_in > hi_out)
     return flat.reshape(shape + (E,))
 
 
@@ -296,4 +297,16 @@ def stack_inputs(cfg, steps=None, routing=None):
                 sets[:, l, b] = uniform_sets(st["routing"], steps, cfg.E, cfg.top_k)
     logits = logits_from_sets(st["routing"], sets, cfg.E)
     x0 = hidden_states(st["hidden"], (steps, B, cfg.H), cfg.fmt)
+    return logits, x0
+
+
+def prefill_inputs(cfg, layers=None, tokens=None, salt=0):
+    """Prefill inputs: logits float32 [layers][T][E] (fresh uniform k of E per
+    token and layer), x0 [T][H] hidden states."""
+    layers = cfg.layers if layers is None else layers
+    T = cfg.tokens if tokens is None else tokens
+    st = streams(cfg.cid, 100 + salt)
+    sets = uniform_sets(st["routing"], layers * T, cfg.E, cfg.top_k).reshape(layers, T, cfg.top_k)
+    logits = logits_from_sets(st["routing"], sets, cfg.E)
+    x0 = hidden_states(st["hidden"], (T, cfg.H), cfg.fmt)
     return logits, x0
