@@ -1,17 +1,28 @@
 """Benchmark of the Paged Experts hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode-bf16|...]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [...]
 
-A step is one pass of the whole decode hot path over one batch: router ->
-slot plan (host sees the plan) -> page-in of the misses (pinned host -> slot,
-copy stream) -> expert FFN over the slots (compute stream), for every wave.
+Workloads (synthetic, seeded, Qwen3-30B-A3B shapes: 128 experts, top-8,
+hidden 2048, MoE intermediate 768):
+  decode-bf16  (default) one bf16 MoE layer, K=40 slots, batch-1 decode,
+               correlated routing p=0.75, cold table. A step is one token:
+               router -> slot plan (host sees the plan) -> page-in of the
+               misses (pinned host -> slots, copy stream) -> expert FFN over
+               the slots (compute stream), every wave.
+  decode-fp8   the same layer with block-FP8 experts, --batch B
+  stack-int4   48 int4 layers, K=92 each, batch-1 decode; a step is one token
+               through all 48 layers with the bf16 residual; --routing
+               uniform for the control run; --lookahead to route/page-in
+               layer l+1 while layer l computes
+  prefill-bf16 one 2048-token chunk through 48 bf16 layers, K=92, warm
+               tables, uniform routing; a step is one chunk
 Inputs (router logits, hidden states) are resident in HBM before the timed
-region; the expert store lives in pinned host memory by design of the method.
+region; expert stores live in pinned host memory by design of the method.
 
-Prints one JSON line: the metric value is decode tokens/s; `roofline` is the
-dominant kernel's achieved HBM bandwidth measured with HIP events on the
-stream it runs on; `cpu_baseline` is the float64 CPU oracle timed on a
-bounded sample of the same workload.
+Prints ONE JSON line: `value` is tokens/s of the workload; `roofline` is the
+dominant kernel's achieved rate over the timed region, from HIP events
+recorded on the stream the kernel runs on, against the MI355X peak;
+`cpu_baseline` is the float64 CPU oracle timed on a bounded sample.
 """
 import argparse
 import hashlib
@@ -28,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode tok/s at batch 1 (Qwen3-30B-A3B shapes) + achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FMT_NAME = {0: "f32", 1: "bf16", 2: "fp8", 3: "int4"}
 
 
 def log(*a):
@@ -36,10 +48,25 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "expert_weight_paging_amd", "csrc"))):
-        with open(os.path.join(ROOT, "expert_weight_paging_amd", "csrc", f), "rb") as fh:
+    d = os.path.join(ROOT, "expert_weight_paging_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_name, workload):
+    """HBM bytes per launch from the committed PMC summary, only if it was taken
+    on the current kernel sources (else null)."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("workloads", {}).get(workload, {}).get(kernel_name)
+    return None if not k else k.get("bytes_per_launch")
 
 
 def measured_peaks(torch, dev):
@@ -70,9 +97,35 @@ def measured_peaks(torch, dev):
     return {"hbm_copy_read_plus_write_GBps": round(hbm, 1), "h2d_pinned_GBps": round(h2d, 2)}
 
 
-# ---------------------------------------------------------------- decode workloads
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return 1
 
-def decode_bench(args, torch, dev):
+
+def merge_timing(ts):
+    out = {}
+    for t in ts:
+        for k, v in t.items():
+            o = out.setdefault(k, {"count": 0, "ms": 0.0, "bytes": 0.0, "flops": 0.0})
+            for f in o:
+                o[f] += v[f]
+    return out
+
+
+def sum_stats(layers):
+    tot = {}
+    for l in layers:
+        for k, v in l.stats().items():
+            tot[k] = tot.get(k, 0) + v
+    return tot
+
+
+# ---------------------------------------------------------------- decode: one layer
+
+def bench_decode(args, torch, dev):
     import expert_weight_paging_amd as ewp
     import workloads as W
     from workloads import gen
@@ -106,77 +159,261 @@ def decode_bench(args, torch, dev):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     s1 = layer.stats()
-    log("timed %d steps in %.3f s" % (args.steps, el))
-
-    # roofline pass: same workload replayed from the start with event timing
+    # roofline pass: the timed steps again, same table state, with events
     layer.reset()
+    run(0, args.warmup)
     layer.timing_enable(True)
-    nprof = min(total, 128)
-    run(0, nprof)
+    run(args.warmup, args.steps)
     torch.cuda.synchronize()
     tm = layer.timing_read()
     layer.timing_enable(False)
-
-    misses = s1["misses"] - s0["misses"]
-    refs = s1["refs"] - s0["refs"]
-    res = {
-        "value": args.steps * B / el,
-        "ms_per_step": el / args.steps * 1e3,
-        "timing": tm,
-        "hits": s1["hits"] - s0["hits"], "misses": misses, "refs": refs,
-        "waves": s1["waves"] - s0["waves"],
-        "cfg": cfg, "B": B, "rec": rec,
-        "logits": logits, "x": x, "host": host,
-    }
     plan.close()
     layer.close()
+    d = {k: s1[k] - s0[k] for k in s1}
+    res = {"value": args.steps * B / el, "ms_per_step": el / args.steps * 1e3, "timing": tm,
+           "stats": d, "cfg": cfg, "B": B,
+           "workload": "one Qwen3-30B-A3B-shaped MoE layer, %s experts, E=%d top_k=%d hidden=%d "
+                       "intermediate=%d, K=%d resident slots, decode at batch %d, correlated routing "
+                       "p=%.2f, cold table" % (FMT_NAME[cfg.fmt], cfg.E, cfg.top_k, cfg.H, cfg.I,
+                                              cfg.K, B, cfg.p_keep)}
+
+    def cpu(budget):
+        from oracle.layer import PagedLayer
+        ref = PagedLayer(np.array(host.array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K)
+        n = 0
+        t0 = time.perf_counter()
+        while n < total and (time.perf_counter() - t0) < budget:
+            ref.step(logits[n], gen.bf16_bits_to_f32(x[n]).astype(np.float64))
+            n += 1
+        el = time.perf_counter() - t0
+        return {"value": n * B / el, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
+                "sample": "first %d decode steps (batch %d) of the same workload from a cold table: "
+                          "float64 numpy oracle incl. routing, LRU plan, record copies (host memcpy, "
+                          "no PCIe) and SwiGLU experts, %.1f s" % (n, B, el)}
+    res["cpu"] = cpu
+    res["cleanup"] = host.free
     return res
 
 
-def cpu_baseline_decode(res, budget_s):
-    """The float64 oracle, as it stands, on the first steps of the same workload."""
-    from oracle.layer import PagedLayer
+# ---------------------------------------------------------------- 48-layer stacks
+
+def build_stack(cfg, dev, torch, max_tokens, initial_fill):
+    import expert_weight_paging_amd as ewp
     from workloads import gen
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    cfg, B = res["cfg"], res["B"]
-    ref = PagedLayer(np.array(res["host"].array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K)
-    logits, x = res["logits"], res["x"]
-    n = 0
+    rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
+    log("generating the %d-record pool (%s)" % (cfg.E, FMT_NAME[cfg.fmt]))
+    pool = gen.pool_records(cfg)
+    compute, copy, route = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    hosts, layers, plans = [], [], []
     t0 = time.perf_counter()
-    while n < logits.shape[0] and (time.perf_counter() - t0) < budget_s:
-        ref.step(logits[n], gen.bf16_bits_to_f32(x[n]).astype(np.float64))
-        n += 1
+    for l in range(cfg.layers):
+        h = ewp.HostStore(cfg.E, rec)
+        gen.fill_layer_store(cfg, l, h.array, pool)
+        slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, dev)
+        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, h, slots, state,
+                      compute, copy, route, initial_fill=initial_fill)
+        hosts.append(h)
+        layers.append(L)
+        plans.append(ewp.Plan(L, max_tokens))
+    log("built %d layers: %.1f GB pinned, %.1f GB of slots, in %.1f s"
+        % (cfg.layers, cfg.layers * cfg.E * rec / 1e9, cfg.layers * cfg.K * rec / 1e9,
+           time.perf_counter() - t0))
+    return hosts, layers, plans, pool
+
+
+def bench_stack(args, torch, dev):
+    import expert_weight_paging_amd as ewp
+    import workloads as W
+    from workloads import gen
+
+    cfg = W.CONFIGS[4]
+    hosts, layers, plans, pool = build_stack(cfg, dev, torch, 1, False)
+    total = args.warmup + args.steps
+    logits, x0 = gen.stack_inputs(cfg, steps=total, routing=args.routing)
+    lg_d = torch.from_numpy(logits).to(dev)             # [steps][L][1][E]
+    x0_d = torch.from_numpy(x0.view(np.int16)).to(dev)  # [steps][1][H]
+    x = torch.empty(1, cfg.H, dtype=torch.int16, device=dev)
+    out = torch.empty(1, cfg.H, dtype=torch.float32, device=dev)
+
+    def run(t0, n):
+        for t in range(t0, t0 + n):
+            x.copy_(x0_d[t])
+            ewp.stack_forward(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+    s0 = sum_stats(layers)
+    t0 = time.perf_counter()
+    run(args.warmup, args.steps)
+    torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    return {"value": n * B / el, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d decode steps (batch %d) of the same workload from a cold table, "
-                      "float64 numpy oracle incl. routing, LRU plan, record copies and SwiGLU "
-                      "experts, %.1f s" % (n, B, el)}
+    s1 = sum_stats(layers)
+    for L in layers:
+        L.reset()
+    run(0, args.warmup)
+    for L in layers:
+        L.timing_enable(True)
+    run(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    tm = merge_timing([L.timing_read() for L in layers])
+    d = {k: s1[k] - s0[k] for k in s1}
+    res = {"value": args.steps / el, "ms_per_step": el / args.steps * 1e3, "timing": tm, "stats": d,
+           "cfg": cfg, "B": 1,
+           "workload": "48-layer Qwen3-30B-A3B-shaped MoE stack (attention omitted), int4 asym g128 "
+                       "experts, E=128 top_k=8 hidden=2048 intermediate=768, K=92 slots per layer, "
+                       "batch-1 decode, %s routing%s, %s, cold tables"
+                       % ("correlated p=0.75" if args.routing == "correlated" else "uniform",
+                          "", "one-layer lookahead" if args.lookahead else "strict layer order")}
+
+    def cpu(budget):
+        from oracle.layer import PagedLayer
+        refs = [PagedLayer(pool[gen.layer_permutation(cfg, l)], cfg.fmt, cfg.E, cfg.top_k, cfg.H,
+                           cfg.I, cfg.K) for l in range(4)]
+        xv = gen.bf16_bits_to_f32(x0[0]).astype(np.float64)
+        from oracle.layer import bf16_rne
+        t0 = time.perf_counter()
+        nl = 0
+        for l in range(4):
+            o, *_ = refs[l].step(logits[0, l], xv)
+            xv = bf16_rne(xv + o)
+            nl += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        el = time.perf_counter() - t0
+        per_token = el / nl * cfg.layers
+        return {"value": 1.0 / per_token, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
+                "sample": "token 0 through the first %d of 48 layers (cold tables) with the float64 "
+                          "numpy oracle, %.1f s, scaled to 48 layers" % (nl, el)}
+    res["cpu"] = cpu
+
+    def cleanup():
+        for p in plans:
+            p.close()
+        for L in layers:
+            L.close()
+        for h in hosts:
+            h.free()
+    res["cleanup"] = cleanup
+    return res
 
 
-def traffic_from_profiles(kernel_name, hash_now):
-    """HBM bytes per launch from the committed PMC summary, if taken on this source."""
-    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if not os.path.exists(p):
-        return None
-    with open(p) as f:
-        d = json.load(f)
-    k = d.get("kernels", {}).get(kernel_name)
-    if not k or d.get("source_hash") != hash_now:
-        return None
-    return k.get("bytes_per_launch")
+def bench_prefill(args, torch, dev):
+    import expert_weight_paging_amd as ewp
+    import workloads as W
+    from workloads import gen
+
+    cfg = W.CONFIGS[5]
+    T = cfg.tokens
+    hosts, layers, plans, pool = build_stack(cfg, dev, torch, T, True)
+    total = args.warmup + args.steps
+    chunks = [gen.prefill_inputs(cfg, salt=c) for c in range(total)]
+    x_d = torch.empty(T, cfg.H, dtype=torch.int16, device=dev)
+    out = torch.empty(T, cfg.H, dtype=torch.float32, device=dev)
+    lg_d = [torch.from_numpy(c[0]).to(dev) for c in chunks]
+    x0_d = [torch.from_numpy(c[1].view(np.int16)).to(dev) for c in chunks]
+
+    def run(c0, n):
+        for c in range(c0, c0 + n):
+            x_d.copy_(x0_d[c])
+            ewp.stack_forward(layers, plans, lg_d[c], x_d, out, lookahead=args.lookahead)
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+    s0 = sum_stats(layers)
+    t0 = time.perf_counter()
+    run(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    s1 = sum_stats(layers)
+    for L in layers:
+        L.reset()
+    run(0, args.warmup)
+    for L in layers:
+        L.timing_enable(True)
+    run(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    tm = merge_timing([L.timing_read() for L in layers])
+    d = {k: s1[k] - s0[k] for k in s1}
+    res = {"value": args.steps * T / el, "ms_per_step": el / args.steps * 1e3, "timing": tm,
+           "stats": d, "cfg": cfg, "B": T,
+           "workload": "prefill: one 2048-token chunk through a 48-layer Qwen3-30B-A3B-shaped bf16 "
+                       "MoE stack (attention omitted), E=128 top_k=8 hidden=2048 intermediate=768, "
+                       "K=92 slots per layer warm with experts 0..91, uniform routing"}
+
+    def cpu(budget):
+        from oracle.layer import PagedLayer, bf16_rne
+        lg, x0 = chunks[0]
+        xv = gen.bf16_bits_to_f32(x0).astype(np.float64)
+        t0 = time.perf_counter()
+        nl = 0
+        for l in range(cfg.layers):
+            ref = PagedLayer(pool[gen.layer_permutation(cfg, l)], cfg.fmt, cfg.E, cfg.top_k, cfg.H,
+                             cfg.I, cfg.K, initial_fill=True)
+            o, *_ = ref.step(lg[l], xv)
+            xv = bf16_rne(xv + o)
+            nl += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        el = time.perf_counter() - t0
+        return {"value": T / (el / nl * cfg.layers), "unit": "tok/s", "cores": oracle_threads(),
+                "kind": "oracle",
+                "sample": "chunk 0 (2048 tokens) through the first %d of 48 layers with the float64 "
+                          "numpy oracle, %.1f s, scaled to 48 layers" % (nl, el)}
+    res["cpu"] = cpu
+
+    def cleanup():
+        for p in plans:
+            p.close()
+        for L in layers:
+            L.close()
+        for h in hosts:
+            h.free()
+    res["cleanup"] = cleanup
+    return res
+
+
+# ---------------------------------------------------------------- report
+
+def roofline(res, workload):
+    tm = res["timing"]
+    if workload == "prefill-bf16":
+        kinds = [k for k in ("gemm_up", "gemm_down") if tm[k]["count"]]
+        dom = max(kinds, key=lambda k: tm[k]["ms"])
+        sec = tm[dom]["ms"] * 1e-3
+        flops = tm[dom]["flops"] / sec / 1e12
+        gbps = tm[dom]["bytes"] / sec / 1e9
+        kname = "grouped_gemm_kernel<%s>" % ("true" if dom == "gemm_up" else "false")
+        return {"bound": "mfma", "kernel": kname, "achieved": round(flops, 1),
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(flops / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profiles(kname, workload),
+                "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
+                "algorithmic_flops_per_launch": tm[dom]["flops"] / tm[dom]["count"],
+                "weight_GBps": round(gbps, 1), "weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    kinds = [k for k in ("ffn_up", "ffn_down") if tm[k]["count"]]
+    dom = max(kinds, key=lambda k: tm[k]["ms"])
+    sec = tm[dom]["ms"] * 1e-3
+    achieved = tm[dom]["bytes"] / sec / 1e9
+    kname = {"ffn_up": "ffn_up_kernel", "ffn_down": "ffn_down_kernel"}[dom]
+    both = (tm["ffn_up"]["bytes"] + tm["ffn_down"]["bytes"]) / ((tm["ffn_up"]["ms"] + tm["ffn_down"]["ms"]) * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles(kname, workload),
+            "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
+            "algorithmic_bytes_per_launch": tm[dom]["bytes"] / tm[dom]["count"],
+            "ffn_up_plus_down_GBps": round(both, 1)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", default="decode-bf16", choices=["decode-bf16", "decode-fp8"])
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode-bf16",
+                    choices=["decode-bf16", "decode-fp8", "stack-int4", "prefill-bf16"])
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--routing", default="correlated", choices=["correlated", "uniform"])
+    ap.add_argument("--lookahead", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
@@ -185,25 +422,21 @@ def main():
         print("bench.py measures one GPU only: the Paged Experts path is single-GPU and this "
               "build has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    defaults = {"decode-bf16": (256, 32), "decode-fp8": (256, 32), "stack-int4": (128, 16),
+                "prefill-bf16": (3, 1)}[args.workload]
+    args.steps = defaults[0] if args.steps is None else args.steps
+    args.warmup = defaults[1] if args.warmup is None else args.warmup
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
-    res = decode_bench(args, torch, dev)
-    tm = res["timing"]
-    cfg = res["cfg"]
-    # dominant kernel by measured time
-    kinds = [k for k in ("ffn_up", "ffn_down") if tm[k]["count"]]
-    dom = max(kinds, key=lambda k: tm[k]["ms"])
-    avg_ms = tm[dom]["ms"] / tm[dom]["count"]
-    bytes_per_launch = tm[dom]["bytes"] / tm[dom]["count"]
-    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
-    ffn_bytes = tm["ffn_up"]["bytes"] + tm["ffn_down"]["bytes"]
-    ffn_ms = tm["ffn_up"]["ms"] + tm["ffn_down"]["ms"]
-    kname = {"ffn_up": "ffn_up_kernel", "ffn_down": "ffn_down_kernel"}[dom]
-    traffic = traffic_from_profiles(kname, kernel_source_hash())
+    fn = {"decode-bf16": bench_decode, "decode-fp8": bench_decode, "stack-int4": bench_stack,
+          "prefill-bf16": bench_prefill}[args.workload]
+    res = fn(args, torch, dev)
+    log("timed %d steps: %.3f ms/step" % (args.steps, res["ms_per_step"]))
+    tm, st, cfg = res["timing"], res["stats"], res["cfg"]
     pin = tm["page_in"]
     line = {
         "metric": METRIC,
@@ -216,38 +449,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {1: "bf16", 2: "fp8"}.get(cfg.fmt, "bf16"),
-        "data": "synthetic (seeded; correlated routing p=0.75, weights N(0,0.02))",
-        "config": {
-            "workload": "one Qwen3-30B-A3B-shaped MoE layer, %s experts, E=%d top_k=%d hidden=%d "
-                        "intermediate=%d, K=%d resident slots, decode at batch %d, cold start"
-                        % ({1: "bf16", 2: "block-FP8"}[cfg.fmt], cfg.E, cfg.top_k, cfg.H, cfg.I,
-                           cfg.K, res["B"]),
-            "batch": res["B"], "num_slots": cfg.K, "experts": cfg.E, "top_k": cfg.top_k,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "bound": "hbm", "kernel": kname,
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "avg_launch_us": round(avg_ms * 1e3, 3),
-            "algorithmic_bytes_per_launch": bytes_per_launch,
-        },
-        "ffn": {"achieved_GBps": round(ffn_bytes / (ffn_ms * 1e-3) / 1e9, 1),
-                "up_us": round(tm["ffn_up"]["ms"] / max(tm["ffn_up"]["count"], 1) * 1e3, 3),
-                "down_us": round(tm["ffn_down"]["ms"] / max(tm["ffn_down"]["count"], 1) * 1e3, 3)},
+        "dtype": FMT_NAME[cfg.fmt],
+        "data": "synthetic (seeded; %s routing, weights N(0,0.02))"
+                % ("correlated p=0.75" if cfg.routing == "correlated" and args.routing == "correlated"
+                   else "uniform"),
+        "config": {"workload": res["workload"], "batch": res["B"], "num_slots": cfg.K,
+                   "experts": cfg.E, "top_k": cfg.top_k, "layers": cfg.layers,
+                   "lookahead": bool(args.lookahead), "parallelism": "single GPU"},
+        "roofline": roofline(res, args.workload),
+        "kernels_us": {k: round(v["ms"] / v["count"] * 1e3, 3) for k, v in tm.items() if v["count"]},
         "page_in": {"GBps": round(pin["bytes"] / max(pin["ms"], 1e-9) / 1e6, 2),
-                    "waves_with_copies": pin["count"]},
-        "route_us": round(tm["route"]["ms"] / max(tm["route"]["count"], 1) * 1e3, 3),
-        "hit_rate": round(res["hits"] / max(res["refs"], 1), 4),
-        "misses_per_step": round(res["misses"] / args.steps, 4),
+                    "waves_with_copies": pin["count"], "bytes_per_step": st["bytes_paged"] / args.steps},
+        "hit_rate": round(st["hits"] / max(st["refs"], 1), 4),
+        "miss_rate_per_activation": round(st["misses"] / max(st["activations"], 1), 4),
+        "misses_per_step": round(st["misses"] / args.steps, 4),
+        "waves_per_layer_step": round(st["waves"] / max(st["steps"], 1), 4),
         "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (budget %.0f s)" % args.cpu_budget)
-        line["cpu_baseline"] = cpu_baseline_decode(res, args.cpu_budget)
-    res["host"].free()
+        line["cpu_baseline"] = res["cpu"](args.cpu_budget)
+    res["cleanup"]()
     print(json.dumps(line), flush=True)
 
 

@@ -81,6 +81,9 @@ EXPORTS = {
                                    ctypes.c_void_p, ctypes.c_void_p]),
     "moe_residual_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int64, ctypes.c_void_p]),
+    "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
     "moe_layer_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_Stats)]),
     "moe_layer_get_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]),
@@ -286,6 +289,18 @@ def residual_bf16(x_in, out, x_out, stream=None):
     """x_out = bf16_rne(x_in + out) on the device (x bf16, out float32)."""
     _check(lib().moe_residual_bf16(_ptr(x_in), _ptr(out), _ptr(x_out), int(out.numel()),
                                    _stream(stream)))
+
+
+def stack_forward(layers, plans, logits, x, out, lookahead=False):
+    """One batch through a stack of layers: out = MoE_l(x); x = bf16_rne(x + out).
+
+    logits: device float32 [L][T][E]; x: device bf16 (int16 view) [T][H], in
+    place; out: device float32 [T][H] scratch."""
+    n = len(layers)
+    la = (ctypes.c_void_p * n)(*[l.handle.value for l in layers])
+    pa = (ctypes.c_void_p * n)(*[p.handle.value for p in plans])
+    _check(lib().moe_stack_forward(la, pa, n, _ptr(logits), int(logits.shape[1]), _ptr(x), _ptr(out),
+                                   int(bool(lookahead))))
 
 
 def alloc_layer_buffers(num_experts, num_slots, rec_bytes, device="cuda"):

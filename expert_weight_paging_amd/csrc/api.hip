@@ -173,7 +173,7 @@ double down_weight_bytes(const moe_layer* L) {
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows);
+                   int max_rows, bool combine);
 
 moe_status self_check(moe_layer* L);
 
@@ -283,6 +283,7 @@ void moe_layer_destroy(moe_layer* L) {
   if (L->ev_fwd_done) (void)hipEventDestroy(L->ev_fwd_done);
   if (L->ev_copied) (void)hipEventDestroy(L->ev_copied);
   if (L->ev_routed) (void)hipEventDestroy(L->ev_routed);
+
   for (auto& t : L->pending) {
     (void)hipEventDestroy(t.a);
     (void)hipEventDestroy(t.b);
@@ -372,21 +373,38 @@ void moe_plan_destroy(moe_plan* p) {
   delete p;
 }
 
+namespace {
+moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after);
+}
+
 moe_status moe_route(moe_layer* L, const float* logits, int32_t T, moe_plan* p) {
+  return route_impl(L, logits, T, p, nullptr);
+}
+
+namespace {
+// `after`, if given, is an event the route stream waits for before routing.
+moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after) {
   if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
   if (p->layer != L) return fail(MOE_ERR_INVALID_ARG, "plan was created for another layer");
   if (T < 0 || T > p->max_tokens) return fail(MOE_ERR_INVALID_ARG, "num_tokens out of 0..max_tokens");
   if (T > 0 && !logits) return fail(MOE_ERR_INVALID_ARG, "null logits");
   if (L->cur_plan && L->next_fwd < L->n_waves)
     return fail(MOE_ERR_STATE, "previous step of this layer has waves not yet forwarded");
+
   if (p->consumed_recorded) HIP_TRY(hipStreamWaitEvent(L->route, p->ev_consumed, 0));
+  if (after) HIP_TRY(hipStreamWaitEvent(L->route, after, 0));
   TimerRec tr{};
   moe_status st = timer_begin(L, L->route, &tr);
   if (st) return st;
-  HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, L->route));
   const int32_t seq = ++p->seq;
-  HIP_TRY(launch_plan(p->dev.ids, T, L->k, L->E, L->K, L->state, p->dev, p->hdr_dev, seq, L->route));
-  HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, L->route));
+  if (route_small_ok(T, L->k)) {
+    HIP_TRY(launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, p->hdr_dev, seq,
+                                    L->route));
+  } else {
+    HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, L->route));
+    HIP_TRY(launch_plan(p->dev.ids, T, L->k, L->E, L->K, L->state, p->dev, p->hdr_dev, seq, L->route));
+    HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, L->route));
+  }
   st = timer_end(L, L->route, &tr, MOE_T_ROUTE, 0.0, 0.0);
   if (st) return st;
   HIP_TRY(hipEventRecord(L->ev_routed, L->route));
@@ -427,6 +445,8 @@ moe_status moe_route(moe_layer* L, const float* logits, int32_t T, moe_plan* p) 
   L->cur_plan = h.num_waves > 0 ? p : nullptr;
   return MOE_OK;
 }
+
+}  // namespace
 
 moe_status moe_plan_get_info(const moe_plan* p, moe_plan_info* out) {
   if (!p || !out) return fail(MOE_ERR_INVALID_ARG, "null plan or output");
@@ -505,13 +525,33 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
   if (((uintptr_t)x & 15) || ((uintptr_t)out & 15))
     return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_routed, 0));
-  if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
-  const int K = L->K, D = p->info.num_distinct;
+  const int K = L->K, D = p->info.num_distinct, nH = p->info.num_hits;
   const int o_lo = w * K, n_exp = std::min(K, D - o_lo);
+  // The wave order lists the experts that were resident first: they can be
+  // computed while the wave's misses are still being copied; only the missed
+  // experts wait for the copy ([SRV]-style overlap of transfer and compute).
+  const int n_res = std::max(0, std::min(nH, o_lo + n_exp) - o_lo);
   moe_plan* pm = const_cast<moe_plan*>(p);
-  moe_status st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, T * L->k, T, x, out,
-                          w > 0, p->dev.pair_pos, p->dev.wave_of, w, T);
-  if (st) return st;
+  const bool gemm = T > MOE_MAX_GEMV_TOKENS;
+  // Splitting costs extra launches; it only pays while this wave's copies are
+  // still in flight.
+  const bool copies_pending = n_res < n_exp && L->copy_recorded &&
+                              hipEventQuery(L->ev_copied) == hipErrorNotReady;
+  moe_status st;
+  if (n_res > 0 && copies_pending) {
+    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_res, T * L->k, T, x, out, w > 0,
+                 p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false);
+    if (st) return st;
+    HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
+    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo + n_res, n_exp - n_res, T * L->k, T, x,
+                 out, w > 0 || !gemm, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm);
+    if (st) return st;
+  } else {
+    if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
+    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, T * L->k, T, x, out, w > 0,
+                 p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm);
+    if (st) return st;
+  }
   HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
   L->fwd_recorded = true;
   HIP_TRY(hipEventRecord(pm->ev_consumed, L->compute));
@@ -529,6 +569,68 @@ moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out, in
     return fail(MOE_ERR_INVALID_ARG, "x must be 8-byte and out 16-byte aligned");
   HIP_TRY(launch_residual((const uint16_t*)x_in, out, (uint16_t*)x_out, n, (hipStream_t)stream));
   return MOE_OK;
+}
+
+moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, int32_t n,
+                             const float* logits, int32_t T, void* x, float* out, int32_t lookahead) {
+  if (!layers || !plans || n < 1) return fail(MOE_ERR_INVALID_ARG, "need n_layers >= 1 layers and plans");
+  if (T < 0 || (T > 0 && (!logits || !x || !out))) return fail(MOE_ERR_INVALID_ARG, "bad buffers");
+  const moe_layer* L0 = layers[0];
+  if (!L0) return fail(MOE_ERR_INVALID_ARG, "null layer");
+  for (int l = 0; l < n; ++l) {
+    const moe_layer* L = layers[l];
+    if (!L || !plans[l] || plans[l]->layer != L)
+      return fail(MOE_ERR_INVALID_ARG, "layer/plan " + std::to_string(l) + " missing or mismatched");
+    if (L->E != L0->E || L->k != L0->k || L->H != L0->H || L->fmt != L0->fmt ||
+        L->compute != L0->compute)
+      return fail(MOE_ERR_INVALID_ARG, "stack layers must share E, top_k, H, format and compute stream");
+    if (T > plans[l]->max_tokens) return fail(MOE_ERR_INVALID_ARG, "T exceeds a plan's max_tokens");
+  }
+  if (L0->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
+  if (T == 0) return MOE_OK;
+  const size_t lstride = (size_t)T * L0->E;
+  hipStream_t cs = L0->compute;
+  hipEvent_t resid_done = nullptr;
+  HIP_TRY(hipEventCreateWithFlags(&resid_done, hipEventDisableTiming));
+  moe_status st = MOE_OK;
+  auto run = [&]() -> moe_status {
+    moe_status r = route_impl(layers[0], logits, T, plans[0], nullptr);
+    if (r) return r;
+    if (lookahead) {
+      r = moe_page_in(layers[0], plans[0], 0);
+      if (r) return r;
+    }
+    for (int l = 0; l < n; ++l) {
+      moe_layer* L = layers[l];
+      moe_plan* P = plans[l];
+      if (lookahead && l + 1 < n) {
+        r = route_impl(layers[l + 1], logits + (l + 1) * lstride, T, plans[l + 1], nullptr);
+        if (r) return r;
+        r = moe_page_in(layers[l + 1], plans[l + 1], 0);
+        if (r) return r;
+      }
+      const int nw = P->info.num_waves;
+      for (int w = 0; w < nw; ++w) {
+        if (w > 0 || !lookahead) {
+          r = moe_page_in(L, P, w);
+          if (r) return r;
+        }
+        r = moe_forward(L, P, w, x, out);
+        if (r) return r;
+      }
+      if (launch_residual((const uint16_t*)x, out, (uint16_t*)x, (int64_t)T * L->H, cs) != hipSuccess)
+        return fail(MOE_ERR_HIP, "residual launch failed");
+      if (!lookahead && l + 1 < n) {
+        if (hipEventRecord(resid_done, cs) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord");
+        r = route_impl(layers[l + 1], logits + (l + 1) * lstride, T, plans[l + 1], resid_done);
+        if (r) return r;
+      }
+    }
+    return MOE_OK;
+  };
+  st = run();
+  (void)hipEventDestroy(resid_done);
+  return st;
 }
 
 moe_status moe_layer_stats(const moe_layer* L, moe_stats* out) {
@@ -580,10 +682,14 @@ moe_status moe_timing_read(moe_layer* L, moe_timing* out) {
 
 namespace {
 
+// Expert FFN over wave-order positions [o_lo, o_lo + n_exp). GEMV path: the
+// down kernel writes (or, with accumulate, adds to) out. GEMM path: the two
+// grouped GEMMs fill y for those experts' pairs; with combine, the combine
+// kernel then adds the whole wave's pairs into out.
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows) {
+                   int max_rows, bool combine) {
   FfnArgs a{};
   a.fmt = L->fmt;
   a.E = L->E;
@@ -633,9 +739,11 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     if ((st = timer_begin(L, L->compute, &t2))) return st;
     HIP_TRY(launch_gemm_down(a, L->compute));
     if ((st = timer_end(L, L->compute, &t2, MOE_T_GEMM_DOWN, dn_b, flop_dn))) return st;
-    if ((st = timer_begin(L, L->compute, &t3))) return st;
-    HIP_TRY(launch_combine(a, pair_pos, wave_of, wave, L->compute));
-    if ((st = timer_end(L, L->compute, &t3, MOE_T_COMBINE, 0.0, 0.0))) return st;
+    if (combine) {
+      if ((st = timer_begin(L, L->compute, &t3))) return st;
+      HIP_TRY(launch_combine(a, pair_pos, wave_of, wave, L->compute));
+      if ((st = timer_end(L, L->compute, &t3, MOE_T_COMBINE, 0.0, 0.0))) return st;
+    }
   }
   return MOE_OK;
 }
@@ -703,7 +811,7 @@ moe_status self_check(moe_layer* L) {
         float* o = (float*)(b + o_out) + ((size_t)perm * n + i) * H;
         // the one-pair plan addresses token 0 as pair 0 (k may exceed 1: pair 0 / k == 0)
         result = run_ffn(L, dev, (float*)(b + o_h), nullptr, nullptr, nullptr, 0, 1, 1, 1, b + o_x,
-                         o, 0, nullptr, nullptr, 0, 1);
+                         o, 0, nullptr, nullptr, 0, 1, false);
         if (!result && hipStreamSynchronize(L->compute) != hipSuccess)
           result = fail(MOE_ERR_HIP, "self-check forward failed");
       }

@@ -12,10 +12,11 @@
 //          (16-byte loads, all issued before any arithmetic), dots them with
 //          the tokens routed to that expert, reduces across the wavefront and
 //          writes h = SiLU(g) * u (fp32) for each (token, expert) pair.
-//   down : one wavefront per RW output rows; it walks the wave's experts,
-//          streaming the RW rows of each W_d (next expert's rows prefetched
-//          while the current ones are used), dots them with h and adds
-//          w_tj * y into the accumulator of token t held by lane t.
+//   down : one workgroup of 8 wavefronts per RW output rows; the wave's
+//          experts are split over the wavefronts, each streaming the RW rows
+//          of its experts' W_d, dotting them with h and adding w_tj * y into
+//          the accumulator of token t held by lane t; the partial sums are
+//          combined in LDS in a fixed order.
 // Every weight byte of the wave is read from HBM exactly once; the summation
 // order is fixed, so results are bitwise reproducible.
 #include "internal.h"
@@ -271,22 +272,25 @@ __device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
   return acc;
 }
 
+// Down projection: a workgroup of 8 wavefronts owns RW output rows;
+// wavefront w takes experts w, w+8, ... of the wave (the next one's rows
+// prefetched while the current ones are used), keeps the per-token sums in
+// lane t, and the eight partial sums are added in LDS in wavefront order
+// (fixed, so the result is bitwise reproducible).
 template <int F, int NJ, int RW>
-__global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
+__global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
   constexpr int CB2 = Fmt<F>::CB2, CV2 = Fmt<F>::CV2, NW = CB2 / 4;
+  __shared__ float part[8][kWave][RW];
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int H = a.H, I = a.I;
-  const int r0 = (blockIdx.x * 4 + wid) * RW;
-  if (r0 >= H) return;
+  const int r0 = blockIdx.x * RW;
   const RecLayout L = rec_layout(F, H, I);
   const int nch = I / CV2;
   const size_t row_bytes = (size_t)I * fmt_elem_bits(F) / 8;
-
   float acc[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) acc[r] = 0.f;
-
   uint32_t cur[RW][NJ][NW], nxt[RW][NJ][NW];
   auto load_expert = [&](int e, uint32_t (&dst)[RW][NJ][NW]) {
     const uint8_t* wd = a.slots + (size_t)a.order_slot[a.o_lo + e] * a.stride + L.wd;
@@ -304,10 +308,9 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
       }
     }
   };
-
-  if (a.n_exp > 0) load_expert(0, cur);
-  for (int e = 0; e < a.n_exp; ++e) {
-    if (e + 1 < a.n_exp) load_expert(e + 1, nxt);
+  if (wid < a.n_exp) load_expert(wid, cur);
+  for (int e = wid; e < a.n_exp; e += 8) {
+    if (e + 8 < a.n_exp) load_expert(e + 8, nxt);
     const int o = a.o_lo + e;
     const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
     float sc[RW][NJ], zc[RW][NJ];
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
         if (lane == t) acc[r] = fmaf(wq, y, acc[r]);
       }
     }
-    if (e + 1 < a.n_exp) {
+    if (e + 8 < a.n_exp) {
 #pragma unroll
       for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -379,17 +382,23 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FfnArgs a) {
           for (int n = 0; n < NW; ++n) cur[r][j][n] = nxt[r][j][n];
     }
   }
-  if (lane < a.T) {
-    float* o = a.out + (size_t)lane * H;
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      if (r0 + r < H) o[r0 + r] = (a.accumulate ? o[r0 + r] : 0.f) + acc[r];
-    }
+  for (int r = 0; r < RW; ++r) part[wid][lane][r] = acc[r];
+  __syncthreads();
+  const int T = a.T;
+  for (int idx = threadIdx.x; idx < T * RW; idx += blockDim.x) {
+    const int t = idx / RW, r = idx % RW;
+    if (r0 + r >= H) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) v += part[w][t][r];
+    float* o = a.out + (size_t)t * H + r0 + r;
+    *o = (a.accumulate ? *o : 0.f) + v;
   }
 }
 
-constexpr int kRPW = 2;  // h rows per wavefront (up)
-constexpr int kRW = 2;   // output rows per wavefront (down)
+constexpr int kRPW = 1;  // h rows per wavefront (up)
+constexpr int kRW = 4;   // output rows per workgroup (down)
 
 template <int F, typename XT>
 hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
@@ -410,7 +419,7 @@ hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
 template <int F>
 hipError_t down_dispatch(const FfnArgs& a, hipStream_t s) {
   const int nj = (a.I / Fmt<F>::CV2 + kWave - 1) / kWave;
-  const dim3 grid((a.H + 4 * kRW - 1) / (4 * kRW)), block(256);
+  const dim3 grid((a.H + kRW - 1) / kRW), block(512);
   switch (nj) {
     case 1: ffn_down_kernel<F, 1, kRW><<<grid, block, 0, s>>>(a); break;
     case 2: ffn_down_kernel<F, 2, kRW><<<grid, block, 0, s>>>(a); break;

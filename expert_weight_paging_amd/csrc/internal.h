@@ -105,6 +105,11 @@ hipError_t launch_plan(const int32_t* ids, int T, int k, int E, int K, void* sta
 
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s);
 
+// Router + slot plan + grouping in one launch, for decode-sized steps.
+bool route_small_ok(int T, int k);
+hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
+                                   PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s);
+
 struct FfnArgs {
   int fmt, E, k, H, I, K;
   size_t stride;

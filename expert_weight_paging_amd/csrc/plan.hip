@@ -19,76 +19,102 @@ __device__ inline uint32_t float_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// (key, id) packed so that a larger packed value means a larger logit, or an
+// equal logit and a smaller id: all packed values of a token are distinct.
+__device__ inline unsigned long long pack_logit(float v, int e) {
+  return ((unsigned long long)float_key(v) << 32) | (uint32_t)(~(uint32_t)e);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
+// Orders LDS accesses of one wavefront (its lanes exchange data through LDS).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------------------ router
 // One wavefront per token ([PE] "What does Paged Experts actually do?": each
-// token goes to top_k of E experts). k rounds of a wavefront arg-max over
-// packed (key << 32 | ~id): the largest logit wins, equal logits go to the
-// smaller id, so the result is unique and listed by descending logit. The
-// weights are the softmax of the selected logits, which equals the softmax
-// over all E renormalised over the selected k.
+// token goes to top_k of E experts). Every logit's rank is the number of
+// packed (logit, id) values above it, counted over the token's E values in
+// LDS; ranks 0..k-1 are the selection, listed by descending logit with equal
+// logits in ascending id. The weights are the softmax of the selected logits,
+// which equals the softmax over all E renormalised over the selected k.
+// pk: wavefront-private LDS of E (rounded up to even) entries, 16-byte
+// aligned; zs: of k entries. Lane l owns experts l, l+64, ... (NJ of them).
+template <int NJ>
+__device__ inline void route_token(const float* __restrict__ z, int E, int k, int lane,
+                                   unsigned long long* pk, float* zs, int32_t* ids_out,
+                                   float* w_out) {
+  unsigned long long mine[NJ];
+  float zv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    zv[j] = 0.f;
+    mine[j] = ~0ull;
+    if (e < E) {
+      zv[j] = z[e];
+      mine[j] = pack_logit(zv[j], e);
+      pk[e] = mine[j];
+    }
+  }
+  // a zero entry is below every packed logit, so it pads E to even harmlessly
+  if ((E & 1) && lane == 0) pk[E] = 0ull;
+  wave_lds_sync();
+  int rank[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rank[j] = 0;
+  const ulonglong2* pk2 = (const ulonglong2*)pk;
+  const int n2 = (E + 1) >> 1;
+#pragma unroll 8
+  for (int u = 0; u < n2; ++u) {
+    const ulonglong2 v = pk2[u];  // same address in every lane: a broadcast read
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) rank[j] += (v.x > mine[j] ? 1 : 0) + (v.y > mine[j] ? 1 : 0);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E && rank[j] < k) {
+      ids_out[rank[j]] = e;
+      zs[rank[j]] = zv[j];
+    }
+  }
+  wave_lds_sync();
+  const float zr = lane < k ? zs[lane] : 0.f;
+  const float zmax = zs[0];
+  const float ex = lane < k ? __expf(zr - zmax) : 0.f;
+  const float sum = wave_sum(ex);
+  if (lane < k) w_out[lane] = ex / sum;
+  wave_lds_sync();
+}
+
+// Large steps: 4 wavefronts per workgroup, one token each.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int T, int E,
                                                      int k, int32_t* __restrict__ ids,
                                                      float* __restrict__ weights) {
+  __shared__ __attribute__((aligned(16))) unsigned long long s_pk[4][MOE_MAX_EXPERTS];
+  __shared__ float s_z[4][MOE_MAX_TOP_K];
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  if (t >= T) return;  // uniform per wavefront
-  const float* z = logits + (size_t)t * E;
-  uint32_t key[NJ];
-  uint32_t valid = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + kWave * j;
-    key[j] = 0;
-    if (e < E) {
-      key[j] = float_key(z[e]);
-      valid |= 1u << j;
-    }
-  }
-  int my_id = 0;
-  float my_z = 0.f;
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (valid & (1u << j)) {
-        const unsigned long long p =
-            ((unsigned long long)key[j] << 32) | (uint32_t)(~(uint32_t)(lane + kWave * j));
-        best = p > best ? p : best;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const unsigned long long o = __shfl_xor(best, off, kWave);
-      best = o > best ? o : best;
-    }
-    const int e = (int)(~(uint32_t)best);
-    if ((e & (kWave - 1)) == lane) valid &= ~(1u << (e / kWave));
-    if (lane == r) {
-      my_id = e;
-      my_z = z[e];
-    }
-  }
-  const float zmax = __shfl(my_z, 0, kWave);
-  const float ex = lane < k ? __expf(my_z - zmax) : 0.f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    weights[(size_t)t * k + lane] = ex / sum;
-  }
+  const int wid = threadIdx.x / kWave;
+  const int t = blockIdx.x * 4 + wid;
+  if (t >= T) return;  // uniform per wavefront; no workgroup barrier below
+  route_token<NJ>(logits + (size_t)t * E, E, k, lane, s_pk[wid], s_z[wid], ids + (size_t)t * k,
+                  weights + (size_t)t * k);
 }
 
 // ------------------------------------------------------------------ block scan
-constexpr int kPlanThreads = 1024;
-
-// Exclusive prefix sum over the block (1024 threads); *total gets the sum.
+// Exclusive prefix sum over a block of NT threads; *total gets the sum.
+template <int NT>
 __device__ inline int block_exscan(int v, int* s_warp, int* total) {
+  constexpr int NWV = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   int inc = v;
@@ -100,25 +126,25 @@ __device__ inline int block_exscan(int v, int* s_warp, int* total) {
   if (lane == kWave - 1) s_warp[wid] = inc;
   __syncthreads();
   if (wid == 0) {
-    int w = lane < kPlanThreads / kWave ? s_warp[lane] : 0;
+    const int w = lane < NWV ? s_warp[lane] : 0;
     int winc = w;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
+    for (int off = 1; off < NWV; off <<= 1) {
       const int o = __shfl_up(winc, off, kWave);
       if (lane >= off) winc += o;
     }
-    if (lane < kPlanThreads / kWave) s_warp[lane] = winc - w;
-    if (lane == kPlanThreads / kWave - 1) s_warp[kPlanThreads / kWave] = winc;
+    if (lane < NWV) s_warp[lane] = winc - w;
+    if (lane == NWV - 1) s_warp[NWV] = winc;
   }
   __syncthreads();
   const int res = s_warp[wid] + inc - v;
-  *total = s_warp[kPlanThreads / kWave];
+  *total = s_warp[NWV];
   __syncthreads();
   return res;
 }
 
 // ------------------------------------------------------------------ slot plan
-// One workgroup of 1024 threads; thread e owns expert e, thread s owns slot s.
+// One workgroup of NT >= E threads; thread e owns expert e, thread s owns slot s.
 // [PE] "TL;DR" / "What does Paged Experts actually do?": only routed experts
 // that are not resident are copied in, the least recently used slot goes out.
 // [PE] "What happens with more than one request?": a step that routes more
@@ -127,20 +153,46 @@ __device__ inline int block_exscan(int v, int* s_warp, int* total) {
 // experts, each ascending; waves are chunks of K; the clock ticks per wave;
 // victims are slots not used by the wave, ordered by (stamp, slot); the i-th
 // missing expert goes to the i-th victim.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ ids, int P,
-                                                            int T, int E, int K, uint8_t* state,
-                                                            StateLayout sl, PlanDev dev,
-                                                            PlanHdr* hdr, int32_t seq) {
-  __shared__ int s_cnt[MOE_MAX_EXPERTS];
-  __shared__ int s_pos[MOE_MAX_EXPERTS];
-  __shared__ int s_order_e[MOE_MAX_EXPERTS];
-  __shared__ int s_order_s[MOE_MAX_EXPERTS];
-  __shared__ int s_slot_expert[MOE_MAX_EXPERTS];
-  __shared__ int s_expert_slot[MOE_MAX_EXPERTS];
-  __shared__ long long s_stamp[MOE_MAX_EXPERTS];
-  __shared__ int s_prot[MOE_MAX_EXPERTS];
-  __shared__ int s_warp[kPlanThreads / kWave + 1];
+struct PlanSmem {
+  int cnt[MOE_MAX_EXPERTS];
+  int pos[MOE_MAX_EXPERTS];
+  int order_e[MOE_MAX_EXPERTS];
+  int order_s[MOE_MAX_EXPERTS];
+  int slot_expert[MOE_MAX_EXPERTS];
+  int expert_slot[MOE_MAX_EXPERTS];
+  long long stamp[MOE_MAX_EXPERTS];
+  __attribute__((aligned(16))) unsigned long long vkey[MOE_MAX_EXPERTS];
+  int warp[MOE_MAX_EXPERTS / kWave + 1];
+};
 
+// Victim order key of a slot: empty slots (stamp -1) first, then by stamp,
+// then by slot index; slots of the current wave never become victims.
+__device__ inline unsigned long long victim_key(long long stamp, int slot, bool prot) {
+  return prot ? ~0ull : (((unsigned long long)(stamp + 1)) << 11) | (unsigned)slot;
+}
+
+// This thread's part of the table state, loaded from HBM (issued early so
+// that its latency overlaps other work).
+struct StateRegs {
+  int expert_slot, slot_expert;
+  long long stamp, clock;
+};
+
+__device__ inline StateRegs load_state(const uint8_t* state, const StateLayout& sl, int E, int K) {
+  const int tid = threadIdx.x;
+  StateRegs r;
+  r.expert_slot = tid < E ? ((const int32_t*)(state + sl.expert_slot))[tid] : -1;
+  r.slot_expert = tid < K ? ((const int32_t*)(state + sl.slot_expert))[tid] : -1;
+  r.stamp = tid < K ? ((const long long*)(state + sl.stamp))[tid] : 0;
+  r.clock = *(const long long*)(state + sl.clock);
+  return r;
+}
+
+// ids: the step's routed ids (LDS or global), P = T * k of them.
+template <int NT>
+__device__ void plan_body(const int32_t* ids, int P, int T, int E, int K, uint8_t* state,
+                          const StateLayout& sl, const StateRegs& pre, const PlanDev& dev,
+                          PlanSmem& sm, int* D_out, int* nH_out, int* nw_out) {
   int32_t* g_slot_expert = (int32_t*)(state + sl.slot_expert);
   int32_t* g_expert_slot = (int32_t*)(state + sl.expert_slot);
   long long* g_stamp = (long long*)(state + sl.stamp);
@@ -148,29 +200,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
   const int tid = threadIdx.x;
   if (tid < E) {
-    s_cnt[tid] = 0;
-    s_expert_slot[tid] = g_expert_slot[tid];
+    sm.cnt[tid] = 0;
+    sm.expert_slot[tid] = pre.expert_slot;
   }
   if (tid < K) {
-    s_slot_expert[tid] = g_slot_expert[tid];
-    s_stamp[tid] = g_stamp[tid];
+    sm.slot_expert[tid] = pre.slot_expert;
+    sm.stamp[tid] = pre.stamp;
   }
-  long long clock = *g_clock;
+  long long clock = pre.clock;
   __syncthreads();
-  for (int p = tid; p < P; p += kPlanThreads) atomicAdd(&s_cnt[ids[p]], 1);
+  for (int p = tid; p < P; p += NT) atomicAdd(&sm.cnt[ids[p]], 1);
   __syncthreads();
 
-  const bool ref = tid < E && s_cnt[tid] > 0;
-  const bool hit = ref && s_expert_slot[tid] >= 0;
+  const bool ref = tid < E && sm.cnt[tid] > 0;
+  const bool hit = ref && sm.expert_slot[tid] >= 0;
   const bool miss = ref && !hit;
   int nH, nM;
-  const int hit_rank = block_exscan(hit ? 1 : 0, s_warp, &nH);
-  const int miss_rank = block_exscan(miss ? 1 : 0, s_warp, &nM);
+  const int hit_rank = block_exscan<NT>(hit ? 1 : 0, sm.warp, &nH);
+  const int miss_rank = block_exscan<NT>(miss ? 1 : 0, sm.warp, &nM);
   const int D = nH + nM;
   if (tid < E) {
     const int pos = hit ? hit_rank : (miss ? nH + miss_rank : -1);
-    s_pos[tid] = pos;
-    if (pos >= 0) s_order_e[pos] = tid;
+    sm.pos[tid] = pos;
+    if (pos >= 0) sm.order_e[pos] = tid;
   }
   const int n_waves = (D + K - 1) / K;
   __syncthreads();
@@ -181,81 +233,154 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int hi = min(lo + K, D);
     const int m_lo = max(lo, nH);
     const int nm = hi - m_lo;
-    int prot = 1;
-    long long my_stamp = 0;
+    unsigned long long my_key = ~0ull;
     if (tid < K) {
-      const int e = s_slot_expert[tid];
-      prot = (e >= 0 && s_pos[e] >= lo && s_pos[e] < hi) ? 1 : 0;
-      s_prot[tid] = prot;
-      my_stamp = s_stamp[tid];
+      const int e = sm.slot_expert[tid];
+      const bool prot = e >= 0 && sm.pos[e] >= lo && sm.pos[e] < hi;
+      my_key = victim_key(sm.stamp[tid], tid, prot);
+      sm.vkey[tid] = my_key;
     }
     __syncthreads();
-    if (tid < K && !prot && nm > 0) {
+    if (tid < K && my_key != ~0ull && nm > 0) {
       int rank = 0;
-      for (int s = 0; s < K; ++s) {
-        if (s_prot[s]) continue;
-        const long long st = s_stamp[s];
-        rank += (st < my_stamp || (st == my_stamp && s < tid)) ? 1 : 0;
-      }
+      for (int s = 0; s < K; ++s) rank += sm.vkey[s] < my_key ? 1 : 0;
       if (rank < nm) {
-        const int e_new = s_order_e[m_lo + rank];
-        const int old = s_slot_expert[tid];
-        if (old >= 0) s_expert_slot[old] = -1;
-        s_slot_expert[tid] = e_new;
-        s_expert_slot[e_new] = tid;
-        s_order_s[m_lo + rank] = tid;
+        const int e_new = sm.order_e[m_lo + rank];
+        const int old = sm.slot_expert[tid];
+        if (old >= 0) sm.expert_slot[old] = -1;
+        sm.slot_expert[tid] = e_new;
+        sm.expert_slot[e_new] = tid;
+        sm.order_s[m_lo + rank] = tid;
       }
     }
     __syncthreads();
-    if (tid >= lo && tid < min(hi, nH)) s_order_s[tid] = s_expert_slot[s_order_e[tid]];
+    if (tid >= lo && tid < min(hi, nH)) sm.order_s[tid] = sm.expert_slot[sm.order_e[tid]];
     __syncthreads();
-    if (tid >= lo && tid < hi) s_stamp[s_order_s[tid]] = clock;
+    if (tid >= lo && tid < hi) sm.stamp[sm.order_s[tid]] = clock;
     __syncthreads();
   }
 
   // table state back to HBM
-  if (tid < E) g_expert_slot[tid] = s_expert_slot[tid];
+  if (tid < E) g_expert_slot[tid] = sm.expert_slot[tid];
   if (tid < K) {
-    g_slot_expert[tid] = s_slot_expert[tid];
-    g_stamp[tid] = s_stamp[tid];
+    g_slot_expert[tid] = sm.slot_expert[tid];
+    g_stamp[tid] = sm.stamp[tid];
   }
   if (tid == 0) *g_clock = clock;
 
   // per-pair slot and wave
-  for (int p = tid; p < P; p += kPlanThreads) {
-    const int pos = s_pos[ids[p]];
-    dev.slot_ids[p] = s_order_s[pos];
+  for (int p = tid; p < P; p += NT) {
+    const int pos = sm.pos[ids[p]];
+    dev.slot_ids[p] = sm.order_s[pos];
     dev.wave_of[p] = pos / K;
   }
   // CSR offsets of the pairs of each expert, in wave order
   int total;
-  const int c = tid < D ? s_cnt[s_order_e[tid]] : 0;
-  const int off = block_exscan(c, s_warp, &total);
+  const int c = tid < D ? sm.cnt[sm.order_e[tid]] : 0;
+  const int off = block_exscan<NT>(c, sm.warp, &total);
   if (tid < E) dev.pair_off[tid] = tid < D ? off : P;
   if (tid == 0) dev.pair_off[E] = P;
-
-  // wave order, device and host-visible copies
-  int32_t* h_order_e = (int32_t*)(hdr + 1);
-  int32_t* h_order_s = h_order_e + E;
   if (tid < D) {
-    dev.order_expert[tid] = s_order_e[tid];
-    dev.order_slot[tid] = s_order_s[tid];
-    h_order_e[tid] = s_order_e[tid];
-    h_order_s[tid] = s_order_s[tid];
+    dev.order_expert[tid] = sm.order_e[tid];
+    dev.order_slot[tid] = sm.order_s[tid];
   }
   if (tid == 0) {
     dev.counts[0] = D;
     dev.counts[1] = nH;
     dev.counts[2] = n_waves;
     dev.counts[3] = T;
+  }
+  if (tid < D) sm.cnt[tid] = off;  // from here on: pair offset of order position tid
+  __syncthreads();
+  *D_out = D;
+  *nH_out = nH;
+  *nw_out = n_waves;
+}
+
+// Publish the plan to pinned host memory: wavefront 0 writes the wave order
+// and the header, makes its writes visible at system scope, then stores seq.
+__device__ void publish(const PlanSmem& sm, int E, int T, int D, int nH, int n_waves, PlanHdr* hdr,
+                        int32_t seq) {
+  if (threadIdx.x >= kWave) return;
+  int32_t* h_order_e = (int32_t*)(hdr + 1);
+  int32_t* h_order_s = h_order_e + E;
+  for (int i = threadIdx.x; i < D; i += kWave) {
+    h_order_e[i] = sm.order_e[i];
+    h_order_s[i] = sm.order_s[i];
+  }
+  if (threadIdx.x == 0) {
     hdr->num_tokens = T;
     hdr->num_distinct = D;
     hdr->num_hits = nH;
     hdr->num_waves = n_waves;
   }
   __threadfence_system();
+  if (threadIdx.x == 0) __hip_atomic_store(&hdr->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ ids, int P, int T,
+                                                  int E, int K, uint8_t* state, StateLayout sl,
+                                                  PlanDev dev, PlanHdr* hdr, int32_t seq) {
+  __shared__ PlanSmem sm;
+  const StateRegs pre = load_state(state, sl, E, K);
+  int D, nH, nw;
+  plan_body<NT>(ids, P, T, E, K, state, sl, pre, dev, sm, &D, &nH, &nw);
+  publish(sm, E, T, D, nH, nw, hdr, seq);
+}
+
+// Decode-sized steps (T <= 64, T * k <= kSmallPairs): router, slot plan and
+// grouping in one workgroup, one launch.
+constexpr int kSmallPairs = 2048;
+
+template <int NT, int NJ>
+__global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __restrict__ logits, int T,
+                                                              int E, int k, int K, uint8_t* state,
+                                                              StateLayout sl, PlanDev dev,
+                                                              PlanHdr* hdr, int32_t seq) {
+  constexpr int NWV = NT / kWave;
+  __shared__ PlanSmem sm;
+  __shared__ int32_t s_ids[kSmallPairs];
+  __shared__ float s_z[NWV][MOE_MAX_TOP_K];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int P = T * k;
+  const StateRegs pre = load_state(state, sl, E, K);
+  // the router's per-token LDS borrows the victim-key array (unused until the plan)
+  unsigned long long* pk = sm.vkey + 0;
+  const int per_wave = MOE_MAX_EXPERTS / NWV;
+  if (E < per_wave) {
+    for (int t = wid; t < T; t += NWV)
+      route_token<NJ>(logits + (size_t)t * E, E, k, lane, pk + wid * per_wave, s_z[wid],
+                      s_ids + t * k, dev.weights + (size_t)t * k);
+  } else if (wid == 0) {
+    for (int t = 0; t < T; ++t)
+      route_token<NJ>(logits + (size_t)t * E, E, k, lane, pk, s_z[0], s_ids + t * k,
+                      dev.weights + (size_t)t * k);
+  }
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(&hdr->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  for (int p = threadIdx.x; p < P; p += NT) dev.ids[p] = s_ids[p];
+  int D, nH, nw;
+  plan_body<NT>(s_ids, P, T, E, K, state, sl, pre, dev, sm, &D, &nH, &nw);
+  // grouping: wavefront w collects the pairs of order positions w, w+NWV, ...
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int i = wid; i < D; i += NWV) {
+    const int e = sm.order_e[i];
+    const int base = sm.cnt[i];
+    int running = 0;
+    for (int c = 0; c < P; c += kWave) {
+      const int p = c + lane;
+      const bool m = p < P && s_ids[p] == e;
+      const unsigned long long mask = __ballot(m);
+      if (m) {
+        const int q = base + running + __popcll(mask & below);
+        dev.pair_list[q] = p;
+        dev.pair_pos[p] = q;
+      }
+      running += __popcll(mask);
+    }
+  }
+  publish(sm, E, T, D, nH, nw, hdr, seq);
 }
 
 // ------------------------------------------------------------------ grouping
@@ -317,20 +442,39 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x_in, con
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
                          hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int nj = (E + kWave - 1) / kWave;
-  const dim3 grid((T + 3) / 4), block(256);
-  if (nj <= 1) router_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (nj <= 2) router_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (nj <= 4) router_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (nj <= 8) router_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
-  else router_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
+  const dim3 g((T + 3) / 4), b(256);
+  if (E <= 64) router_kernel<1><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
+  else if (E <= 128) router_kernel<2><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
+  else if (E <= 256) router_kernel<4><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
+  else if (E <= 512) router_kernel<8><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
+  else router_kernel<16><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
   return hipGetLastError();
 }
 
 hipError_t launch_plan(const int32_t* ids, int T, int k, int E, int K, void* state, PlanDev dev,
                        PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s) {
-  plan_kernel<<<1, kPlanThreads, 0, s>>>(ids, T * k, T, E, K, (uint8_t*)state, state_layout(E, K),
-                                         dev, host_hdr_dev, seq);
+  const StateLayout sl = state_layout(E, K);
+  if (E <= 256)
+    plan_kernel<256><<<1, 256, 0, s>>>(ids, T * k, T, E, K, (uint8_t*)state, sl, dev, host_hdr_dev, seq);
+  else
+    plan_kernel<1024><<<1, 1024, 0, s>>>(ids, T * k, T, E, K, (uint8_t*)state, sl, dev, host_hdr_dev, seq);
+  return hipGetLastError();
+}
+
+bool route_small_ok(int T, int k) { return T <= MOE_MAX_GEMV_TOKENS && T * k <= kSmallPairs; }
+
+hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
+                                   PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s) {
+  const StateLayout sl = state_layout(E, K);
+  uint8_t* st = (uint8_t*)state;
+#define MOE_SMALL(NT, NJ) \
+  route_plan_small_kernel<NT, NJ><<<1, NT, 0, s>>>(logits, T, E, k, K, st, sl, dev, host_hdr_dev, seq)
+  if (E <= 64) MOE_SMALL(256, 1);
+  else if (E <= 128) MOE_SMALL(256, 2);
+  else if (E <= 256) MOE_SMALL(256, 4);
+  else if (E <= 512) MOE_SMALL(1024, 8);
+  else MOE_SMALL(1024, 16);
+#undef MOE_SMALL
   return hipGetLastError();
 }
 

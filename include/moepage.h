@@ -205,6 +205,28 @@ moe_status moe_forward(moe_layer* layer, const moe_plan* plan, int32_t wave,
 moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out,
                              int64_t n, void* stream);
 
+/* A batch through a stack of paged MoE layers, attention omitted: for each
+ * layer l, out = MoE_l(x) and then x = bf16_rne(x + out), in place.
+ *   layers, plans: n_layers handles (plan l created for layer l with
+ *                  max_tokens >= T); all layers share E, top_k, H, format and
+ *                  the compute stream
+ *   logits:        device, float32 [n_layers][T][E]
+ *   x:             device, bf16 [T][H], updated in place
+ *   out:           device, float32 [T][H], scratch
+ *   lookahead:     0 = strict order (layer l+1 is routed after layer l's
+ *                  residual, on the compute stream's timeline); 1 = layer l+1
+ *                  is routed and its first wave paged in while layer l
+ *                  computes, so its copies overlap layer l's math ([PE] "TL;DR":
+ *                  the expert math stays on the GPU while experts cross PCIe).
+ *                  Lookahead is only valid when the router input of layer l+1
+ *                  does not depend on layer l's output (e.g. logits computed
+ *                  in advance), which is the caller's promise.
+ * Host-synchronous per layer (each moe_route waits for its plan); the GPU
+ * work is asynchronous. */
+moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, int32_t n_layers,
+                             const float* logits, int32_t num_tokens, void* x, float* out,
+                             int32_t lookahead);
+
 typedef struct moe_stats {
   int64_t steps;        /* moe_route calls with T > 0                          */
   int64_t refs;         /* sum of distinct experts per step                    */

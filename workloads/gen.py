@@ -213,6 +213,14 @@ def pool_records(cfg):
     return expert_store(cfg)
 
 
+def fill_layer_store(cfg, layer, out, pool):
+    """Layer `layer` of a stack: out[e] = pool[perm_layer[e]] (pool from pool_records)."""
+    perm = layer_permutation(cfg, layer)
+    for e in range(cfg.E):
+        out[e] = pool[perm[e]]
+    return out
+
+
 # ------------------------------------------------------------ routing
 
 def correlated_sets(rng, steps, E, k, p):
