@@ -20,6 +20,7 @@
 // Every weight byte of the wave is read from HBM exactly once; the summation
 // order is fixed, so results are bitwise reproducible.
 #include "internal.h"
+#include "wave.h"
 
 namespace moepage {
 
@@ -27,11 +28,6 @@ namespace {
 
 constexpr int kWave = 64;
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
 
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -107,16 +103,58 @@ __device__ inline float dot1(const uint4 w, const float* x, float* xsum) {
       acc = fmaf(b.y, x[4 * i + 3], acc);
     }
   } else {
-    float s = 0.f;
+    // int4: handled by dot1_int4 (fp16 pair path)
+  }
+  return acc;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline f16x2 as_h2(uint32_t v) {
+  f16x2 r;
+  __builtin_memcpy(&r, &v, 4);
+  return r;
+}
+
+// Activations of one int4 chunk (32 values) as fp16 pairs in the order the
+// code pairs come out of a word: word i, step n pairs values 8i+n and 8i+n+4.
+// bf16 -> fp16 is exact for normal-range values (8 significant bits fit 11).
+struct XPairs {
+  uint32_t p[16];
+  float sum;  // sum of the 32 activations (for the zero point)
+};
+
+__device__ inline void make_xpairs(const float* x, XPairs& xp) {
+  float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        acc = fmaf((float)((wv[i] >> (4 * n)) & 0xFu), x[8 * i + n], acc);
-        s += x[8 * i + n];
-      }
+    for (int n = 0; n < 4; ++n) {
+      const auto h = __builtin_amdgcn_cvt_pkrtz(x[8 * i + n], x[8 * i + n + 4]);
+      uint32_t u;
+      __builtin_memcpy(&u, &h, 4);
+      xp.p[4 * i + n] = u;
     }
-    *xsum = s;
+#pragma unroll
+  for (int v = 0; v < 32; ++v) s += x[v];
+  xp.sum = s;
+}
+
+// Raw sum of q * x over one 16-byte int4 chunk (32 codes): each code pair
+// becomes the fp16 pair (1024 + q) exactly via the 0x6400 exponent pattern,
+// 1024 is subtracted in fp16 (exact), and v_dot2_f32_f16 accumulates in fp32.
+__device__ inline float dot1_int4(const uint4 w, const XPairs& xp) {
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  const f16x2 k1024 = as_h2(0x64006400u);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const uint32_t q = ((wv[i] >> (4 * n)) & 0x000F000Fu) | 0x64006400u;
+      const f16x2 qf = as_h2(q) - k1024;
+      acc = __builtin_amdgcn_fdot2(qf, as_h2(xp.p[4 * i + n]), acc, false);
+    }
   }
   return acc;
 }
@@ -189,7 +227,8 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
   const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
   const XT* xbase = (const XT*)a.x;
   for (int q = p0; q < p1; ++q) {
-    const int t = a.pair_list[q] / a.k;
+    // with one token every pair is token 0: no dependent pair-list load
+    const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
     float xv[NJ][CV1];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -200,23 +239,32 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
         for (int v = 0; v < CV1; ++v) xv[j][v] = 0.f;
       }
     }
+    XPairs xp[F == MOE_FMT_INT4_ASYM_G128 ? NJ : 1];
+    if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) make_xpairs(xv[j], xp[j]);
+    }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       float g = 0.f, u = 0.f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        float xs = 0.f;
-        const float dg = dot1<F>(wg[r][j], xv[j], &xs);
-        const float du = dot1<F>(wu[r][j], xv[j], &xs);
-        if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
-          g = fmaf(dg, sg[r][j], g);
-          u = fmaf(du, su[r][j], u);
-        } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
-          g = fmaf(sg[r][j], dg - zg[r][j] * xs, g);
-          u = fmaf(su[r][j], du - zu[r][j] * xs, u);
+        if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+          const float dg = dot1_int4(wg[r][j], xp[j]);
+          const float du = dot1_int4(wu[r][j], xp[j]);
+          g = fmaf(sg[r][j], dg - zg[r][j] * xp[j].sum, g);
+          u = fmaf(su[r][j], du - zu[r][j] * xp[j].sum, u);
         } else {
-          g += dg;
-          u += du;
+          float xs = 0.f;
+          const float dg = dot1<F>(wg[r][j], xv[j], &xs);
+          const float du = dot1<F>(wu[r][j], xv[j], &xs);
+          if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+            g = fmaf(dg, sg[r][j], g);
+            u = fmaf(du, su[r][j], u);
+          } else {
+            g += dg;
+            u += du;
+          }
         }
       }
       g = wave_sum(g);
@@ -261,13 +309,8 @@ __device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
     acc = fmaf(b.x, h[2], acc);
     acc = fmaf(b.y, h[3], acc);
   } else {
-    float s = 0.f;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      acc = fmaf((float)((w[0] >> (4 * n)) & 0xFu), h[n], acc);
-      s += h[n];
-    }
-    *hsum = s;
+    for (int n = 0; n < 8; ++n) acc = fmaf((float)((w[0] >> (4 * n)) & 0xFu), h[n], acc);
   }
   return acc;
 }
@@ -341,7 +384,7 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
     const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
     for (int q = p0; q < p1; ++q) {
       const int pair = a.pair_list[q];
-      const int t = pair / a.k;
+      const int t = a.T == 1 ? 0 : pair / a.k;
       const float wq = a.weights[pair];
       float hv[NJ][CV2];
 #pragma unroll
@@ -358,13 +401,23 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
           for (int v = 0; v < CV2; ++v) hv[j][v] = 0.f;
         }
       }
+      float hsum[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        hsum[j] = 0.f;
+        if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+#pragma unroll
+          for (int v = 0; v < CV2; ++v) hsum[j] += hv[j][v];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         float y = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          float hs = 0.f;
-          const float d = dot2<F>(cur[r][j], hv[j], &hs);
+          const float hs = hsum[j];
+          float unused = 0.f;
+          const float d = dot2<F>(cur[r][j], hv[j], &unused);
           if constexpr (F == MOE_FMT_FP8_E4M3_B128) y = fmaf(d, sc[r][j], y);
           else if constexpr (F == MOE_FMT_INT4_ASYM_G128) y = fmaf(sc[r][j], d - zc[r][j] * hs, y);
           else y += d;

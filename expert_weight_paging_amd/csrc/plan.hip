@@ -4,6 +4,7 @@
 // PCIe Math, and the 4-Request Cliff". [LRU] = "Locality of reference helped
 // 94GB Qwen3.8-Flash-Next runs at 68 tok/s on one RTX 5090".
 #include "internal.h"
+#include "wave.h"
 
 namespace moepage {
 
@@ -25,11 +26,6 @@ __device__ inline unsigned long long pack_logit(float v, int e) {
   return ((unsigned long long)float_key(v) << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
 
 // Orders LDS accesses of one wavefront (its lanes exchange data through LDS).
 __device__ inline void wave_lds_sync() {
