@@ -105,6 +105,24 @@ moe_status timer_begin(moe_layer* L, hipStream_t s, TimerRec* t) {
   return MOE_OK;
 }
 
+// Kernel timers: the two events are handed to the launch, which stamps them at
+// the kernel's start and end.
+moe_status timer_events(moe_layer* L, TimerRec* t) {
+  t->a = t->b = nullptr;
+  if (!L->timing) return MOE_OK;
+  moe_status st = get_event(L, &t->a);
+  if (st) return st;
+  return get_event(L, &t->b);
+}
+
+void timer_push(moe_layer* L, TimerRec* t, int cls, double bytes, double flops) {
+  if (!L->timing) return;
+  t->cls = cls;
+  t->bytes = bytes;
+  t->flops = flops;
+  L->pending.push_back(*t);
+}
+
 moe_status timer_end(moe_layer* L, hipStream_t s, TimerRec* t, int cls, double bytes,
                      double flops) {
   if (!L->timing) return MOE_OK;
@@ -352,7 +370,7 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->hb = gemm ? (uint16_t*)(b + o_hb) : nullptr;
   p->hb_lo = gemm ? (uint16_t*)(b + o_hl) : nullptr;
   p->y = gemm ? (float*)(b + o_y) : nullptr;
-  const size_t hbytes = sizeof(PlanHdr) + 2 * sizeof(int32_t) * E;
+  const size_t hbytes = sizeof(PlanHdr) + sizeof(int32_t) * (3 * E + 1);
   if (hipHostMalloc((void**)&p->hdr, hbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipHostMalloc plan header"));
   std::memset(p->hdr, 0, hbytes);
@@ -394,19 +412,22 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
   if (p->consumed_recorded) HIP_TRY(hipStreamWaitEvent(L->route, p->ev_consumed, 0));
   if (after) HIP_TRY(hipStreamWaitEvent(L->route, after, 0));
   TimerRec tr{};
-  moe_status st = timer_begin(L, L->route, &tr);
+  moe_status st = timer_events(L, &tr);
   if (st) return st;
   const int32_t seq = ++p->seq;
   if (route_small_ok(T, L->k)) {
     HIP_TRY(launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, p->hdr_dev, seq,
-                                    L->route));
+                                    L->route, tr.a, tr.b));
   } else {
-    HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, L->route));
+    HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, L->route, tr.a));
     HIP_TRY(launch_plan(p->dev.ids, T, L->k, L->E, L->K, L->state, p->dev, p->hdr_dev, seq, L->route));
-    HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, L->route));
+    HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, L->route, tr.b));
   }
-  st = timer_end(L, L->route, &tr, MOE_T_ROUTE, 0.0, 0.0);
-  if (st) return st;
+  if (T > 0) timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
+  else if (L->timing) {
+    L->pool.push_back(tr.a);
+    L->pool.push_back(tr.b);
+  }
   HIP_TRY(hipEventRecord(L->ev_routed, L->route));
   // The one host synchronisation of a layer-step: wait until the slot-plan
   // kernel has published the plan into pinned host memory.
@@ -532,6 +553,8 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
   // experts wait for the copy ([SRV]-style overlap of transfer and compute).
   const int n_res = std::max(0, std::min(nH, o_lo + n_exp) - o_lo);
   moe_plan* pm = const_cast<moe_plan*>(p);
+  const int32_t* hoff = (const int32_t*)(p->hdr + 1) + 2 * L->E;  // CSR offsets, host copy
+  auto pairs_in = [&](int lo, int n) { return hoff[lo + n] - hoff[lo]; };
   const bool gemm = T > MOE_MAX_GEMV_TOKENS;
   // Splitting costs extra launches; it only pays while this wave's copies are
   // still in flight.
@@ -539,17 +562,18 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
                               hipEventQuery(L->ev_copied) == hipErrorNotReady;
   moe_status st;
   if (n_res > 0 && copies_pending) {
-    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_res, T * L->k, T, x, out, w > 0,
-                 p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false);
+    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_res, pairs_in(o_lo, n_res), T, x, out,
+                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false);
     if (st) return st;
     HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
-    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo + n_res, n_exp - n_res, T * L->k, T, x,
-                 out, w > 0 || !gemm, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm);
+    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo + n_res, n_exp - n_res,
+                 pairs_in(o_lo + n_res, n_exp - n_res), T, x, out, w > 0 || !gemm, p->dev.pair_pos,
+                 p->dev.wave_of, w, T, /*combine=*/gemm);
     if (st) return st;
   } else {
     if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
-    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, T * L->k, T, x, out, w > 0,
-                 p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm);
+    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, pairs_in(o_lo, n_exp), T, x, out,
+                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm);
     if (st) return st;
   }
   HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
@@ -725,24 +749,32 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
   moe_status st;
   if (T <= MOE_MAX_GEMV_TOKENS) {
     TimerRec t1{}, t2{};
-    if ((st = timer_begin(L, L->compute, &t1))) return st;
+    if ((st = timer_events(L, &t1)) || (st = timer_events(L, &t2))) return st;
+    a.ev0 = t1.a;
+    a.ev1 = t1.b;
     HIP_TRY(launch_ffn_up(a, L->compute));
-    if ((st = timer_end(L, L->compute, &t1, MOE_T_FFN_UP, up_b, flop_up))) return st;
-    if ((st = timer_begin(L, L->compute, &t2))) return st;
+    timer_push(L, &t1, MOE_T_FFN_UP, up_b, flop_up);
+    a.ev0 = t2.a;
+    a.ev1 = t2.b;
     HIP_TRY(launch_ffn_down(a, L->compute));
-    if ((st = timer_end(L, L->compute, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn))) return st;
+    timer_push(L, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn);
   } else {
     TimerRec t1{}, t2{}, t3{};
-    if ((st = timer_begin(L, L->compute, &t1))) return st;
+    if ((st = timer_events(L, &t1)) || (st = timer_events(L, &t2))) return st;
+    a.ev0 = t1.a;
+    a.ev1 = t1.b;
     HIP_TRY(launch_gemm_up(a, L->compute));
-    if ((st = timer_end(L, L->compute, &t1, MOE_T_GEMM_UP, up_b, flop_up))) return st;
-    if ((st = timer_begin(L, L->compute, &t2))) return st;
+    timer_push(L, &t1, MOE_T_GEMM_UP, up_b, flop_up);
+    a.ev0 = t2.a;
+    a.ev1 = t2.b;
     HIP_TRY(launch_gemm_down(a, L->compute));
-    if ((st = timer_end(L, L->compute, &t2, MOE_T_GEMM_DOWN, dn_b, flop_dn))) return st;
+    timer_push(L, &t2, MOE_T_GEMM_DOWN, dn_b, flop_dn);
     if (combine) {
-      if ((st = timer_begin(L, L->compute, &t3))) return st;
+      if ((st = timer_events(L, &t3))) return st;
+      a.ev0 = t3.a;
+      a.ev1 = t3.b;
       HIP_TRY(launch_combine(a, pair_pos, wave_of, wave, L->compute));
-      if ((st = timer_end(L, L->compute, &t3, MOE_T_COMBINE, 0.0, 0.0))) return st;
+      timer_push(L, &t3, MOE_T_COMBINE, 0.0, 0.0);
     }
   }
   return MOE_OK;

@@ -237,13 +237,13 @@ bool gemm_shape_supported(int H, int I) {
 
 hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
-  grouped_gemm_kernel<true><<<dim3(a.I / UP_COLS, a.n_exp), 256, 0, s>>>(a);
+  launch_k(grouped_gemm_kernel<true>, dim3(a.I / UP_COLS, a.n_exp), dim3(256), s, a.ev0, a.ev1, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
-  grouped_gemm_kernel<false><<<dim3(a.H / DN_COLS, a.n_exp), 256, 0, s>>>(a);
+  launch_k(grouped_gemm_kernel<false>, dim3(a.H / DN_COLS, a.n_exp), dim3(256), s, a.ev0, a.ev1, a);
   return hipGetLastError();
 }
 
@@ -251,8 +251,8 @@ hipError_t launch_combine(const FfnArgs& a, const int32_t* pair_pos, const int32
                           int wave, hipStream_t s) {
   const int64_t n4 = ((int64_t)a.T * a.H) / 4;
   if (n4 <= 0) return hipSuccess;
-  combine_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(a.y, pair_pos, wave_of, wave, a.T, a.k,
-                                                              a.H, a.out, a.accumulate);
+  launch_k(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, a.ev0, a.ev1, a.y, pair_pos,
+           wave_of, wave, a.T, a.k, a.H, a.out, a.accumulate);
   return hipGetLastError();
 }
 

@@ -450,20 +450,23 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
   }
 }
 
-constexpr int kRPW = 1;  // h rows per wavefront (up)
-constexpr int kRW = 4;   // output rows per workgroup (down)
+// Work per wavefront scaled so that each moves about the same bytes whatever
+// the weight format: h rows per wavefront (up), output rows per workgroup (down).
+template <int F> constexpr int rpw() { return F == MOE_FMT_INT4_ASYM_G128 ? 4 : F == MOE_FMT_FP8_E4M3_B128 ? 2 : 1; }
+template <int F> constexpr int rw() { return F == MOE_FMT_INT4_ASYM_G128 ? 8 : F == MOE_FMT_FP8_E4M3_B128 ? 8 : 4; }
 
 template <int F, typename XT>
 hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
+  constexpr int kRPW = rpw<F>();
   const int nj = (a.H / Fmt<F>::CV1 + kWave - 1) / kWave;
   const dim3 grid((a.I + 4 * kRPW - 1) / (4 * kRPW), a.n_exp), block(256);
   switch (nj) {
-    case 1: ffn_up_kernel<F, 1, kRPW, XT><<<grid, block, 0, s>>>(a); break;
-    case 2: ffn_up_kernel<F, 2, kRPW, XT><<<grid, block, 0, s>>>(a); break;
-    case 3: ffn_up_kernel<F, 3, kRPW, XT><<<grid, block, 0, s>>>(a); break;
-    case 4: ffn_up_kernel<F, 4, kRPW, XT><<<grid, block, 0, s>>>(a); break;
-    case 6: ffn_up_kernel<F, 6, kRPW, XT><<<grid, block, 0, s>>>(a); break;
-    case 8: ffn_up_kernel<F, 8, kRPW, XT><<<grid, block, 0, s>>>(a); break;
+    case 1: launch_k(ffn_up_kernel<F, 1, kRPW, XT>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 2: launch_k(ffn_up_kernel<F, 2, kRPW, XT>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 3: launch_k(ffn_up_kernel<F, 3, kRPW, XT>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 4: launch_k(ffn_up_kernel<F, 4, kRPW, XT>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 6: launch_k(ffn_up_kernel<F, 6, kRPW, XT>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 8: launch_k(ffn_up_kernel<F, 8, kRPW, XT>, grid, block, s, a.ev0, a.ev1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -471,15 +474,16 @@ hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
 
 template <int F>
 hipError_t down_dispatch(const FfnArgs& a, hipStream_t s) {
+  constexpr int kRW = rw<F>();
   const int nj = (a.I / Fmt<F>::CV2 + kWave - 1) / kWave;
   const dim3 grid((a.H + kRW - 1) / kRW), block(512);
   switch (nj) {
-    case 1: ffn_down_kernel<F, 1, kRW><<<grid, block, 0, s>>>(a); break;
-    case 2: ffn_down_kernel<F, 2, kRW><<<grid, block, 0, s>>>(a); break;
-    case 3: ffn_down_kernel<F, 3, kRW><<<grid, block, 0, s>>>(a); break;
-    case 4: ffn_down_kernel<F, 4, kRW><<<grid, block, 0, s>>>(a); break;
-    case 6: ffn_down_kernel<F, 6, kRW><<<grid, block, 0, s>>>(a); break;
-    case 8: ffn_down_kernel<F, 8, kRW><<<grid, block, 0, s>>>(a); break;
+    case 1: launch_k(ffn_down_kernel<F, 1, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 2: launch_k(ffn_down_kernel<F, 2, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 3: launch_k(ffn_down_kernel<F, 3, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 4: launch_k(ffn_down_kernel<F, 4, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 6: launch_k(ffn_down_kernel<F, 6, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 8: launch_k(ffn_down_kernel<F, 8, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,6 +1,7 @@
 // Internal declarations of libmoepage (not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <cstddef>
 #include <cstdint>
@@ -27,7 +28,8 @@ inline StateLayout state_layout(int E, int K) {
 }
 
 // Header of the host-visible plan (pinned, mapped, coherent). The slot-plan
-// kernel writes the header fields and the two order arrays that follow it,
+// kernel writes the header fields and the arrays that follow it (wave order,
+// slot of each, CSR pair offsets over the wave order),
 // then publishes `seq` with a system-scope release store; the host waits for
 // seq to reach the value it expects.
 struct PlanHdr {
@@ -37,7 +39,7 @@ struct PlanHdr {
   int32_t num_hits;
   int32_t num_waves;
   int32_t pad[3];
-  // int32_t order_expert[E]; int32_t order_slot[E];
+  // int32_t order_expert[E]; int32_t order_slot[E]; int32_t pair_off[E + 1];
 };
 
 // Device-side arrays of a plan.
@@ -97,18 +99,32 @@ __host__ __device__ inline RecLayout rec_layout(int fmt, int H, int I) {
 
 // ---------------------------------------------------------------- launchers
 
+// Launch a kernel; when timing events are given they are stamped by the
+// dispatch itself (start and end of the kernel's execution on the stream).
+template <typename K, typename... Args>
+inline void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                     Args... args) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, args...);
+  else
+    kernel<<<grid, block, 0, s>>>(args...);
+}
+
+// ev0 / ev1: optional timing events stamped at the start / end of the kernel.
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
-                         hipStream_t s);
+                         hipStream_t s, hipEvent_t ev0);
 
 hipError_t launch_plan(const int32_t* ids, int T, int k, int E, int K, void* state,
                        PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s);
 
-hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s);
+hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s,
+                        hipEvent_t ev1);
 
 // Router + slot plan + grouping in one launch, for decode-sized steps.
 bool route_small_ok(int T, int k);
 hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
-                                   PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s);
+                                   PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s,
+                                   hipEvent_t ev0, hipEvent_t ev1);
 
 struct FfnArgs {
   int fmt, E, k, H, I, K;
@@ -128,6 +144,7 @@ struct FfnArgs {
   uint16_t* hb_lo;     // GEMM scratch bf16 [T*k][I], low part of h
   float* y;            // GEMM scratch fp32 [T*k][H]
   int max_rows;        // upper bound on pairs of one expert in this wave (GEMM)
+  hipEvent_t ev0, ev1; // optional timing events for the next launch
 };
 
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);

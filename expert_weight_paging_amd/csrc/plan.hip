@@ -295,15 +295,18 @@ __device__ void plan_body(const int32_t* ids, int P, int T, int E, int K, uint8_
 
 // Publish the plan to pinned host memory: wavefront 0 writes the wave order
 // and the header, makes its writes visible at system scope, then stores seq.
-__device__ void publish(const PlanSmem& sm, int E, int T, int D, int nH, int n_waves, PlanHdr* hdr,
-                        int32_t seq) {
+__device__ void publish(const PlanSmem& sm, int E, int T, int P, int D, int nH, int n_waves,
+                        PlanHdr* hdr, int32_t seq) {
   if (threadIdx.x >= kWave) return;
   int32_t* h_order_e = (int32_t*)(hdr + 1);
   int32_t* h_order_s = h_order_e + E;
+  int32_t* h_pair_off = h_order_s + E;
   for (int i = threadIdx.x; i < D; i += kWave) {
     h_order_e[i] = sm.order_e[i];
     h_order_s[i] = sm.order_s[i];
+    h_pair_off[i] = sm.cnt[i];
   }
+  if (threadIdx.x == 0) h_pair_off[D] = P;
   if (threadIdx.x == 0) {
     hdr->num_tokens = T;
     hdr->num_distinct = D;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ id
   const StateRegs pre = load_state(state, sl, E, K);
   int D, nH, nw;
   plan_body<NT>(ids, P, T, E, K, state, sl, pre, dev, sm, &D, &nH, &nw);
-  publish(sm, E, T, D, nH, nw, hdr, seq);
+  publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
 // Decode-sized steps (T <= 64, T * k <= kSmallPairs): router, slot plan and
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
       running += __popcll(mask);
     }
   }
-  publish(sm, E, T, D, nH, nw, hdr, seq);
+  publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
 // ------------------------------------------------------------------ grouping
@@ -436,14 +439,14 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x_in, con
 }  // namespace
 
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t ev0) {
   if (T <= 0) return hipSuccess;
   const dim3 g((T + 3) / 4), b(256);
-  if (E <= 64) router_kernel<1><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (E <= 128) router_kernel<2><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (E <= 256) router_kernel<4><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (E <= 512) router_kernel<8><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
-  else router_kernel<16><<<g, b, 0, s>>>(logits, T, E, k, ids, weights);
+  if (E <= 64) launch_k(router_kernel<1>, g, b, s, ev0, nullptr, logits, T, E, k, ids, weights);
+  else if (E <= 128) launch_k(router_kernel<2>, g, b, s, ev0, nullptr, logits, T, E, k, ids, weights);
+  else if (E <= 256) launch_k(router_kernel<4>, g, b, s, ev0, nullptr, logits, T, E, k, ids, weights);
+  else if (E <= 512) launch_k(router_kernel<8>, g, b, s, ev0, nullptr, logits, T, E, k, ids, weights);
+  else launch_k(router_kernel<16>, g, b, s, ev0, nullptr, logits, T, E, k, ids, weights);
   return hipGetLastError();
 }
 
@@ -460,11 +463,13 @@ hipError_t launch_plan(const int32_t* ids, int T, int k, int E, int K, void* sta
 bool route_small_ok(int T, int k) { return T <= MOE_MAX_GEMV_TOKENS && T * k <= kSmallPairs; }
 
 hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
-                                   PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s) {
+                                   PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s,
+                                   hipEvent_t ev0, hipEvent_t ev1) {
   const StateLayout sl = state_layout(E, K);
   uint8_t* st = (uint8_t*)state;
-#define MOE_SMALL(NT, NJ) \
-  route_plan_small_kernel<NT, NJ><<<1, NT, 0, s>>>(logits, T, E, k, K, st, sl, dev, host_hdr_dev, seq)
+#define MOE_SMALL(NT, NJ)                                                                   \
+  launch_k(route_plan_small_kernel<NT, NJ>, dim3(1), dim3(NT), s, ev0, ev1, logits, T, E, k, K, st, \
+           sl, dev, host_hdr_dev, seq)
   if (E <= 64) MOE_SMALL(256, 1);
   else if (E <= 128) MOE_SMALL(256, 2);
   else if (E <= 256) MOE_SMALL(256, 4);
@@ -474,9 +479,10 @@ hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int
   return hipGetLastError();
 }
 
-hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s) {
+hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s,
+                        hipEvent_t ev1) {
   if (T <= 0) return hipSuccess;
-  group_kernel<<<(E + 3) / 4, 256, 0, s>>>(ids, T * k, dev);
+  launch_k(group_kernel, dim3((E + 3) / 4), dim3(256), s, nullptr, ev1, ids, T * k, dev);
   return hipGetLastError();
 }
 
