@@ -20,22 +20,25 @@
 //   combine: out[t] (+)= sum over j in 0..k-1 of y[pair (t, j)] for the pairs
 //          of this wave, j ascending (fixed order -> bitwise reproducible)
 //
-// Tiling (v_mfma_f32_16x16x32_bf16, 64-wide wavefronts). A workgroup of four
-// wavefronts owns one expert and 128 output columns (up: 64 gate rows and the
-// 64 matching up rows of W13; down: 128 rows of W_d) and covers up to 256 of
-// the expert's rows per pass, so each weight byte leaves HBM once per expert
-// for all but the hottest experts. The k loop runs in steps of 32; each step
-// is one pipeline stage in LDS holding the weight tile (128 x 32) and the
-// activation tile(s) (rows x 32). Stages are filled by direct global-to-LDS
-// loads (no register staging), NSTAGE - 1 steps ahead of the matrix cores,
-// so HBM latency hides behind the MFMAs; a wait on the vector-memory counter
-// plus a barrier hands a stage over. Only the 64-row groups that hold routed
-// rows are loaded (template RG). The 16-byte chunks of a tile row are
-// XOR-swizzled by (row / 2) mod 4, which makes the fragment reads free of
-// LDS bank conflicts; the swizzle is applied by choosing each DMA lane's
-// source chunk, since a DMA instruction writes its 64 lanes contiguously.
-// The four wavefronts form a 2 x 2 grid: wavefront (wm, wn) takes the 16-row
-// sub-tiles with index = wm (mod 2) and output columns wn*64 .. wn*64+63.
+// Tiling (v_mfma_f32_16x16x32_bf16, 64-wide wavefronts). A workgroup of eight
+// wavefronts, one per CU, owns one expert and 256 weight rows (up: 128 gate
+// rows and the 128 matching up rows of W13; down: 256 rows of W_d) and covers
+// up to 256 of the expert's rows per pass, so each weight byte leaves HBM
+// once per expert for all but the hottest experts, and each activation row is
+// copied once per 256 weight rows. The k loop runs in steps
+// of 32. Each step's weight tile (128 x 32) and activation tile(s) (rows x 32)
+// are filled by direct global-to-LDS copies (no register staging) into two
+// LDS rings: the weight ring, fed from HBM, runs 3 to 7 steps ahead of the
+// matrix cores; the activation ring, mostly fed from L2, 2 steps ahead.
+// A wait on the vector-memory counter plus a barrier hands a step over. Only
+// the 64-row groups that hold routed rows are copied (template RG). The
+// 16-byte chunks of a tile row are XOR-swizzled by (row / 2) mod 4, which
+// makes the fragment reads free of LDS bank conflicts; the swizzle is applied
+// by choosing each copy lane's source chunk, since one copy instruction
+// writes its 64 lanes contiguously.
+// The eight wavefronts form a 2 x 4 grid: wavefront (wm, wn) takes the 16-row
+// sub-tiles with index = wm (mod 2) and 64 of the output columns (up: h
+// columns wn*32 .. wn*32+31 from their gate and up rows; down: wn*64 ..).
 // Workgroups are numbered so that each XCD (which schedules every eighth
 // workgroup and has its own L2) works through a contiguous run of experts,
 // keeping an expert's activation rows in one L2.
@@ -50,11 +53,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BM = 256;                    // expert rows per pass
-constexpr int BN = 128;                    // weight rows per workgroup
-constexpr int BK = 32;                     // reduction elements per stage
-constexpr int A_CH = BM * BK * 2 / 16;     // 16-byte chunks of an activation tile (1024)
-constexpr int W_CH = BN * BK * 2 / 16;     // 16-byte chunks of the weight tile (512)
+constexpr int kThreads = 512;              // eight wavefronts per workgroup
+constexpr int BN = 256;                    // weight rows per workgroup
+constexpr int BK = 32;                     // reduction elements per k-step
+constexpr int W_CH = BN * BK * 2 / 16;     // 16-byte chunks of the weight tile (1024)
 constexpr int UP_HCOLS = BN / 2;           // h columns per workgroup (up)
 constexpr int DN_COLS = BN;                // output columns per workgroup (down)
 constexpr int kXcd = 8;                    // XCDs; consecutive workgroups go round-robin over them
@@ -77,14 +79,18 @@ __device__ inline int lds_chunk(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 
 __device__ inline int src_chunk(int p) { return (p & 3) ^ ((p >> 3) & 3); }
 
 // Global-to-LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
-// address lds + 16 * l (lds wave-uniform, in M0). Issued from inline assembly
-// so that the compiler neither waits for it before every LDS read nor counts
-// it: the pipeline below does its own waiting on the vector-memory counter.
+// address lds + 16 * l (lds wave-uniform, passed in M0). Issued from inline
+// assembly so that the compiler neither waits for it before every LDS read nor
+// counts it: the pipeline below does its own waiting on the vector-memory
+// counter. M0 is saved and restored around the copy (the compiler reserves it).
 __device__ inline void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
@@ -100,34 +106,52 @@ __device__ inline void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Two LDS rings per pass with RG 64-row groups (RG = 2 or 4). The weight tile
+// of a k-step comes from HBM and the activation tile(s) mostly from L2, so the
+// weight ring runs deeper (SW stages) than the activation ring (SA stages) to
+// keep enough HBM bytes in flight. One workgroup per CU owns the 160 KB LDS.
 template <bool UP>
 struct Tiles {
-  static constexpr int NA = UP ? 1 : 2;                 // activation tiles: x, or (h_hi, h_lo)
-  static constexpr int NSTAGE = UP ? 3 : 2;             // pipeline depth (LDS: 72 KB / 80 KB)
-  static constexpr int STAGE_CH = NA * A_CH + W_CH;
+  static constexpr int NA = UP ? 1 : 2;  // activation tiles: x, or (h_hi, h_lo)
+  static constexpr int BUDGET_CH = 160 * 1024 / 16;
+};
+template <bool UP, int RG>
+struct Ring {
+  static constexpr int A_CH = Tiles<UP>::NA * RG * 256;  // activation chunks per stage
+  static constexpr int SW3 = (Tiles<UP>::BUDGET_CH - 3 * A_CH) / W_CH;
+  static constexpr int SA = SW3 > 3 ? 3 : 2;
+  static constexpr int SW_FIT = (Tiles<UP>::BUDGET_CH - SA * A_CH) / W_CH;
+  static constexpr int SW = SW_FIT > 8 ? 8 : SW_FIT;
+  static_assert(SW > SA && SA >= 2, "LDS budget too small for the two rings");
 };
 
 // One pass over rows [mb, mb + mcnt) of expert position o, mcnt <= 64 * RG.
+// Copies are issued per k-step as [activation stage it + SA - 1][weight stage
+// it + SW - 1]; since SW > SA, the activation copy of a stage is issued after
+// its weight copy, so "stage it has landed" is "all copies up to the
+// activation copy of stage it have completed" (copies complete in order).
 template <bool UP, int RG>
 __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (&wsrc)[2], int col0,
                           int q0, int mb, int mcnt) {
-  using Tl = Tiles<UP>;
-  constexpr int NA = Tl::NA, NSTAGE = Tl::NSTAGE, STAGE_CH = Tl::STAGE_CH;
-  constexpr int NIS = NA * RG + 2;  // DMA instructions per thread per stage
+  static_assert(RG == 2 || RG == 4, "passes cover 128 or 256 rows");
+  using R = Ring<UP, RG>;
+  constexpr int NA = Tiles<UP>::NA, SA = R::SA, SW = R::SW;
+  constexpr int GI = RG / 2;           // activation copies per tile per thread (512 chunks each)
+  constexpr int nA = NA * GI, nW = 2;  // copy instructions per thread per stage
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform, kept in an SGPR
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid >> 2, wn = wid & 3;
   const int H = a.H, I = a.I;
   const int KD = UP ? H : I;
   const int nit = KD / BK;
 
-  // Activation sources: chunk p = g * 256 + tid of tile u is row p / 4; rows
+  // Activation sources: chunk p = g * 512 + tid of tile u is row p / 4; rows
   // past the expert's end reload the pass's first row (their results are
   // discarded: a row of the product depends only on that row of A).
-  const uint16_t* asrc[NA][RG];
+  const uint16_t* asrc[NA][GI];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int p = g * 256 + tid;
+  for (int g = 0; g < GI; ++g) {
+    const int p = g * kThreads + tid;
     const int r = p >> 2, c = src_chunk(p);
     const int q = q0 + mb + (r < mcnt ? r : 0);
     if (UP) {
@@ -137,16 +161,22 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
       asrc[NA - 1][g] = a.hb_lo + (size_t)q * I + c * 8;
     }
   }
+  // LDS: activation ring [SA][A_CH], then weight ring [SW][W_CH]
   const uint32_t lds0 = lds_addr(smem) + wid * kWave * 16;
-  auto issue = [&](int it) {
-    const uint32_t st = lds0 + (it % NSTAGE) * STAGE_CH * 16;
-    const int ko = it * BK;
+  const uint32_t ldsw = lds0 + SA * R::A_CH * 16;
+  auto issue_a = [&](int s) {
+    if (s < 0 || s >= nit) return;
+    const uint32_t st = lds0 + (s % SA) * R::A_CH * 16;
 #pragma unroll
     for (int u = 0; u < NA; ++u)
 #pragma unroll
-      for (int g = 0; g < RG; ++g) dma16(asrc[u][g] + ko, st + (u * A_CH + g * 256) * 16);
+      for (int g = 0; g < GI; ++g) dma16(asrc[u][g] + s * BK, st + (u * RG * 256 + g * kThreads) * 16);
+  };
+  auto issue_w = [&](int s) {
+    if (s < 0 || s >= nit) return;
+    const uint32_t st = ldsw + (s % SW) * W_CH * 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(wsrc[i] + ko, st + (NA * A_CH + i * 256) * 16);
+    for (int i = 0; i < 2; ++i) dma16(wsrc[i] + s * BK, st + (i * kThreads) * 16);
   };
 
   constexpr int MT = RG * 2;  // 16-row sub-tiles per wavefront
@@ -156,22 +186,38 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nit) issue(s);
+  // prologue: the k-steps before 0 of the same issue schedule
+  for (int j = 1 - SW; j < 0; ++j) {
+    issue_a(j + SA - 1);
+    issue_w(j + SW - 1);
+  }
   for (int it = 0; it < nit; ++it) {
-    // stage `it` has landed once at most the NSTAGE - 2 later stages are in flight
-    if (it + NSTAGE - 2 < nit) stage_barrier<NIS * (NSTAGE - 2)>();
-    else stage_barrier<0>();
-    if (it + NSTAGE - 1 < nit) issue(it + NSTAGE - 1);
-    const uint4* st = smem + (it % NSTAGE) * STAGE_CH;
-    const uint4* wt = st + NA * A_CH;
+    // Copies issued after the activation copy of stage it: the weight copy of
+    // its own k-step (stage it - SA + SW) and, for SA = 3, both copies of
+    // k-step it - 1 (stages it + 1 and it + SW - 2); only those below nit exist.
+    {
+      const bool w0 = it - SA + SW < nit;
+      if (SA == 3) {
+        const bool a1 = it + 1 < nit, w1 = it + SW - 2 < nit;  // w1 implies w0 implies a1
+        if (w1) stage_barrier<2 * nW + nA>();
+        else if (w0) stage_barrier<nW + nA>();
+        else if (a1) stage_barrier<nA>();
+        else stage_barrier<0>();
+      } else {
+        if (w0) stage_barrier<nW>();
+        else stage_barrier<0>();
+      }
+    }
+    issue_a(it + SA - 1);
+    issue_w(it + SW - 1);
+    const uint4* st = smem + (it % SA) * R::A_CH;
+    const uint4* wt = smem + SA * R::A_CH + (it % SW) * W_CH;
     // B fragments: lane holds weight-tile row (lane % 16) of the sub-tile, chunk lane / 16
     bf16x8 bf[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       // up: h columns wn*32 + (n%2)*16 .. (gate rows for n < 2, the matching up
-      // rows 64 further down the tile for n >= 2); down: columns wn*64 + n*16 ..
+      // rows 128 further down the tile for n >= 2); down: columns wn*64 + n*16 ..
       const int trow = UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15))
                           : (wn * 64 + n * 16 + (lane & 15));
       bf[n] = as_bf16x8(wt[lds_chunk(trow, lane >> 4)]);
@@ -185,7 +231,7 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
       bf16x8 af[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        af[m] = as_bf16x8(st[u * A_CH + lds_chunk((2 * m + wm) * 16 + (lane & 15), lane >> 4)]);
+        af[m] = as_bf16x8(st[u * RG * 256 + lds_chunk((2 * m + wm) * 16 + (lane & 15), lane >> 4)]);
 #pragma unroll
       for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(af[m]));
 #pragma unroll
@@ -219,7 +265,7 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
           a.hb[at] = hi;
           a.hb_lo[at] = f32_to_bf16_rne(h - __uint_as_float((uint32_t)hi << 16));
         }
-      } else {
+      } else if (col0 + wn * 64 < H) {  // the last tile may hold only 128 columns
         const float w = a.weights[a.pair_list[q]];
 #pragma unroll
         for (int n = 0; n < 4; ++n)
@@ -230,9 +276,9 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
 }
 
 template <bool UP>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(FfnArgs a, int tiles_per_expert) {
-  using Tl = Tiles<UP>;
-  __shared__ __attribute__((aligned(16))) uint4 smem[Tl::NSTAGE * Tl::STAGE_CH];
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, int tiles_per_expert) {
+  __shared__ __attribute__((aligned(16))) uint4 smem[Tiles<UP>::BUDGET_CH];
+  constexpr int BMP = 256;  // rows per pass
   // XCD-contiguous numbering: hardware block b runs on XCD b % 8; give the
   // blocks of one XCD consecutive virtual ids.
   const int nb = gridDim.x, b = blockIdx.x;
@@ -248,23 +294,20 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(FfnArgs a, int til
   const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
   const uint16_t* W = (const uint16_t*)(rec + (UP ? (size_t)0 : (size_t)2 * I * H * 2));
   const int col0 = tile * (UP ? UP_HCOLS : DN_COLS);
-  // weight DMA sources: chunk p = i * 256 + tid of the weight tile is tile row p / 4
+  // weight copy sources: chunk p = i * 512 + tid of the weight tile is tile row
+  // p / 4 (down: rows past H, in a last half-width tile, reread row H - 1)
   const uint16_t* wsrc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int p = i * 256 + threadIdx.x;
+    const int p = i * kThreads + threadIdx.x;
     const int r = p >> 2, c = src_chunk(p);
-    const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : col0 + r;
+    const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
     wsrc[i] = W + (size_t)wrow * KD + c * 8;
   }
-  for (int mb = 0; mb < M; mb += BM) {
-    const int mcnt = min(BM, M - mb);
-    switch ((mcnt + 63) >> 6) {  // uniform over the workgroup
-      case 1: gemm_pass<UP, 1>(a, smem, wsrc, col0, q0, mb, mcnt); break;
-      case 2: gemm_pass<UP, 2>(a, smem, wsrc, col0, q0, mb, mcnt); break;
-      case 3: gemm_pass<UP, 3>(a, smem, wsrc, col0, q0, mb, mcnt); break;
-      default: gemm_pass<UP, 4>(a, smem, wsrc, col0, q0, mb, mcnt); break;
-    }
+  for (int mb = 0; mb < M; mb += BMP) {
+    const int mcnt = min(BMP, M - mb);
+    if (mcnt <= 128) gemm_pass<UP, 2>(a, smem, wsrc, col0, q0, mb, mcnt);  // uniform branch
+    else gemm_pass<UP, 4>(a, smem, wsrc, col0, q0, mb, mcnt);
   }
 }
 
@@ -298,14 +341,14 @@ bool gemm_shape_supported(int H, int I) {
 hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
   const int tpe = a.I / UP_HCOLS;
-  launch_k(grouped_gemm_kernel<true>, dim3(tpe * a.n_exp), dim3(256), s, a.ev0, a.ev1, a, tpe);
+  launch_k(grouped_gemm_kernel<true>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a, tpe);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
-  const int tpe = a.H / DN_COLS;
-  launch_k(grouped_gemm_kernel<false>, dim3(tpe * a.n_exp), dim3(256), s, a.ev0, a.ev1, a, tpe);
+  const int tpe = (a.H + DN_COLS - 1) / DN_COLS;
+  launch_k(grouped_gemm_kernel<false>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a, tpe);
   return hipGetLastError();
 }
 
