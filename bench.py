@@ -65,8 +65,64 @@ def traffic_from_profiles(kernel_name, workload):
         d = json.load(f)
     if d.get("source_hash") != kernel_source_hash():
         return None
-    k = d.get("workloads", {}).get(workload, {}).get(kernel_name)
+    k = d.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_name)
     return None if not k else k.get("bytes_per_launch")
+
+
+KERNEL_KEYS = (("ffn_up_kernel", "ffn_up_kernel"), ("ffn_down_kernel", "ffn_down_kernel"),
+               ("grouped_gemm_kernel<true>", "grouped_gemm_kernel<true>"),
+               ("grouped_gemm_kernel<false>", "grouped_gemm_kernel<false>"),
+               ("route_plan_small_kernel", "route_plan_small_kernel"), ("combine_kernel", "combine_kernel"))
+
+
+def ingest_pmc(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of each of this library's kernels from two
+    rocprofv3 --pmc runs of the same bench command (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch). Each counter is scaled by the factor that
+    maps its reading for the run's 1 GiB device-to-device copy (the copy in
+    measured_peaks) onto 1 GiB. Writes profiles/pmc_traffic.json, keyed by the
+    hash of the kernel sources, so bench.py drops the figure once a kernel
+    changes."""
+    import csv
+    def load(path, counter):
+        per = {}
+        calib = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                name = r["Kernel_Name"]
+                if "copyBuffer" in name and v > 256 * 1024:  # the 1 GiB copy (>= 256 MiB read)
+                    calib.append(v)
+                    continue
+                for pat, key in KERNEL_KEYS:
+                    if pat in name.replace(" ", ""):
+                        per.setdefault(key, []).append(v)
+        if not calib:
+            raise SystemExit("no 1 GiB copy in %s: run the bench without --no-peaks" % path)
+        calib.sort()
+        return per, (1 << 20) / calib[len(calib) // 2]
+    fetch, ff = load(fetch_csv, "FETCH_SIZE")
+    write, wf = load(write_csv, "WRITE_SIZE")
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    d = {}
+    if os.path.exists(p):
+        with open(p) as f:
+            d = json.load(f)
+    h = kernel_source_hash()
+    if d.get("source_hash") != h:
+        d = {"source_hash": h, "workloads": {}}
+    w = {}
+    for key in sorted(set(fetch) & set(write)):
+        fk = sum(fetch[key]) / len(fetch[key]) * ff
+        wk = sum(write[key]) / len(write[key]) * wf
+        w[key] = {"bytes_per_launch": round((fk + wk) * 1024.0, 1), "fetch_bytes": round(fk * 1024.0, 1),
+                  "write_bytes": round(wk * 1024.0, 1), "launches": len(fetch[key])}
+    d["workloads"][workload] = {"kernels": w, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
+    with open(p, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+    print(json.dumps(d["workloads"][workload], indent=1))
 
 
 def measured_peaks(torch, dev):
@@ -166,11 +222,13 @@ def bench_decode(args, torch, dev):
     run(args.warmup, args.steps)
     torch.cuda.synchronize()
     tm = layer.timing_read()
+    floor_us = ewp.timing_floor(compute)
     layer.timing_enable(False)
     plan.close()
     layer.close()
     d = {k: s1[k] - s0[k] for k in s1}
     res = {"value": args.steps * B / el, "ms_per_step": el / args.steps * 1e3, "timing": tm,
+           "floor_us": floor_us,
            "stats": d, "cfg": cfg, "B": B,
            "workload": "one Qwen3-30B-A3B-shaped MoE layer, %s experts, E=%d top_k=%d hidden=%d "
                        "intermediate=%d, K=%d resident slots, decode at batch %d, correlated routing "
@@ -180,14 +238,17 @@ def bench_decode(args, torch, dev):
     def cpu(budget):
         from oracle.layer import PagedLayer
         ref = PagedLayer(np.array(host.array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K)
+        # a longer decode sequence from the same seeded generator (same recipe),
+        # so that the sample holds about `budget` seconds of oracle work
+        lg_c, x_c = gen.decode_inputs(cfg, B, steps=max(total, 4096))
         n = 0
         t0 = time.perf_counter()
-        while n < total and (time.perf_counter() - t0) < budget:
-            ref.step(logits[n], gen.bf16_bits_to_f32(x[n]).astype(np.float64))
+        while n < len(lg_c) and (time.perf_counter() - t0) < budget:
+            ref.step(lg_c[n], gen.bf16_bits_to_f32(x_c[n]).astype(np.float64))
             n += 1
         el = time.perf_counter() - t0
         return {"value": n * B / el, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
-                "sample": "first %d decode steps (batch %d) of the same workload from a cold table: "
+                "sample": "%d decode steps (batch %d) of the same workload recipe from a cold table: "
                           "float64 numpy oracle incl. routing, LRU plan, record copies (host memcpy, "
                           "no PCIe) and SwiGLU experts, %.1f s" % (n, B, el)}
     res["cpu"] = cpu
@@ -256,8 +317,10 @@ def bench_stack(args, torch, dev):
     run(args.warmup, args.steps)
     torch.cuda.synchronize()
     tm = merge_timing([L.timing_read() for L in layers])
+    floor_us = ewp.timing_floor()
     d = {k: s1[k] - s0[k] for k in s1}
     res = {"value": args.steps / el, "ms_per_step": el / args.steps * 1e3, "timing": tm, "stats": d,
+           "floor_us": floor_us,
            "cfg": cfg, "B": 1,
            "workload": "48-layer Qwen3-30B-A3B-shaped MoE stack (attention omitted), int4 asym g128 "
                        "experts, E=128 top_k=8 hidden=2048 intermediate=768, K=92 slots per layer, "
@@ -269,21 +332,23 @@ def bench_stack(args, torch, dev):
         from oracle.layer import PagedLayer
         refs = [PagedLayer(pool[gen.layer_permutation(cfg, l)], cfg.fmt, cfg.E, cfg.top_k, cfg.H,
                            cfg.I, cfg.K) for l in range(4)]
-        xv = gen.bf16_bits_to_f32(x0[0]).astype(np.float64)
         from oracle.layer import bf16_rne
         t0 = time.perf_counter()
-        nl = 0
-        for l in range(4):
-            o, *_ = refs[l].step(logits[0, l], xv)
-            xv = bf16_rne(xv + o)
-            nl += 1
-            if time.perf_counter() - t0 > budget:
-                break
+        nl = nt = 0
+        # tokens in order through the first four layers (tables start cold),
+        # until the budget is spent; the rate is scaled to 48 layers
+        while nt < len(x0) and time.perf_counter() - t0 < budget:
+            xv = gen.bf16_bits_to_f32(x0[nt]).astype(np.float64)
+            for l in range(4):
+                o, *_ = refs[l].step(logits[nt, l], xv)
+                xv = bf16_rne(xv + o)
+                nl += 1
+            nt += 1
         el = time.perf_counter() - t0
         per_token = el / nl * cfg.layers
         return {"value": 1.0 / per_token, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
-                "sample": "token 0 through the first %d of 48 layers (cold tables) with the float64 "
-                          "numpy oracle, %.1f s, scaled to 48 layers" % (nl, el)}
+                "sample": "tokens 0..%d through the first 4 of 48 layers (tables start cold) with the "
+                          "float64 numpy oracle, %.1f s, scaled to 48 layers" % (nt - 1, el)}
     res["cpu"] = cpu
 
     def cleanup():
@@ -333,8 +398,10 @@ def bench_prefill(args, torch, dev):
     run(args.warmup, args.steps)
     torch.cuda.synchronize()
     tm = merge_timing([L.timing_read() for L in layers])
+    floor_us = ewp.timing_floor()
     d = {k: s1[k] - s0[k] for k in s1}
     res = {"value": args.steps * T / el, "ms_per_step": el / args.steps * 1e3, "timing": tm,
+           "floor_us": floor_us,
            "stats": d, "cfg": cfg, "B": T,
            "workload": "prefill: one 2048-token chunk through a 48-layer Qwen3-30B-A3B-shaped bf16 "
                        "MoE stack (attention omitted), E=128 top_k=8 hidden=2048 intermediate=768, "
@@ -374,7 +441,9 @@ def bench_prefill(args, torch, dev):
 
 # ---------------------------------------------------------------- report
 
-def roofline(res, workload):
+def roofline(res, workload, variant):
+    """variant: the workload name plus any non-default option; PMC traffic is
+    stored per variant (the committed profiles use the default options)."""
     tm = res["timing"]
     if workload == "prefill-bf16":
         kinds = [k for k in ("gemm_up", "gemm_down") if tm[k]["count"]]
@@ -386,22 +455,27 @@ def roofline(res, workload):
         return {"bound": "mfma", "kernel": kname, "achieved": round(flops, 1),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(flops / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profiles(kname, workload),
+                "traffic": traffic_from_profiles(kname, variant),
                 "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
                 "algorithmic_flops_per_launch": tm[dom]["flops"] / tm[dom]["count"],
-                "weight_GBps": round(gbps, 1), "weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+                "weight_GBps": round(gbps, 1), "weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "launch_floor_us": round(res["floor_us"], 3)}
     kinds = [k for k in ("ffn_up", "ffn_down") if tm[k]["count"]]
     dom = max(kinds, key=lambda k: tm[k]["ms"])
     sec = tm[dom]["ms"] * 1e-3
     achieved = tm[dom]["bytes"] / sec / 1e9
     kname = {"ffn_up": "ffn_up_kernel", "ffn_down": "ffn_down_kernel"}[dom]
     both = (tm["ffn_up"]["bytes"] + tm["ffn_down"]["bytes"]) / ((tm["ffn_up"]["ms"] + tm["ffn_down"]["ms"]) * 1e-3) / 1e9
+    avg_us = tm[dom]["ms"] / tm[dom]["count"] * 1e3
+    per_launch = tm[dom]["bytes"] / tm[dom]["count"]
+    # launch_floor_us: what the same events report for an empty kernel (context only)
     return {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_from_profiles(kname, workload),
-            "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
-            "algorithmic_bytes_per_launch": tm[dom]["bytes"] / tm[dom]["count"],
-            "ffn_up_plus_down_GBps": round(both, 1)}
+            "traffic": traffic_from_profiles(kname, variant),
+            "avg_launch_us": round(avg_us, 3),
+            "algorithmic_bytes_per_launch": per_launch,
+            "ffn_up_plus_down_GBps": round(both, 1),
+            "launch_floor_us": round(res["floor_us"], 3)}
 
 
 def main():
@@ -417,7 +491,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter CSVs of this workload "
+                         "(FETCH_SIZE, WRITE_SIZE) into profiles/pmc_traffic.json")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Paged Experts path is single-GPU and this "
               "build has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -437,6 +517,9 @@ def main():
     res = fn(args, torch, dev)
     log("timed %d steps: %.3f ms/step" % (args.steps, res["ms_per_step"]))
     tm, st, cfg = res["timing"], res["stats"], res["cfg"]
+    variant = args.workload + "".join(
+        s for s, on in ((" lookahead", args.lookahead), (" uniform", args.routing != "correlated"),
+                        (" batch=%d" % args.batch, args.batch != 1)) if on)
     pin = tm["page_in"]
     line = {
         "metric": METRIC,
@@ -456,7 +539,7 @@ def main():
         "config": {"workload": res["workload"], "batch": res["B"], "num_slots": cfg.K,
                    "experts": cfg.E, "top_k": cfg.top_k, "layers": cfg.layers,
                    "lookahead": bool(args.lookahead), "parallelism": "single GPU"},
-        "roofline": roofline(res, args.workload),
+        "roofline": roofline(res, args.workload, variant),
         "kernels_us": {k: round(v["ms"] / v["count"] * 1e3, 3) for k, v in tm.items() if v["count"]},
         "page_in": {"GBps": round(pin["bytes"] / max(pin["ms"], 1e-9) / 1e6, 2),
                     "waves_with_copies": pin["count"], "bytes_per_step": st["bytes_paged"] / args.steps},

@@ -89,6 +89,7 @@ EXPORTS = {
                                            ctypes.c_void_p, ctypes.c_void_p]),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_Timing)]),
+    "moe_timing_floor": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]),
     "moe_host_alloc": (ctypes.c_void_p, [ctypes.c_size_t]),
     "moe_host_free": (None, [ctypes.c_void_p]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -283,6 +284,14 @@ class Layer:
         _check(lib().moe_timing_read(self.handle, ctypes.byref(t)))
         return {name: {"count": t.count[i], "ms": t.ms[i], "bytes": t.bytes[i], "flops": t.flops[i]}
                 for i, name in enumerate(TIMERS)}
+
+
+def timing_floor(stream=None, reps=100):
+    """Microseconds the layer timers report for an empty kernel on `stream`:
+    the per-launch floor included in every timing_read figure."""
+    us = ctypes.c_double()
+    _check(lib().moe_timing_floor(_stream(stream), int(reps), ctypes.byref(us)))
+    return us.value
 
 
 def residual_bf16(x_in, out, x_out, stream=None):

@@ -197,6 +197,11 @@ moe_status self_check(moe_layer* L);
 
 }  // namespace
 
+namespace {
+// Does nothing: its timed duration is the floor of every timed launch.
+__global__ void empty_kernel() {}
+}  // namespace
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
@@ -700,6 +705,32 @@ moe_status moe_timing_read(moe_layer* L, moe_timing* out) {
   *out = L->acc;
   std::memset(&L->acc, 0, sizeof(L->acc));
   return MOE_OK;
+}
+
+moe_status moe_timing_floor(void* stream, int32_t reps, double* us) {
+  if (!us) return fail(MOE_ERR_INVALID_ARG, "null output");
+  if (reps < 1 || reps > 10000) return fail(MOE_ERR_INVALID_ARG, "reps must be in 1..10000");
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t a = nullptr, b = nullptr;
+  moe_status st = MOE_OK;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    st = fail(MOE_ERR_HIP, "event creation failed");
+  } else {
+    double total = 0.0;
+    for (int r = 0; r <= reps && !st; ++r) {  // launch 0 warms up, untimed
+      hipExtLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s, a, b, 0);
+      float ms = 0.f;
+      if (hipGetLastError() != hipSuccess || hipEventSynchronize(b) != hipSuccess ||
+          hipEventElapsedTime(&ms, a, b) != hipSuccess)
+        st = fail(MOE_ERR_HIP, "empty-kernel timing failed");
+      else if (r > 0)
+        total += ms;
+    }
+    if (!st) *us = total * 1e3 / reps;
+  }
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  return st;
 }
 
 }  // extern "C"

@@ -274,6 +274,15 @@ typedef struct moe_timing {
 moe_status moe_timing_enable(moe_layer* layer, int32_t enable);
 moe_status moe_timing_read(moe_layer* layer, moe_timing* out);
 
+/* Floor of the figures above: the average duration the same dispatch-stamped
+ * events report for an empty one-workgroup kernel, over `reps` (1..10000)
+ * launches on `stream` (a hipStream_t; NULL = default stream). It is the
+ * part of every timed launch that does not depend on the kernel's work (the
+ * dispatch and the cache actions at kernel boundaries). Synchronous; *us
+ * receives microseconds. MOE_ERR_INVALID_ARG for a null us or reps out of
+ * range, MOE_ERR_HIP if a launch or event call fails. */
+moe_status moe_timing_floor(void* stream, int32_t reps, double* us);
+
 /* Page-locked host memory for expert stores (hipHostMalloc), and its release. */
 void* moe_host_alloc(size_t bytes);
 void moe_host_free(void* p);
