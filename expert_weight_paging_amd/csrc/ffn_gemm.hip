@@ -25,14 +25,15 @@
 // rows and the 128 matching up rows of W13; down: 256 rows of W_d) and covers
 // up to 256 of the expert's rows per pass, so each weight byte leaves HBM
 // once per expert for all but the hottest experts, and each activation row is
-// copied once per 256 weight rows. The k loop runs in steps
-// of 32. Each step's weight tile (128 x 32) and activation tile(s) (rows x 32)
-// are filled by direct global-to-LDS copies (no register staging) into two
-// LDS rings: the weight ring, fed from HBM, runs 3 to 7 steps ahead of the
-// matrix cores; the activation ring, mostly fed from L2, 2 steps ahead.
+// copied once per 256 weight rows. The k loop runs in steps of 64 (up) or 32
+// (down). Each step's weight tile (256 x 64 or 256 x 32) and activation
+// tile(s) are filled by direct global-to-LDS copies (no register staging) into
+// two LDS rings: the weight ring, fed from HBM, runs 2 to 6 steps ahead of the
+// matrix cores; the activation ring, mostly fed from L2, 1 or 2 steps ahead.
 // A wait on the vector-memory counter plus a barrier hands a step over. Only
-// the 64-row groups that hold routed rows are copied (template RG). The
-// 16-byte chunks of a tile row are XOR-swizzled by (row / 2) mod 4, which
+// the 64-row groups that hold routed rows are copied (template RG; the down
+// GEMM rounds up to an even count). The
+// 16-byte chunks of a tile row are XOR-swizzled by row (see lds_chunk), which
 // makes the fragment reads free of LDS bank conflicts; the swizzle is applied
 // by choosing each copy lane's source chunk, since one copy instruction
 // writes its 64 lanes contiguously.
@@ -55,8 +56,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 512;              // eight wavefronts per workgroup
 constexpr int BN = 256;                    // weight rows per workgroup
-constexpr int BK = 32;                     // reduction elements per k-step
-constexpr int W_CH = BN * BK * 2 / 16;     // 16-byte chunks of the weight tile (1024)
 constexpr int UP_HCOLS = BN / 2;           // h columns per workgroup (up)
 constexpr int DN_COLS = BN;                // output columns per workgroup (down)
 constexpr int kXcd = 8;                    // XCDs; consecutive workgroups go round-robin over them
@@ -73,10 +72,21 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)(b >> 16);
 }
 
-// LDS chunk of logical chunk c (0..3) of tile row r; and, for LDS chunk p, the
-// logical chunk it holds (row p / 4): the two are inverse of each other.
-__device__ inline int lds_chunk(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
-__device__ inline int src_chunk(int p) { return (p & 3) ^ ((p >> 3) & 3); }
+// Tile rows of CPR 16-byte chunks (CPR = 4: 32 bf16 per row, CPR = 8: 64).
+// LDS chunk of logical chunk c of tile row r; and, for LDS chunk p, the
+// logical chunk it holds (its row is p / CPR): the two are inverse of each
+// other. The XOR spreads the 8 rows that one quarter-wavefront of a fragment
+// read touches over all 32 banks.
+template <int CPR>
+__device__ inline int lds_chunk(int r, int c) {
+  if constexpr (CPR == 4) return r * 4 + (c ^ ((r >> 1) & 3));
+  else return r * 8 + (c ^ (r & 7));
+}
+template <int CPR>
+__device__ inline int src_chunk(int p) {
+  if constexpr (CPR == 4) return (p & 3) ^ ((p >> 3) & 3);
+  else return (p & 7) ^ ((p >> 3) & 7);
+}
 
 // Global-to-LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
 // address lds + 16 * l (lds wave-uniform, passed in M0). Issued from inline
@@ -110,14 +120,22 @@ __device__ inline void stage_barrier() {
 // of a k-step comes from HBM and the activation tile(s) mostly from L2, so the
 // weight ring runs deeper (SW stages) than the activation ring (SA stages) to
 // keep enough HBM bytes in flight. One workgroup per CU owns the 160 KB LDS.
+// The up GEMM (k = H) runs k-steps of 64, so that every copy instruction moves
+// whole 128-byte lines (8 rows); the down GEMM (k = I, two activation tiles)
+// keeps k-steps of 32 to fit its rings.
 template <bool UP>
 struct Tiles {
   static constexpr int NA = UP ? 1 : 2;  // activation tiles: x, or (h_hi, h_lo)
   static constexpr int BUDGET_CH = 160 * 1024 / 16;
+  static constexpr int BK = UP ? 64 : 32;  // reduction elements per k-step
+  static constexpr int CPR = BK / 8;       // 16-byte chunks per tile row
+  static constexpr int W_CH = BN * CPR;    // chunks of the weight tile
+  static constexpr int NW = W_CH / kThreads;  // weight copies per thread per stage
 };
 template <bool UP, int RG>
 struct Ring {
-  static constexpr int A_CH = Tiles<UP>::NA * RG * 256;  // activation chunks per stage
+  static constexpr int W_CH = Tiles<UP>::W_CH;
+  static constexpr int A_CH = Tiles<UP>::NA * RG * 64 * Tiles<UP>::CPR;  // activation chunks per stage
   static constexpr int SW3 = (Tiles<UP>::BUDGET_CH - 3 * A_CH) / W_CH;
   static constexpr int SA = SW3 > 3 ? 3 : 2;
   static constexpr int SW_FIT = (Tiles<UP>::BUDGET_CH - SA * A_CH) / W_CH;
@@ -131,13 +149,15 @@ struct Ring {
 // its weight copy, so "stage it has landed" is "all copies up to the
 // activation copy of stage it have completed" (copies complete in order).
 template <bool UP, int RG>
-__device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (&wsrc)[2], int col0,
-                          int q0, int mb, int mcnt) {
-  static_assert(RG == 2 || RG == 4, "passes cover 128 or 256 rows");
+__device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (&wsrc)[Tiles<UP>::NW],
+                          int col0, int q0, int mb, int mcnt) {
+  static_assert(RG >= 1 && RG <= 4 && (RG * 64 * Tiles<UP>::CPR) % kThreads == 0,
+                "a pass covers 64 * RG rows, copied by whole 512-chunk instructions");
   using R = Ring<UP, RG>;
-  constexpr int NA = Tiles<UP>::NA, SA = R::SA, SW = R::SW;
-  constexpr int GI = RG / 2;           // activation copies per tile per thread (512 chunks each)
-  constexpr int nA = NA * GI, nW = 2;  // copy instructions per thread per stage
+  using Tl = Tiles<UP>;
+  constexpr int NA = Tl::NA, SA = R::SA, SW = R::SW, BK = Tl::BK, CPR = Tl::CPR;
+  constexpr int GI = RG * 64 * CPR / kThreads;  // activation copies per tile per thread
+  constexpr int nA = NA * GI, nW = Tl::NW;      // copy instructions per thread per stage
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform, kept in an SGPR
   const int wm = wid >> 2, wn = wid & 3;
@@ -145,14 +165,14 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
   const int KD = UP ? H : I;
   const int nit = KD / BK;
 
-  // Activation sources: chunk p = g * 512 + tid of tile u is row p / 4; rows
+  // Activation sources: chunk p = g * 512 + tid of tile u is row p / CPR; rows
   // past the expert's end reload the pass's first row (their results are
   // discarded: a row of the product depends only on that row of A).
   const uint16_t* asrc[NA][GI];
 #pragma unroll
   for (int g = 0; g < GI; ++g) {
     const int p = g * kThreads + tid;
-    const int r = p >> 2, c = src_chunk(p);
+    const int r = p / CPR, c = src_chunk<CPR>(p);
     const int q = q0 + mb + (r < mcnt ? r : 0);
     if (UP) {
       asrc[0][g] = (const uint16_t*)a.x + (size_t)(a.pair_list[q] / a.k) * H + c * 8;
@@ -170,13 +190,13 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
 #pragma unroll
     for (int u = 0; u < NA; ++u)
 #pragma unroll
-      for (int g = 0; g < GI; ++g) dma16(asrc[u][g] + s * BK, st + (u * RG * 256 + g * kThreads) * 16);
+      for (int g = 0; g < GI; ++g) dma16(asrc[u][g] + s * BK, st + (u * GI + g) * kThreads * 16);
   };
   auto issue_w = [&](int s) {
     if (s < 0 || s >= nit) return;
-    const uint32_t st = ldsw + (s % SW) * W_CH * 16;
+    const uint32_t st = ldsw + (s % SW) * R::W_CH * 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(wsrc[i] + s * BK, st + (i * kThreads) * 16);
+    for (int i = 0; i < nW; ++i) dma16(wsrc[i] + s * BK, st + (i * kThreads) * 16);
   };
 
   constexpr int MT = RG * 2;  // 16-row sub-tiles per wavefront
@@ -211,35 +231,40 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
     issue_a(it + SA - 1);
     issue_w(it + SW - 1);
     const uint4* st = smem + (it % SA) * R::A_CH;
-    const uint4* wt = smem + SA * R::A_CH + (it % SW) * W_CH;
-    // B fragments: lane holds weight-tile row (lane % 16) of the sub-tile, chunk lane / 16
-    bf16x8 bf[4];
+    const uint4* wt = smem + SA * R::A_CH + (it % SW) * R::W_CH;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      // up: h columns wn*32 + (n%2)*16 .. (gate rows for n < 2, the matching up
-      // rows 128 further down the tile for n >= 2); down: columns wn*64 + n*16 ..
-      const int trow = UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15))
-                          : (wn * 64 + n * 16 + (lane & 15));
-      bf[n] = as_bf16x8(wt[lds_chunk(trow, lane >> 4)]);
-    }
+    for (int ks = 0; ks < BK / 32; ++ks) {  // 32-element sub-steps of one MFMA each
+      // B fragments: lane holds weight-tile row (lane % 16) of the sub-tile,
+      // chunk 4 * ks + lane / 16
+      bf16x8 bf[4];
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      // all of this wavefront's A fragments are read up front (sub-tiles past the
-      // expert's end read stale LDS rows, in bounds and unused); the empty asm
-      // keeps the reads from being sunk into the per-sub-tile branches below,
-      // which would serialise read, wait and MFMA
-      bf16x8 af[MT];
+      for (int n = 0; n < 4; ++n) {
+        // up: h columns wn*32 + (n%2)*16 .. (gate rows for n < 2, the matching up
+        // rows 128 further down the tile for n >= 2); down: columns wn*64 + n*16 ..
+        const int trow = UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15))
+                            : (wn * 64 + n * 16 + (lane & 15));
+        bf[n] = as_bf16x8(wt[lds_chunk<CPR>(trow, 4 * ks + (lane >> 4))]);
+      }
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        af[m] = as_bf16x8(st[u * RG * 256 + lds_chunk((2 * m + wm) * 16 + (lane & 15), lane >> 4)]);
+      for (int u = 0; u < NA; ++u) {
+        // all of this wavefront's A fragments are read up front (sub-tiles past the
+        // expert's end read stale LDS rows, in bounds and unused); the empty asm
+        // keeps the reads from being sunk into the per-sub-tile branches below,
+        // which would serialise read, wait and MFMA
+        bf16x8 af[MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(af[m]));
+        for (int m = 0; m < MT; ++m)
+          af[m] = as_bf16x8(st[u * GI * kThreads +
+                               lds_chunk<CPR>((2 * m + wm) * 16 + (lane & 15), 4 * ks + (lane >> 4))]);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if ((2 * m + wm) * 16 >= mcnt) break;  // uniform per wavefront
+        for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(af[m]));
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf[n], acc[m][n], 0, 0, 0);
+        for (int m = 0; m < MT; ++m) {
+          if ((2 * m + wm) * 16 >= mcnt) break;  // uniform per wavefront
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf[n], acc[m][n], 0, 0, 0);
+        }
       }
     }
   }
@@ -295,18 +320,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
   const uint16_t* W = (const uint16_t*)(rec + (UP ? (size_t)0 : (size_t)2 * I * H * 2));
   const int col0 = tile * (UP ? UP_HCOLS : DN_COLS);
   // weight copy sources: chunk p = i * 512 + tid of the weight tile is tile row
-  // p / 4 (down: rows past H, in a last half-width tile, reread row H - 1)
-  const uint16_t* wsrc[2];
+  // p / CPR (down: rows past H, in a last half-width tile, reread row H - 1)
+  constexpr int CPR = Tiles<UP>::CPR, NW = Tiles<UP>::NW;
+  const uint16_t* wsrc[NW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int p = i * kThreads + threadIdx.x;
-    const int r = p >> 2, c = src_chunk(p);
+    const int r = p / CPR, c = src_chunk<CPR>(p);
     const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
     wsrc[i] = W + (size_t)wrow * KD + c * 8;
   }
   for (int mb = 0; mb < M; mb += BMP) {
     const int mcnt = min(BMP, M - mb);
-    if (mcnt <= 128) gemm_pass<UP, 2>(a, smem, wsrc, col0, q0, mb, mcnt);  // uniform branch
+    // uniform branches: the smallest pass shape that holds mcnt rows (up: any
+    // number of 64-row groups; down, with 32-wide rows: an even number)
+    const int rg = (mcnt + 63) >> 6;
+    if (UP && rg == 1) gemm_pass<UP, (UP ? 1 : 2)>(a, smem, wsrc, col0, q0, mb, mcnt);
+    else if (rg <= 2) gemm_pass<UP, 2>(a, smem, wsrc, col0, q0, mb, mcnt);
+    else if (UP && rg == 3) gemm_pass<UP, (UP ? 3 : 4)>(a, smem, wsrc, col0, q0, mb, mcnt);
     else gemm_pass<UP, 4>(a, smem, wsrc, col0, q0, mb, mcnt);
   }
 }
