@@ -205,6 +205,7 @@ __device__ void plan_body(const int32_t* ids, int P, int T, int E, int K, uint8_
   }
   long long clock = pre.clock;
   __syncthreads();
+#pragma unroll 4
   for (int p = tid; p < P; p += NT) atomicAdd(&sm.cnt[ids[p]], 1);
   __syncthreads();
 
@@ -265,6 +266,7 @@ __device__ void plan_body(const int32_t* ids, int P, int T, int E, int K, uint8_
   if (tid == 0) *g_clock = clock;
 
   // per-pair slot and wave
+#pragma unroll 4
   for (int p = tid; p < P; p += NT) {
     const int pos = sm.pos[ids[p]];
     dev.slot_ids[p] = sm.order_s[pos];
@@ -383,29 +385,44 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
 }
 
 // ------------------------------------------------------------------ grouping
-// One wavefront per position of the wave order: collects the pair indices of
-// its expert in ascending order (ballot + prefix popcount), so that the list
-// and therefore every later summation order is deterministic.
-__global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ ids, int P,
-                                                    PlanDev dev) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int i = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+// One workgroup per position i of the wave order: a stable compaction of the
+// pair indices routed to its expert, in ascending order (so the list, and
+// every later summation order, is deterministic). Thread t owns 64 consecutive
+// pairs of each round of 256 x 64: a 64-bit match mask, a workgroup exclusive
+// scan of the match counts, then each thread writes its matches in order.
+constexpr int kGroupThreads = 256;
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int P,
+                                                              PlanDev dev) {
+  __shared__ int s_warp[kGroupThreads / kWave + 1];
+  const int i = blockIdx.x;
   const int D = dev.counts[0];
-  if (i >= D) return;
+  if (i >= D) return;  // uniform over the workgroup
   const int e = dev.order_expert[i];
-  const int base = dev.pair_off[i];
-  int running = 0;
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int c = 0; c < P; c += kWave) {
-    const int p = c + lane;
-    const bool m = p < P && ids[p] == e;
-    const unsigned long long mask = __ballot(m);
-    if (m) {
-      const int q = base + running + __popcll(mask & below);
+  int running = dev.pair_off[i];
+  for (int r0 = 0; r0 < P; r0 += kGroupThreads * 64) {
+    const int p0 = r0 + threadIdx.x * 64;
+    unsigned long long m = 0;
+    if (p0 + 64 <= P) {
+#pragma unroll
+      for (int j = 0; j < 64; j += 4) {
+        const int4 v = *(const int4*)(ids + p0 + j);  // p0 + j is a multiple of 4
+        m |= (unsigned long long)(v.x == e) << j | (unsigned long long)(v.y == e) << (j + 1) |
+             (unsigned long long)(v.z == e) << (j + 2) | (unsigned long long)(v.w == e) << (j + 3);
+      }
+    } else {
+      for (int j = 0; p0 + j < P && j < 64; ++j) m |= (unsigned long long)(ids[p0 + j] == e) << j;
+    }
+    int total;
+    int q = running + block_exscan<kGroupThreads>(__popcll(m), s_warp, &total);
+    while (m) {
+      const int p = p0 + __ffsll((long long)m) - 1;
+      m &= m - 1;
       dev.pair_list[q] = p;
       dev.pair_pos[p] = q;
+      ++q;
     }
-    running += __popcll(mask);
+    running += total;
   }
 }
 
@@ -453,7 +470,8 @@ hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids,
 hipError_t launch_plan(const int32_t* ids, int T, int k, int E, int K, void* state, PlanDev dev,
                        PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s) {
   const StateLayout sl = state_layout(E, K);
-  if (E <= 256)
+  // the per-pair loops dominate for many pairs: use the widest block then
+  if (E <= 256 && T * k <= 4096)
     plan_kernel<256><<<1, 256, 0, s>>>(ids, T * k, T, E, K, (uint8_t*)state, sl, dev, host_hdr_dev, seq);
   else
     plan_kernel<1024><<<1, 1024, 0, s>>>(ids, T * k, T, E, K, (uint8_t*)state, sl, dev, host_hdr_dev, seq);
@@ -482,7 +500,7 @@ hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hipStream_t s,
                         hipEvent_t ev1) {
   if (T <= 0) return hipSuccess;
-  launch_k(group_kernel, dim3((E + 3) / 4), dim3(256), s, nullptr, ev1, ids, T * k, dev);
+  launch_k(group_kernel, dim3(E < T * k ? E : T * k), dim3(kGroupThreads), s, nullptr, ev1, ids, T * k, dev);
   return hipGetLastError();
 }
 
