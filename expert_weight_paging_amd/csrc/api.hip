@@ -191,7 +191,7 @@ double down_weight_bytes(const moe_layer* L) {
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows, bool combine);
+                   int max_rows, bool combine, uint16_t* x_res = nullptr);
 
 moe_status self_check(moe_layer* L);
 
@@ -397,7 +397,8 @@ void moe_plan_destroy(moe_plan* p) {
 }
 
 namespace {
-moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after);
+moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after,
+                      hipStream_t on = nullptr);
 }
 
 moe_status moe_route(moe_layer* L, const float* logits, int32_t T, moe_plan* p) {
@@ -405,8 +406,11 @@ moe_status moe_route(moe_layer* L, const float* logits, int32_t T, moe_plan* p) 
 }
 
 namespace {
-// `after`, if given, is an event the route stream waits for before routing.
-moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after) {
+// `after`, if given, is an event the route stream waits for before routing;
+// `on`, if given, replaces the layer's route stream for this step.
+moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after,
+                      hipStream_t on) {
+  const hipStream_t rs = on ? on : L->route;
   if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
   if (p->layer != L) return fail(MOE_ERR_INVALID_ARG, "plan was created for another layer");
   if (T < 0 || T > p->max_tokens) return fail(MOE_ERR_INVALID_ARG, "num_tokens out of 0..max_tokens");
@@ -414,26 +418,26 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
   if (L->cur_plan && L->next_fwd < L->n_waves)
     return fail(MOE_ERR_STATE, "previous step of this layer has waves not yet forwarded");
 
-  if (p->consumed_recorded) HIP_TRY(hipStreamWaitEvent(L->route, p->ev_consumed, 0));
-  if (after) HIP_TRY(hipStreamWaitEvent(L->route, after, 0));
+  if (p->consumed_recorded && rs != L->compute) HIP_TRY(hipStreamWaitEvent(rs, p->ev_consumed, 0));
+  if (after) HIP_TRY(hipStreamWaitEvent(rs, after, 0));
   TimerRec tr{};
   moe_status st = timer_events(L, &tr);
   if (st) return st;
   const int32_t seq = ++p->seq;
   if (route_small_ok(T, L->k)) {
     HIP_TRY(launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, p->hdr_dev, seq,
-                                    L->route, tr.a, tr.b));
+                                    rs, tr.a, tr.b));
   } else {
-    HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, L->route, tr.a));
-    HIP_TRY(launch_plan(p->dev.ids, T, L->k, L->E, L->K, L->state, p->dev, p->hdr_dev, seq, L->route));
-    HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, L->route, tr.b));
+    HIP_TRY(launch_router(logits, T, L->E, L->k, p->dev.ids, p->dev.weights, rs, tr.a));
+    HIP_TRY(launch_plan(p->dev.ids, T, L->k, L->E, L->K, L->state, p->dev, p->hdr_dev, seq, rs));
+    HIP_TRY(launch_group(p->dev.ids, T, L->k, L->E, p->dev, rs, tr.b));
   }
   if (T > 0) timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
   else if (L->timing) {
     L->pool.push_back(tr.a);
     L->pool.push_back(tr.b);
   }
-  HIP_TRY(hipEventRecord(L->ev_routed, L->route));
+  HIP_TRY(hipEventRecord(L->ev_routed, rs));
   // The one host synchronisation of a layer-step: wait until the slot-plan
   // kernel has published the plan into pinned host memory.
   volatile int32_t* flag = &p->hdr->seq;
@@ -442,7 +446,7 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
   while (__atomic_load_n(flag, __ATOMIC_ACQUIRE) != seq) {
     _mm_pause();
     if (++spins % 4096 == 0) {
-      hipError_t q = hipStreamQuery(L->route);
+      hipError_t q = hipStreamQuery(rs);
       if (q != hipSuccess && q != hipErrorNotReady)
         return fail(MOE_ERR_HIP, std::string("route kernels failed: ") + hipGetErrorString(q));
       if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60))
@@ -541,7 +545,20 @@ moe_status moe_page_in(moe_layer* L, const moe_plan* p, int32_t w) {
   return MOE_OK;
 }
 
+namespace {
+moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out,
+                        uint16_t* x_res);
+}
+
 moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out) {
+  return forward_impl(L, p, w, x, out, nullptr);
+}
+
+namespace {
+// x_res, if given, receives the stack residual bf16_rne(x_res + out) from the
+// kernel that completes out (only on a step's last wave).
+moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out,
+                        uint16_t* x_res) {
   if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
   if (L->cur_plan != p) return fail(MOE_ERR_STATE, "plan is not this layer's current step");
   if (w != L->next_fwd || L->next_page != w + 1)
@@ -573,12 +590,12 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
     HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo + n_res, n_exp - n_res,
                  pairs_in(o_lo + n_res, n_exp - n_res), T, x, out, w > 0 || !gemm, p->dev.pair_pos,
-                 p->dev.wave_of, w, T, /*combine=*/gemm);
+                 p->dev.wave_of, w, T, /*combine=*/gemm, x_res);
     if (st) return st;
   } else {
     if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, pairs_in(o_lo, n_exp), T, x, out,
-                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm);
+                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res);
     if (st) return st;
   }
   HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
@@ -589,6 +606,7 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
   if (L->next_fwd == L->n_waves) L->cur_plan = nullptr;
   return MOE_OK;
 }
+}  // namespace
 
 moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out, int64_t n,
                              void* stream) {
@@ -619,8 +637,6 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
   if (T == 0) return MOE_OK;
   const size_t lstride = (size_t)T * L0->E;
   hipStream_t cs = L0->compute;
-  hipEvent_t resid_done = nullptr;
-  HIP_TRY(hipEventCreateWithFlags(&resid_done, hipEventDisableTiming));
   moe_status st = MOE_OK;
   auto run = [&]() -> moe_status {
     moe_status r = route_impl(layers[0], logits, T, plans[0], nullptr);
@@ -644,21 +660,20 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
           r = moe_page_in(L, P, w);
           if (r) return r;
         }
-        r = moe_forward(L, P, w, x, out);
+        // the kernel that completes the last wave's out also applies the residual
+        r = forward_impl(L, P, w, x, out, w == nw - 1 ? (uint16_t*)x : nullptr);
         if (r) return r;
       }
-      if (launch_residual((const uint16_t*)x, out, (uint16_t*)x, (int64_t)T * L->H, cs) != hipSuccess)
-        return fail(MOE_ERR_HIP, "residual launch failed");
       if (!lookahead && l + 1 < n) {
-        if (hipEventRecord(resid_done, cs) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord");
-        r = route_impl(layers[l + 1], logits + (l + 1) * lstride, T, plans[l + 1], resid_done);
+        // strict order: layer l+1 is routed on the compute stream, behind the
+        // residual, with no cross-stream hand-over
+        r = route_impl(layers[l + 1], logits + (l + 1) * lstride, T, plans[l + 1], nullptr, cs);
         if (r) return r;
       }
     }
     return MOE_OK;
   };
   st = run();
-  (void)hipEventDestroy(resid_done);
   return st;
 }
 
@@ -744,7 +759,7 @@ namespace {
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows, bool combine) {
+                   int max_rows, bool combine, uint16_t* x_res) {
   FfnArgs a{};
   a.fmt = L->fmt;
   a.E = L->E;
@@ -787,6 +802,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     timer_push(L, &t1, MOE_T_FFN_UP, up_b, flop_up);
     a.ev0 = t2.a;
     a.ev1 = t2.b;
+    a.x_res = x_res;  // the down kernel completes out
     HIP_TRY(launch_ffn_down(a, L->compute));
     timer_push(L, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn);
   } else {
@@ -804,6 +820,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
       if ((st = timer_events(L, &t3))) return st;
       a.ev0 = t3.a;
       a.ev1 = t3.b;
+      a.x_res = x_res;  // the combine completes out
       HIP_TRY(launch_combine(a, pair_pos, wave_of, wave, L->compute));
       timer_push(L, &t3, MOE_T_COMBINE, 0.0, 0.0);
     }

@@ -343,10 +343,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
 }
 
 // out[t][n] (+)= sum_j y[pos(t, j)][n] over the pairs of this wave, j ascending.
+// With x_res, the residual of a layer stack is applied to the final out:
+// x_res = bf16_rne(x_res + out).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const int32_t* __restrict__ wave_of, int wave,
-                                                      int T, int k, int H, float* out, int accumulate) {
+                                                      int T, int k, int H, float* out, int accumulate,
+                                                      uint16_t* x_res) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= (int64_t)T * H) return;
   const int t = (int)(i / H), n = (int)(i % H);
@@ -361,6 +364,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     acc.w += v.w;
   }
   *(float4*)(out + i) = acc;
+  if (x_res) {
+    const uint2 xv = *(const uint2*)(x_res + i);
+    uint2 r;
+    r.x = (uint32_t)f32_to_bf16_rne(__uint_as_float(xv.x << 16) + acc.x) |
+          ((uint32_t)f32_to_bf16_rne(__uint_as_float(xv.x & 0xFFFF0000u) + acc.y) << 16);
+    r.y = (uint32_t)f32_to_bf16_rne(__uint_as_float(xv.y << 16) + acc.z) |
+          ((uint32_t)f32_to_bf16_rne(__uint_as_float(xv.y & 0xFFFF0000u) + acc.w) << 16);
+    *(uint2*)(x_res + i) = r;
+  }
 }
 
 }  // namespace
@@ -388,7 +400,7 @@ hipError_t launch_combine(const FfnArgs& a, const int32_t* pair_pos, const int32
   const int64_t n4 = ((int64_t)a.T * a.H) / 4;
   if (n4 <= 0) return hipSuccess;
   launch_k(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, a.ev0, a.ev1, a.y, pair_pos,
-           wave_of, wave, a.T, a.k, a.H, a.out, a.accumulate);
+           wave_of, wave, a.T, a.k, a.H, a.out, a.accumulate, a.x_res);
   return hipGetLastError();
 }
 

@@ -29,6 +29,12 @@ namespace {
 constexpr int kWave = 64;
 
 
+__device__ inline uint16_t f32_to_bf16_rne(float v) {
+  uint32_t b = __float_as_uint(v);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -446,7 +452,12 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) v += part[w][t][r];
     float* o = a.out + (size_t)t * H + r0 + r;
-    *o = (a.accumulate ? *o : 0.f) + v;
+    const float ov = (a.accumulate ? *o : 0.f) + v;
+    *o = ov;
+    if (a.x_res) {  // stack residual on the final value of out
+      uint16_t* xr = a.x_res + (size_t)t * H + r0 + r;
+      *xr = f32_to_bf16_rne(__uint_as_float((uint32_t)*xr << 16) + ov);
+    }
   }
 }
 

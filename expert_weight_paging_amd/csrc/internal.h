@@ -144,6 +144,8 @@ struct FfnArgs {
   uint16_t* hb_lo;     // GEMM scratch bf16 [T*k][I], low part of h
   float* y;            // GEMM scratch fp32 [T*k][H]
   int max_rows;        // upper bound on pairs of one expert in this wave (GEMM)
+  uint16_t* x_res;     // optional: the launch that completes out also applies the
+                       // stack residual x_res = bf16_rne(x_res + out), bf16 [T][H]
   hipEvent_t ev0, ev1; // optional timing events for the next launch
 };
 
