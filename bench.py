@@ -16,6 +16,10 @@ hidden 2048, MoE intermediate 768):
                layer l+1 while layer l computes
   prefill-bf16 one 2048-token chunk through 48 bf16 layers, K=92, warm
                tables, uniform routing; a step is one chunk
+Modes of the decode workloads: --device runs device-resolved single-wave
+steps (the plan stays on the GPU, a copy kernel pages the misses in, no host
+synchronisation); with stack-int4, --graph also captures one token through
+the 48 layers in a HIP graph and replays it per token.
 Inputs (router logits, hidden states) are resident in HBM before the timed
 region; expert stores live in pinned host memory by design of the method.
 
@@ -205,7 +209,10 @@ def bench_decode(args, torch, dev):
 
     def run(t0, n):
         for t in range(t0, t0 + n):
-            layer.step(plan, lg_d[t], x_d[t], out)
+            if args.device:
+                layer.step_device(plan, lg_d[t], x_d[t], out)
+            else:
+                layer.step(plan, lg_d[t], x_d[t], out)
 
     run(0, args.warmup)
     torch.cuda.synchronize()
@@ -232,8 +239,9 @@ def bench_decode(args, torch, dev):
            "stats": d, "cfg": cfg, "B": B,
            "workload": "one Qwen3-30B-A3B-shaped MoE layer, %s experts, E=%d top_k=%d hidden=%d "
                        "intermediate=%d, K=%d resident slots, decode at batch %d, correlated routing "
-                       "p=%.2f, cold table" % (FMT_NAME[cfg.fmt], cfg.E, cfg.top_k, cfg.H, cfg.I,
-                                              cfg.K, B, cfg.p_keep)}
+                       "p=%.2f, cold table%s" % (FMT_NAME[cfg.fmt], cfg.E, cfg.top_k, cfg.H, cfg.I,
+                                                cfg.K, B, cfg.p_keep,
+                                                ", " + mode_name(args) if args.device else "")}
 
     def cpu(budget):
         from oracle.layer import PagedLayer
@@ -279,7 +287,15 @@ def build_stack(cfg, dev, torch, max_tokens, initial_fill):
     log("built %d layers: %.1f GB pinned, %.1f GB of slots, in %.1f s"
         % (cfg.layers, cfg.layers * cfg.E * rec / 1e9, cfg.layers * cfg.K * rec / 1e9,
            time.perf_counter() - t0))
-    return hosts, layers, plans, pool
+    return hosts, layers, plans, pool, compute
+
+
+def mode_name(args):
+    if args.graph:
+        return "device-resolved steps (kernel page-in) captured in one HIP graph per token"
+    if args.device:
+        return "device-resolved steps (kernel page-in, no host synchronisation)"
+    return "one-layer lookahead" if args.lookahead else "strict layer order"
 
 
 def bench_stack(args, torch, dev):
@@ -288,18 +304,35 @@ def bench_stack(args, torch, dev):
     from workloads import gen
 
     cfg = W.CONFIGS[4]
-    hosts, layers, plans, pool = build_stack(cfg, dev, torch, 1, False)
+    hosts, layers, plans, pool, compute = build_stack(cfg, dev, torch, 1, False)
     total = args.warmup + args.steps
     logits, x0 = gen.stack_inputs(cfg, steps=total, routing=args.routing)
     lg_d = torch.from_numpy(logits).to(dev)             # [steps][L][1][E]
     x0_d = torch.from_numpy(x0.view(np.int16)).to(dev)  # [steps][1][H]
     x = torch.empty(1, cfg.H, dtype=torch.int16, device=dev)
     out = torch.empty(1, cfg.H, dtype=torch.float32, device=dev)
+    lg_buf = torch.empty_like(lg_d[0])                  # fixed input of a captured token
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # one token through the 48 device-resolved layers, captured once and
+        # replayed per token (inputs copied into fixed buffers on the stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=compute):
+            ewp.stack_forward_device(layers, plans, lg_buf, x, out)
+        torch.cuda.synchronize()
 
-    def run(t0, n):
-        for t in range(t0, t0 + n):
-            x.copy_(x0_d[t])
-            ewp.stack_forward(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
+    def run(t0, n, eager=False):
+        with torch.cuda.stream(compute):  # inputs are written on the stream that reads them
+            for t in range(t0, t0 + n):
+                x.copy_(x0_d[t])
+                if graph is not None and not eager:
+                    lg_buf.copy_(lg_d[t])
+                    graph.replay()
+                elif args.device:
+                    ewp.stack_forward_device(layers, plans, lg_d[t], x, out)
+                else:
+                    ewp.stack_forward(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
 
     run(0, args.warmup)
     torch.cuda.synchronize()
@@ -311,10 +344,10 @@ def bench_stack(args, torch, dev):
     s1 = sum_stats(layers)
     for L in layers:
         L.reset()
-    run(0, args.warmup)
+    run(0, args.warmup, eager=True)
     for L in layers:
         L.timing_enable(True)
-    run(args.warmup, args.steps)
+    run(args.warmup, args.steps, eager=True)  # timers need eager launches
     torch.cuda.synchronize()
     tm = merge_timing([L.timing_read() for L in layers])
     floor_us = ewp.timing_floor()
@@ -326,7 +359,7 @@ def bench_stack(args, torch, dev):
                        "experts, E=128 top_k=8 hidden=2048 intermediate=768, K=92 slots per layer, "
                        "batch-1 decode, %s routing%s, %s, cold tables"
                        % ("correlated p=0.75" if args.routing == "correlated" else "uniform",
-                          "", "one-layer lookahead" if args.lookahead else "strict layer order")}
+                          "", mode_name(args))}
 
     def cpu(budget):
         from oracle.layer import PagedLayer
@@ -369,7 +402,7 @@ def bench_prefill(args, torch, dev):
 
     cfg = W.CONFIGS[5]
     T = cfg.tokens
-    hosts, layers, plans, pool = build_stack(cfg, dev, torch, T, True)
+    hosts, layers, plans, pool, compute = build_stack(cfg, dev, torch, T, True)
     total = args.warmup + args.steps
     chunks = [gen.prefill_inputs(cfg, salt=c) for c in range(total)]
     x_d = torch.empty(T, cfg.H, dtype=torch.int16, device=dev)
@@ -378,9 +411,10 @@ def bench_prefill(args, torch, dev):
     x0_d = [torch.from_numpy(c[1].view(np.int16)).to(dev) for c in chunks]
 
     def run(c0, n):
-        for c in range(c0, c0 + n):
-            x_d.copy_(x0_d[c])
-            ewp.stack_forward(layers, plans, lg_d[c], x_d, out, lookahead=args.lookahead)
+        with torch.cuda.stream(compute):  # inputs are written on the stream that reads them
+            for c in range(c0, c0 + n):
+                x_d.copy_(x0_d[c])
+                ewp.stack_forward(layers, plans, lg_d[c], x_d, out, lookahead=args.lookahead)
 
     run(0, args.warmup)
     torch.cuda.synchronize()
@@ -488,6 +522,10 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--routing", default="correlated", choices=["correlated", "uniform"])
     ap.add_argument("--lookahead", action="store_true")
+    ap.add_argument("--device", action="store_true",
+                    help="device-resolved single-wave steps (kernel page-in, no host sync)")
+    ap.add_argument("--graph", action="store_true",
+                    help="stack-int4 only: device-resolved token captured in a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
@@ -498,6 +536,15 @@ def main():
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
         return
+    if args.graph:
+        args.device = True
+        if args.workload != "stack-int4":
+            print("--graph applies to --workload stack-int4", file=sys.stderr)
+            sys.exit(2)
+    if args.device and (args.workload == "prefill-bf16" or args.lookahead):
+        print("--device runs single-wave decode steps: not with prefill-bf16 or --lookahead",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Paged Experts path is single-GPU and this "
               "build has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -519,7 +566,8 @@ def main():
     tm, st, cfg = res["timing"], res["stats"], res["cfg"]
     variant = args.workload + "".join(
         s for s, on in ((" lookahead", args.lookahead), (" uniform", args.routing != "correlated"),
-                        (" batch=%d" % args.batch, args.batch != 1)) if on)
+                        (" batch=%d" % args.batch, args.batch != 1), (" device", args.device and not args.graph),
+                        (" graph", args.graph)) if on)
     pin = tm["page_in"]
     line = {
         "metric": METRIC,

@@ -90,6 +90,11 @@ EXPORTS = {
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_Timing)]),
     "moe_timing_floor": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]),
+    "moe_step_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "moe_stack_forward_device": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                                ctypes.c_void_p, ctypes.c_void_p]),
     "moe_host_alloc": (ctypes.c_void_p, [ctypes.c_size_t]),
     "moe_host_free": (None, [ctypes.c_void_p]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -167,6 +172,7 @@ class Plan:
         h = ctypes.c_void_p()
         _check(lib().moe_plan_create(layer.handle, int(max_tokens), ctypes.byref(h)))
         self.handle, self.layer, self.max_tokens = h, layer, int(max_tokens)
+        self.dev_tokens = None  # token count of the last device-resolved step, if that was the last routing
 
     def close(self):
         if self.handle:
@@ -194,8 +200,9 @@ class Plan:
         return ex, sl, misses
 
     def read(self):
-        i = self.info()
-        n = i["num_tokens"] * self.layer.top_k
+        # after a device-resolved step the host view is stale: use its token count
+        T = self.dev_tokens if self.dev_tokens is not None else self.info()["num_tokens"]
+        n = T * self.layer.top_k
         ids = np.zeros(n, np.int32)
         w = np.zeros(n, np.float32)
         sid = np.zeros(n, np.int32)
@@ -204,7 +211,7 @@ class Plan:
                                    w.ctypes.data_as(ctypes.c_void_p),
                                    sid.ctypes.data_as(ctypes.c_void_p),
                                    wo.ctypes.data_as(ctypes.c_void_p)))
-        shp = (i["num_tokens"], self.layer.top_k)
+        shp = (T, self.layer.top_k)
         return ids.reshape(shp), w.reshape(shp), sid.reshape(shp), wo.reshape(shp)
 
 
@@ -241,6 +248,7 @@ class Layer:
     def route(self, plan, logits, num_tokens=None):
         T = logits.shape[0] if num_tokens is None else num_tokens
         _check(lib().moe_route(self.handle, _ptr(logits), int(T), plan.handle))
+        plan.dev_tokens = None
         return plan.info()
 
     def page_in(self, plan, wave):
@@ -256,6 +264,15 @@ class Layer:
             self.page_in(plan, w)
             self.forward(plan, w, x, out)
         return info
+
+    def step_device(self, plan, logits, x, out, x_res=None, num_tokens=None):
+        """Device-resolved single-wave step (no host synchronisation; capturable
+        in a HIP graph): route, page-in by a copy kernel and expert FFN on the
+        compute stream. Requires num_tokens * top_k <= K."""
+        T = logits.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moe_step_device(self.handle, plan.handle, _ptr(logits), int(T), _ptr(x), _ptr(out),
+                                     _ptr(x_res)))
+        plan.dev_tokens = int(T)
 
     def reset(self):
         _check(lib().moe_layer_reset(self.handle))
@@ -310,6 +327,20 @@ def stack_forward(layers, plans, logits, x, out, lookahead=False):
     pa = (ctypes.c_void_p * n)(*[p.handle.value for p in plans])
     _check(lib().moe_stack_forward(la, pa, n, _ptr(logits), int(logits.shape[1]), _ptr(x), _ptr(out),
                                    int(bool(lookahead))))
+    for p in plans:
+        p.dev_tokens = None
+
+
+def stack_forward_device(layers, plans, logits, x, out):
+    """stack_forward through device-resolved steps: every layer's route,
+    page-in and FFN enqueued on the compute stream with no host wait."""
+    n = len(layers)
+    la = (ctypes.c_void_p * n)(*[l.handle.value for l in layers])
+    pa = (ctypes.c_void_p * n)(*[p.handle.value for p in plans])
+    _check(lib().moe_stack_forward_device(la, pa, n, _ptr(logits), int(logits.shape[1]), _ptr(x),
+                                          _ptr(out)))
+    for p in plans:
+        p.dev_tokens = int(logits.shape[1])
 
 
 def alloc_layer_buffers(num_experts, num_slots, rec_bytes, device="cuda"):

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoepage.so")
-SOURCES = ["plan.hip", "ffn_gemv.hip", "ffn_gemm.hip", "api.hip"]
+SOURCES = ["plan.hip", "page_in.hip", "ffn_gemv.hip", "ffn_gemm.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -5,6 +5,7 @@
 // PCIe Math, and the 4-Request Cliff".
 #include <immintrin.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cstring>
 #include <new>
@@ -47,6 +48,11 @@ struct moe_layer {
   RecLayout rl;
   size_t stride;
   const uint8_t* host_store;
+  const uint8_t* host_store_dev;  // device alias of the host store (null if not mapped)
+  long long* dstats;              // device-resolved steps' counters (steps, refs, activations,
+                                  // hits, misses, waves), device memory
+  bool dev_steps;                 // a device-resolved step has been enqueued
+  bool dev_pending;               // ... and no host-mode route has waited for it yet
   uint8_t* slots;
   uint8_t* state;
   hipStream_t compute, copy, route;
@@ -81,6 +87,8 @@ struct moe_plan {
   bool consumed_recorded;
   moe_plan_info info;
   bool valid;
+  bool dev_routed;    // last routed by a device-resolved step (host view not updated)
+  int dev_tokens;     // its token count
 };
 
 namespace {
@@ -191,7 +199,8 @@ double down_weight_bytes(const moe_layer* L) {
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows, bool combine, uint16_t* x_res = nullptr);
+                   int max_rows, bool combine, uint16_t* x_res = nullptr,
+                   const int32_t* n_dev = nullptr);
 
 moe_status self_check(moe_layer* L);
 
@@ -288,6 +297,13 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
       hipEventCreateWithFlags(&L->ev_copied, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&L->ev_routed, hipEventDisableTiming) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "hipEventCreate failed"));
+  // device alias of the host store, for device-resolved steps (none if unmapped)
+  void* hs_dev = nullptr;
+  if (hipHostGetDevicePointer(&hs_dev, (void*)hs, 0) == hipSuccess) L->host_store_dev = (const uint8_t*)hs_dev;
+  else (void)hipGetLastError();
+  if (hipMalloc((void**)&L->dstats, 8 * sizeof(long long)) != hipSuccess ||
+      hipMemset(L->dstats, 0, 8 * sizeof(long long)) != hipSuccess)
+    return bail(fail(MOE_ERR_HIP, "device counters allocation failed"));
   if (d->self_check) {
     st = self_check(L);
     if (st) return bail(st);
@@ -306,6 +322,7 @@ void moe_layer_destroy(moe_layer* L) {
   if (L->ev_fwd_done) (void)hipEventDestroy(L->ev_fwd_done);
   if (L->ev_copied) (void)hipEventDestroy(L->ev_copied);
   if (L->ev_routed) (void)hipEventDestroy(L->ev_routed);
+  if (L->dstats) (void)hipFree(L->dstats);
 
   for (auto& t : L->pending) {
     (void)hipEventDestroy(t.a);
@@ -419,6 +436,9 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
     return fail(MOE_ERR_STATE, "previous step of this layer has waves not yet forwarded");
 
   if (p->consumed_recorded && rs != L->compute) HIP_TRY(hipStreamWaitEvent(rs, p->ev_consumed, 0));
+  // a device-resolved step of this layer (compute stream) may still update the table state
+  if (L->dev_pending && rs != L->compute) HIP_TRY(hipStreamWaitEvent(rs, L->ev_fwd_done, 0));
+  L->dev_pending = false;
   if (after) HIP_TRY(hipStreamWaitEvent(rs, after, 0));
   TimerRec tr{};
   moe_status st = timer_events(L, &tr);
@@ -461,6 +481,7 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
   p->info.num_misses = h.num_distinct - h.num_hits;
   p->info.num_waves = h.num_waves;
   p->valid = true;
+  p->dev_routed = false;
   if (T > 0) {
     L->stats.steps += 1;
     L->stats.refs += h.num_distinct;
@@ -505,10 +526,10 @@ moe_status moe_plan_get_wave(const moe_plan* p, int32_t w, moe_wave_info* out) {
 moe_status moe_plan_read(const moe_plan* p, int32_t* ids, float* weights, int32_t* slot_ids,
                          int32_t* wave_of) {
   if (!p) return fail(MOE_ERR_INVALID_ARG, "null plan");
-  if (!p->valid) return fail(MOE_ERR_STATE, "plan has not been routed");
+  if (!p->valid && !p->dev_routed) return fail(MOE_ERR_STATE, "plan has not been routed");
   const moe_layer* L = p->layer;
-  HIP_TRY(hipStreamSynchronize(L->route));
-  const size_t n = (size_t)p->info.num_tokens * L->k;
+  HIP_TRY(hipStreamSynchronize(p->dev_routed ? L->compute : L->route));
+  const size_t n = (size_t)(p->dev_routed ? p->dev_tokens : p->info.num_tokens) * L->k;
   if (n == 0) return MOE_OK;
   if (ids) HIP_TRY(hipMemcpy(ids, p->dev.ids, 4 * n, hipMemcpyDeviceToHost));
   if (weights) HIP_TRY(hipMemcpy(weights, p->dev.weights, 4 * n, hipMemcpyDeviceToHost));
@@ -677,9 +698,130 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
   return st;
 }
 
+namespace {
+
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus c = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &c) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return c != hipStreamCaptureStatusNone;
+}
+
+moe_status step_device_check(const moe_layer* L, const moe_plan* p, int32_t T) {
+  if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
+  if (p->layer != L) return fail(MOE_ERR_INVALID_ARG, "plan was created for another layer");
+  if (T < 1 || T > p->max_tokens || T > MOE_MAX_GEMV_TOKENS)
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in 1..min(max_tokens, 64)");
+  if ((int64_t)T * L->k > L->K)
+    return fail(MOE_ERR_INVALID_ARG, "T * top_k exceeds K: the step may need more than one wave");
+  if (!route_small_ok(T, L->k)) return fail(MOE_ERR_INVALID_ARG, "too many pairs for one route launch");
+  if (!L->host_store_dev) return fail(MOE_ERR_STATE, "host store is not mapped into the device");
+  if (L->cur_plan) return fail(MOE_ERR_STATE, "a host-driven step of this layer is unfinished");
+  return MOE_OK;
+}
+
+// Device-resolved single-wave step on the compute stream: route + plan (kept on
+// the device, counters in dstats), kernel page-in of the misses, expert FFN
+// with the expert count read on the device, optional stack residual.
+moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
+                            float* out, uint16_t* x_res) {
+  const hipStream_t cs = L->compute;
+  const bool cap = stream_capturing(cs);
+  const bool timing = L->timing;
+  if (cap) L->timing = false;  // dispatch-stamped events are not captured
+  moe_status st = MOE_OK;
+  do {
+    TimerRec tr{}, tc{};
+    if ((st = timer_events(L, &tr)) || (st = timer_events(L, &tc))) break;
+    if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, nullptr, 0, cs, tr.a, tr.b,
+                                L->dstats) != hipSuccess) {
+      st = fail(MOE_ERR_HIP, "route launch failed");
+      break;
+    }
+    timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
+    if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, p->dev, L->E, L->K, cs, tc.a, tc.b) !=
+        hipSuccess) {
+      st = fail(MOE_ERR_HIP, "page-in launch failed");
+      break;
+    }
+    // bytes are not known on the host here; moe_layer_stats has the misses
+    timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
+    // at most min(T * top_k, E) experts; exactly top_k for one token
+    const int n_max = std::min(T * L->k, L->E);
+    st = run_ffn(L, p->dev, p->h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr,
+                 nullptr, 0, T, false, x_res, p->dev.counts);
+  } while (0);
+  L->timing = timing;
+  if (st) return st;
+  if (!cap) {  // ordering for later host-driven calls on other streams
+    HIP_TRY(hipEventRecord(L->ev_fwd_done, cs));
+    L->fwd_recorded = true;
+    HIP_TRY(hipEventRecord(p->ev_consumed, cs));
+    p->consumed_recorded = true;
+  }
+  L->dev_steps = true;
+  L->dev_pending = true;
+  p->valid = false;
+  p->dev_routed = true;
+  p->dev_tokens = T;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_step_device(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
+                           float* out, void* x_res) {
+  moe_status st = step_device_check(L, p, T);
+  if (st) return st;
+  if (!logits || !x || !out) return fail(MOE_ERR_INVALID_ARG, "null logits, x or out");
+  if (((uintptr_t)x & 15) || ((uintptr_t)out & 15) || ((uintptr_t)x_res & 7))
+    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned, x_res 8-byte aligned");
+  if (x_res && L->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
+  return step_device_impl(L, p, logits, T, x, out, (uint16_t*)x_res);
+}
+
+moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans, int32_t n,
+                                    const float* logits, int32_t T, void* x, float* out) {
+  if (!layers || !plans || n < 1) return fail(MOE_ERR_INVALID_ARG, "need n_layers >= 1 layers and plans");
+  if (!logits || !x || !out) return fail(MOE_ERR_INVALID_ARG, "bad buffers");
+  if (((uintptr_t)x & 15) || ((uintptr_t)out & 15))
+    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  const moe_layer* L0 = layers[0];
+  if (!L0) return fail(MOE_ERR_INVALID_ARG, "null layer");
+  for (int l = 0; l < n; ++l) {
+    const moe_layer* L = layers[l];
+    moe_status st = step_device_check(L, plans[l], T);
+    if (st) return fail(st, "layer " + std::to_string(l) + ": " + g_err);
+    if (L->E != L0->E || L->k != L0->k || L->H != L0->H || L->fmt != L0->fmt ||
+        L->compute != L0->compute)
+      return fail(MOE_ERR_INVALID_ARG, "stack layers must share E, top_k, H, format and compute stream");
+  }
+  if (L0->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
+  const size_t lstride = (size_t)T * L0->E;
+  for (int l = 0; l < n; ++l) {
+    moe_status st = step_device_impl(layers[l], plans[l], logits + l * lstride, T, x, out, (uint16_t*)x);
+    if (st) return st;
+  }
+  return MOE_OK;
+}
+
 moe_status moe_layer_stats(const moe_layer* L, moe_stats* out) {
   if (!L || !out) return fail(MOE_ERR_INVALID_ARG, "null layer or output");
   *out = L->stats;
+  if (L->dev_steps) {  // add the device-resolved steps' counters
+    long long d[8];
+    HIP_TRY(hipStreamSynchronize(L->compute));
+    HIP_TRY(hipMemcpy(d, L->dstats, sizeof(d), hipMemcpyDeviceToHost));
+    out->steps += d[0];
+    out->refs += d[1];
+    out->activations += d[2];
+    out->hits += d[3];
+    out->misses += d[4];
+    out->waves += d[5];
+    out->bytes_paged += d[4] * (int64_t)L->stride;
+  }
   return MOE_OK;
 }
 
@@ -759,8 +901,9 @@ namespace {
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows, bool combine, uint16_t* x_res) {
+                   int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev) {
   FfnArgs a{};
+  a.n_dev = n_dev;
   a.fmt = L->fmt;
   a.E = L->E;
   a.k = L->k;

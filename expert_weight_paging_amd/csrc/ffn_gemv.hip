@@ -174,6 +174,7 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
   const int H = a.H, I = a.I;
   const int i0 = (blockIdx.x * 4 + wid) * RPW;
   if (i0 >= I) return;
+  if (a.n_dev && (int)blockIdx.y >= *a.n_dev) return;  // device-resolved count: uniform per block
   const int o = a.o_lo + blockIdx.y;
   const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
   const RecLayout L = rec_layout(F, H, I);
@@ -357,9 +358,10 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
       }
     }
   };
-  if (wid < a.n_exp) load_expert(wid, cur);
-  for (int e = wid; e < a.n_exp; e += 8) {
-    if (e + 8 < a.n_exp) load_expert(e + 8, nxt);
+  const int n_exp = a.n_dev ? min(a.n_exp, *a.n_dev) : a.n_exp;
+  if (wid < n_exp) load_expert(wid, cur);
+  for (int e = wid; e < n_exp; e += 8) {
+    if (e + 8 < n_exp) load_expert(e + 8, nxt);
     const int o = a.o_lo + e;
     const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
     float sc[RW][NJ], zc[RW][NJ];
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
         if (lane == t) acc[r] = fmaf(wq, y, acc[r]);
       }
     }
-    if (e + 8 < a.n_exp) {
+    if (e + 8 < n_exp) {
 #pragma unroll
       for (int r = 0; r < RW; ++r)
 #pragma unroll

@@ -124,7 +124,13 @@ hipError_t launch_group(const int32_t* ids, int T, int k, int E, PlanDev dev, hi
 bool route_small_ok(int T, int k);
 hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
                                    PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s,
-                                   hipEvent_t ev0, hipEvent_t ev1);
+                                   hipEvent_t ev0, hipEvent_t ev1, long long* dstats = nullptr);
+// Device-resolved page-in of a single-wave plan: copies the records of wave
+// order positions [counts[1], counts[0]) (the misses) from the device-mapped
+// host store into their slots.
+hipError_t launch_page_in_device(const uint8_t* host_store_dev, uint8_t* slots, size_t stride,
+                                 const PlanDev& dev, int E, int K, hipStream_t s, hipEvent_t ev0,
+                                 hipEvent_t ev1);
 
 struct FfnArgs {
   int fmt, E, k, H, I, K;
@@ -144,6 +150,8 @@ struct FfnArgs {
   uint16_t* hb_lo;     // GEMM scratch bf16 [T*k][I], low part of h
   float* y;            // GEMM scratch fp32 [T*k][H]
   int max_rows;        // upper bound on pairs of one expert in this wave (GEMM)
+  const int32_t* n_dev; // optional (device-resolved steps): the number of experts,
+                       // read on the device; n_exp is then only an upper bound
   uint16_t* x_res;     // optional: the launch that completes out also applies the
                        // stack residual x_res = bf16_rne(x_res + out), bf16 [T][H]
   hipEvent_t ev0, ev1; // optional timing events for the next launch

@@ -297,9 +297,10 @@ __device__ void plan_body(const int32_t* ids, int P, int T, int E, int K, uint8_
 
 // Publish the plan to pinned host memory: wavefront 0 writes the wave order
 // and the header, makes its writes visible at system scope, then stores seq.
+// Device-resolved steps pass no header: their plan stays on the device.
 __device__ void publish(const PlanSmem& sm, int E, int T, int P, int D, int nH, int n_waves,
                         PlanHdr* hdr, int32_t seq) {
-  if (threadIdx.x >= kWave) return;
+  if (!hdr || threadIdx.x >= kWave) return;
   int32_t* h_order_e = (int32_t*)(hdr + 1);
   int32_t* h_order_s = h_order_e + E;
   int32_t* h_pair_off = h_order_s + E;
@@ -334,11 +335,14 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ id
 // grouping in one workgroup, one launch.
 constexpr int kSmallPairs = 2048;
 
+// dstats, if given (device-resolved steps), accumulates the step counters on
+// the device: steps, distinct experts, activations, hits, misses, waves.
 template <int NT, int NJ>
 __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __restrict__ logits, int T,
                                                               int E, int k, int K, uint8_t* state,
                                                               StateLayout sl, PlanDev dev,
-                                                              PlanHdr* hdr, int32_t seq) {
+                                                              PlanHdr* hdr, int32_t seq,
+                                                              long long* dstats) {
   constexpr int NWV = NT / kWave;
   __shared__ PlanSmem sm;
   __shared__ int32_t s_ids[kSmallPairs];
@@ -380,6 +384,14 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
       }
       running += __popcll(mask);
     }
+  }
+  if (dstats && threadIdx.x == 0 && T > 0) {
+    dstats[0] += 1;
+    dstats[1] += D;
+    dstats[2] += P;
+    dstats[3] += nH;
+    dstats[4] += D - nH;
+    dstats[5] += nw;
   }
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
@@ -482,12 +494,12 @@ bool route_small_ok(int T, int k) { return T <= MOE_MAX_GEMV_TOKENS && T * k <= 
 
 hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
                                    PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s,
-                                   hipEvent_t ev0, hipEvent_t ev1) {
+                                   hipEvent_t ev0, hipEvent_t ev1, long long* dstats) {
   const StateLayout sl = state_layout(E, K);
   uint8_t* st = (uint8_t*)state;
 #define MOE_SMALL(NT, NJ)                                                                   \
   launch_k(route_plan_small_kernel<NT, NJ>, dim3(1), dim3(NT), s, ev0, ev1, logits, T, E, k, K, st, \
-           sl, dev, host_hdr_dev, seq)
+           sl, dev, host_hdr_dev, seq, dstats)
   if (E <= 64) MOE_SMALL(256, 1);
   else if (E <= 128) MOE_SMALL(256, 2);
   else if (E <= 256) MOE_SMALL(256, 4);

@@ -227,6 +227,43 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
                              const float* logits, int32_t num_tokens, void* x, float* out,
                              int32_t lookahead);
 
+/* Device-resolved step: the graph-capturable single-wave path ([PE] "What
+ * happens with more than one request?": a step whose experts fit in the slots
+ * is one wave, the case a graph can capture). Routes the T tokens, plans the
+ * step, pages the misses in and runs the experts, all on the layer's compute
+ * stream, with the plan kept on the device: the miss list is read by a copy
+ * kernel from device memory and the records are read from the host store
+ * through its device mapping, so there is no host synchronisation and no
+ * allocation, and the call may be captured in a HIP graph (timers are skipped
+ * while the stream captures).
+ *   logits: device float32 [T][E]; x: device bf16 [T][H] (fp32 for the f32
+ *           format); out: device float32 [T][H], overwritten (16-byte aligned)
+ *   x_res:  NULL, or device bf16 [T][H] that receives bf16_rne(x_res + out)
+ *           (the stack residual; may alias x)
+ * Requirements: 1 <= T <= min(max_tokens, MOE_MAX_GEMV_TOKENS) and
+ * T * top_k <= K, so the step is always one wave; a host store that is mapped
+ * into the device (moe_host_alloc memory is); no unfinished host-driven step
+ * of the layer. Results (plan arrays, table state, out) are the same as a
+ * host-driven step; the plan's host view is not updated (moe_plan_get_info
+ * and moe_plan_get_wave return MOE_ERR_STATE until the next moe_route;
+ * moe_plan_read reads the device arrays), and the layer counters of these
+ * steps are kept on the device and added by moe_layer_stats. Errors:
+ * MOE_ERR_INVALID_ARG (sizes, pointers, alignment), MOE_ERR_STATE (unmapped
+ * store, unfinished host step), MOE_ERR_FORMAT (x_res on an f32 layer),
+ * MOE_ERR_HIP. */
+moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits,
+                           int32_t num_tokens, const void* x, float* out, void* x_res);
+
+/* moe_stack_forward through device-resolved steps: for each layer l,
+ * moe_step_device(layer l, plan l, logits[l], T, x, out, x_res = x), all on
+ * the shared compute stream, with no host synchronisation (capturable). Same
+ * requirements per layer as moe_step_device; logits device float32
+ * [n_layers][T][E]; x bf16 [T][H] updated in place; out float32 [T][H] holds
+ * the last layer's MoE output. */
+moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans,
+                                    int32_t n_layers, const float* logits, int32_t num_tokens,
+                                    void* x, float* out);
+
 typedef struct moe_stats {
   int64_t steps;        /* moe_route calls with T > 0                          */
   int64_t refs;         /* sum of distinct experts per step                    */

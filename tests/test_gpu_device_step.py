@@ -1,0 +1,239 @@
+"""GPU parity of the device-resolved single-wave path (moe_step_device and
+moe_stack_forward_device: route, slot plan, kernel page-in and FFN with no host
+synchronisation) against the oracle, its interleaving with host-driven steps,
+and its HIP-graph capture against eager runs, all through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_paging_amd as ewp
+import workloads as W
+from oracle.layer import PagedLayer, bf16_rne
+from workloads import gen
+
+from gpu_harness import TOL, PairedLayer, rel_err, say, x_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(cfg, B, K=None, **kw):
+    K = cfg.K if K is None else K
+    return PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt,
+                       lambda a: gen.expert_store(cfg, out=a), max_tokens=B, **kw)
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def _check_device_plan(p, ids_ref, w_ref, p_ref):
+    assert p_ref.n_waves == 1
+    ids, wts, sid, wof = p.plan.read()
+    assert np.array_equal(ids, ids_ref), (ids, ids_ref)
+    assert np.array_equal(sid, p_ref.slot_ids)
+    assert np.array_equal(wof, p_ref.wave_of)
+    assert np.allclose(wts, w_ref, rtol=2e-6, atol=1e-7)
+
+
+def _run_device(p, logits, x, sample, host_every=0):
+    """Device-resolved steps (every host_every-th one host-driven instead);
+    returns the worst output error and the oracle's hit and miss totals."""
+    steps, B = logits.shape[0], logits.shape[1]
+    lg, xd = _dev(logits), _dev(x)
+    out = torch.empty(B, p.H, dtype=torch.float32, device="cuda")
+    worst, hits, misses = 0.0, 0, 0
+    for t in range(steps):
+        comp = bool(sample(t))
+        host = host_every and t % host_every == host_every - 1
+        if host:
+            info = p.gpu.route(p.plan, lg[t])
+            for w in range(info["num_waves"]):
+                p.gpu.page_in(p.plan, w)
+                p.gpu.forward(p.plan, w, xd[t], out)
+        else:
+            p.gpu.step_device(p.plan, lg[t], xd[t], out)
+        o_ref, ids_ref, w_ref, p_ref = p.ref.step(logits[t], x_values(x[t], p.fmt), compute=comp)
+        hits += len(p_ref.hits)
+        misses += len(p_ref.missed)
+        if host:
+            p.check_plan(ids_ref, w_ref, p_ref, B)
+        else:
+            _check_device_plan(p, ids_ref, w_ref, p_ref)
+            with pytest.raises(ewp.MoeError):
+                p.plan.info()  # the host view is not updated by a device step
+        if comp:
+            torch.cuda.synchronize()
+            e = rel_err(out.cpu().numpy(), o_ref)
+            worst = max(worst, e)
+            assert e <= TOL[p.fmt], (t, e)
+        if (t + 1) % 8 == 0:
+            p.check_state()
+    torch.cuda.synchronize()
+    p.check_state()
+    return worst, hits, misses
+
+
+def test_tiny_f32_device_steps():
+    cfg = W.CONFIGS[1]
+    say("case: device steps, tiny f32 E=8 k=2 K=4, 16 steps")
+    p = _layer(cfg, 1)
+    logits, x = gen.decode_inputs(cfg, 1)
+    worst, hits, misses = _run_device(p, logits, x, sample=lambda t: True)
+    st = p.gpu.stats()
+    say("worst rel err %.3g stats %s" % (worst, st))
+    assert st["steps"] == 16 and st["hits"] == hits and st["misses"] == misses
+    assert st["bytes_paged"] == misses * ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
+    p.close()
+
+
+def test_bf16_device_steps():
+    cfg = W.CONFIGS[2]
+    say("case: device steps, bf16 layer K=40, 64 steps at batch 1")
+    p = _layer(cfg, 1)
+    logits, x = gen.decode_inputs(cfg, 1, steps=64)
+    worst, hits, misses = _run_device(p, logits, x, sample=lambda t: t % 8 == 0 or t == 63)
+    st = p.gpu.stats()
+    say("worst rel err %.3g hits %d misses %d" % (worst, hits, misses))
+    assert st["hits"] == hits and st["misses"] == misses and st["waves"] == 64
+    p.close()
+
+
+@pytest.mark.parametrize("B", [1, 2, 5])
+def test_fp8_device_steps(B):
+    cfg = W.CONFIGS[3]
+    say("case: device steps, fp8 layer K=40, B=%d, 24 steps" % B)
+    p = _layer(cfg, B)
+    logits, x = gen.decode_inputs(cfg, B, steps=24)
+    worst, _, _ = _run_device(p, logits, x, sample=lambda t: t % 4 == 0 or t == 23)
+    say("worst rel err %.3g" % worst)
+    p.close()
+
+
+def test_int4_device_steps_interleaved_with_host_steps():
+    cfg = W.CONFIGS[4]
+    say("case: int4 layer K=92, 40 steps, every third one host-driven")
+    p = _layer(cfg, 1)
+    logits, x = gen.decode_inputs(cfg, 1, steps=40)
+    worst, hits, misses = _run_device(p, logits, x, sample=lambda t: t % 4 == 0 or t == 39, host_every=3)
+    st = p.gpu.stats()
+    say("worst rel err %.3g stats %s" % (worst, st))
+    assert st["steps"] == 40 and st["hits"] == hits and st["misses"] == misses
+    p.close()
+
+
+def test_device_step_rejects_multi_wave_batches():
+    cfg = W.CONFIGS[3]
+    say("case: device step with B * top_k > K is rejected")
+    p = _layer(cfg, 6)
+    logits, x = gen.decode_inputs(cfg, 6, steps=1)
+    out = torch.empty(6, cfg.H, dtype=torch.float32, device="cuda")
+    with pytest.raises(ewp.MoeError) as ei:
+        p.gpu.step_device(p.plan, _dev(logits[0]), _dev(x[0]), out)
+    assert ei.value.status == -1  # MOE_ERR_INVALID_ARG
+    p.close()
+
+
+def test_int4_stack_device():
+    cfg = W.CONFIGS[4]
+    n_layers, steps = 4, 12
+    say("case: int4 stack %d layers x %d tokens, device-resolved" % (n_layers, steps))
+    rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
+    pool = gen.pool_records(cfg)
+    s = torch.cuda.Stream()
+    hosts, layers, plans, refs = [], [], [], []
+    for l in range(n_layers):
+        h = ewp.HostStore(cfg.E, rec)
+        gen.fill_layer_store(cfg, l, h.array, pool)
+        slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, "cuda")
+        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, h, slots, state, s, s, s)
+        hosts.append(h)
+        layers.append(L)
+        plans.append(ewp.Plan(L, 1))
+        refs.append(PagedLayer(h.array, cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K))
+    rng = np.random.default_rng(5)
+    worst_hidden = 0.0
+    for step in range(steps):
+        sets = np.stack([np.sort(rng.choice(cfg.E, cfg.top_k, replace=False))[None] for _ in range(n_layers)])
+        logits = gen.logits_from_sets(rng, sets, cfg.E)                      # [L][1][E]
+        x0 = gen.f32_to_bf16_bits(rng.standard_normal((1, cfg.H)).astype(np.float32))
+        x = _dev(x0)
+        out = torch.empty(1, cfg.H, dtype=torch.float32, device="cuda")
+        lg = _dev(logits)
+        torch.cuda.synchronize()  # inputs are in place before the stack's stream reads them
+        ewp.stack_forward_device(layers, plans, lg, x, out)
+        torch.cuda.synchronize()
+        xv = x_values(x0, cfg.fmt)
+        for l in range(n_layers):
+            o, ids_ref, w_ref, p_ref = refs[l].step(logits[l], xv)
+            ids, _, sid, _ = plans[l].read()
+            assert np.array_equal(ids, ids_ref) and np.array_equal(sid, p_ref.slot_ids)
+            se, _, st, clk = layers[l].get_state()
+            rse, _, rst, rclk = refs[l].table.state()
+            assert np.array_equal(se, rse) and np.array_equal(st, rst) and clk == rclk
+            if l == n_layers - 1:
+                assert rel_err(out.cpu().numpy(), o) <= TOL[cfg.fmt]
+            xv = bf16_rne(xv + o)
+        got = gen.bf16_bits_to_f32(x.cpu().numpy().view(np.uint16)).astype(np.float64)
+        bound = TOL[cfg.fmt] * np.sqrt(np.mean(o ** 2)) + n_layers * np.exp2(
+            np.floor(np.log2(np.maximum(np.abs(xv), 2.0 ** -126))) - 7)
+        worst_hidden = max(worst_hidden, float((np.abs(got - xv) / bound).max()))
+        assert np.all(np.abs(got - xv) <= bound)
+    say("worst hidden/bound %.3g" % worst_hidden)
+    for p in plans:
+        p.close()
+    for L in layers:
+        L.close()
+    for h in hosts:
+        h.free()
+
+
+def test_bf16_device_step_graph_replays_match_eager():
+    """One device-resolved step captured in a HIP graph, replayed for 10
+    decode steps with eager input copies and synchronisations between the
+    replays; every replay's output, plan and table state must equal an eager
+    twin layer's bit for bit."""
+    cfg = W.CONFIGS[2]
+    steps = 10
+    say("case: bf16 device step captured in a graph, %d replays vs eager" % steps)
+    rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
+    host = ewp.HostStore(cfg.E, rec)
+    gen.expert_store(cfg, out=host.array)
+    s_eager, s_cap = torch.cuda.Stream(), torch.cuda.Stream()
+    mk = []
+    for s in (s_eager, s_cap):
+        slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, "cuda")
+        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, host, slots, state, s, s, s)
+        mk.append((L, ewp.Plan(L, 1), slots, state))
+    (La, Pa, _, _), (Lb, Pb, _, _) = mk
+    logits, x = gen.decode_inputs(cfg, 1, steps=steps)
+    lg, xd = _dev(logits), _dev(x)
+    lg_buf = torch.zeros(1, cfg.E, dtype=torch.float32, device="cuda")
+    x_buf = torch.zeros(1, cfg.H, dtype=torch.int16, device="cuda")
+    out_b = torch.zeros(1, cfg.H, dtype=torch.float32, device="cuda")
+    out_a = torch.zeros(1, cfg.H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s_cap):
+        Lb.step_device(Pb, lg_buf, x_buf, out_b)
+    torch.cuda.synchronize()
+    for t in range(steps):
+        lg_buf.copy_(lg[t])
+        x_buf.copy_(xd[t])
+        g.replay()
+        with torch.cuda.stream(s_eager):
+            La.step_device(Pa, lg[t], xd[t], out_a)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), t
+        ra, rb = Pa.read(), Pb.read()
+        for u, v in zip(ra, rb):
+            assert np.array_equal(u, v), t
+        for u, v in zip(La.get_state(), Lb.get_state()):
+            assert np.array_equal(np.asarray(u), np.asarray(v)), t
+    assert La.stats() == Lb.stats()
+    say("replays equal eager; stats %s" % Lb.stats())
+    del g
+    for L, P, _, _ in mk:
+        P.close()
+        L.close()
+    host.free()
