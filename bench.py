@@ -291,10 +291,11 @@ def build_stack(cfg, dev, torch, max_tokens, initial_fill):
 
 
 def mode_name(args):
+    la = ", routes and copies ahead on the copy stream (lookahead)" if args.lookahead else ""
     if args.graph:
-        return "device-resolved steps (kernel page-in) captured in one HIP graph per token"
+        return "device-resolved steps (kernel page-in) captured in one HIP graph per token" + la
     if args.device:
-        return "device-resolved steps (kernel page-in, no host synchronisation)"
+        return "device-resolved steps (kernel page-in, no host synchronisation)" + la
     return "one-layer lookahead" if args.lookahead else "strict layer order"
 
 
@@ -319,7 +320,7 @@ def bench_stack(args, torch, dev):
         # replayed per token (inputs copied into fixed buffers on the stream)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=compute):
-            ewp.stack_forward_device(layers, plans, lg_buf, x, out)
+            ewp.stack_forward_device(layers, plans, lg_buf, x, out, lookahead=args.lookahead)
         torch.cuda.synchronize()
 
     def run(t0, n, eager=False):
@@ -330,7 +331,7 @@ def bench_stack(args, torch, dev):
                     lg_buf.copy_(lg_d[t])
                     graph.replay()
                 elif args.device:
-                    ewp.stack_forward_device(layers, plans, lg_d[t], x, out)
+                    ewp.stack_forward_device(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
                 else:
                     ewp.stack_forward(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
 
@@ -541,9 +542,10 @@ def main():
         if args.workload != "stack-int4":
             print("--graph applies to --workload stack-int4", file=sys.stderr)
             sys.exit(2)
-    if args.device and (args.workload == "prefill-bf16" or args.lookahead):
-        print("--device runs single-wave decode steps: not with prefill-bf16 or --lookahead",
-              file=sys.stderr)
+    if args.device and (args.workload == "prefill-bf16" or
+                        (args.lookahead and args.workload != "stack-int4")):
+        print("--device runs single-wave decode steps: not with prefill-bf16; --lookahead only "
+              "with stack-int4", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Paged Experts path is single-GPU and this "

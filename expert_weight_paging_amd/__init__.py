@@ -94,7 +94,7 @@ EXPORTS = {
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "moe_stack_forward_device": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
-                                                ctypes.c_void_p, ctypes.c_void_p]),
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
     "moe_host_alloc": (ctypes.c_void_p, [ctypes.c_size_t]),
     "moe_host_free": (None, [ctypes.c_void_p]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -331,14 +331,15 @@ def stack_forward(layers, plans, logits, x, out, lookahead=False):
         p.dev_tokens = None
 
 
-def stack_forward_device(layers, plans, logits, x, out):
+def stack_forward_device(layers, plans, logits, x, out, lookahead=False):
     """stack_forward through device-resolved steps: every layer's route,
-    page-in and FFN enqueued on the compute stream with no host wait."""
+    page-in and FFN enqueued with no host wait (lookahead: routes and copies
+    on the shared copy stream, FFNs on the compute stream)."""
     n = len(layers)
     la = (ctypes.c_void_p * n)(*[l.handle.value for l in layers])
     pa = (ctypes.c_void_p * n)(*[p.handle.value for p in plans])
     _check(lib().moe_stack_forward_device(la, pa, n, _ptr(logits), int(logits.shape[1]), _ptr(x),
-                                          _ptr(out)))
+                                          _ptr(out), int(bool(lookahead))))
     for p in plans:
         p.dev_tokens = int(logits.shape[1])
 

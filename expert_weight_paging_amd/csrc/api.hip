@@ -722,32 +722,39 @@ moe_status step_device_check(const moe_layer* L, const moe_plan* p, int32_t T) {
   return MOE_OK;
 }
 
-// Device-resolved single-wave step on the compute stream: route + plan (kept on
-// the device, counters in dstats), kernel page-in of the misses, expert FFN
-// with the expert count read on the device, optional stack residual.
+// Device-resolved single-wave step: route + plan (kept on the device,
+// counters in dstats) and the kernel page-in of the misses on stream `ps`,
+// then the expert FFN (expert count read on the device) and the optional stack
+// residual on the compute stream. With ps != compute the host records
+// L->ev_copied on ps and the compute stream waits for it (under capture the
+// pair becomes a graph dependency).
 moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
-                            float* out, uint16_t* x_res) {
+                            float* out, uint16_t* x_res, hipStream_t ps, bool cap) {
   const hipStream_t cs = L->compute;
-  const bool cap = stream_capturing(cs);
   const bool timing = L->timing;
   if (cap) L->timing = false;  // dispatch-stamped events are not captured
   moe_status st = MOE_OK;
   do {
     TimerRec tr{}, tc{};
     if ((st = timer_events(L, &tr)) || (st = timer_events(L, &tc))) break;
-    if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, nullptr, 0, cs, tr.a, tr.b,
+    if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, nullptr, 0, ps, tr.a, tr.b,
                                 L->dstats) != hipSuccess) {
       st = fail(MOE_ERR_HIP, "route launch failed");
       break;
     }
     timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
-    if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, p->dev, L->E, L->K, cs, tc.a, tc.b) !=
+    if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, p->dev, L->E, L->K, ps, tc.a, tc.b) !=
         hipSuccess) {
       st = fail(MOE_ERR_HIP, "page-in launch failed");
       break;
     }
     // bytes are not known on the host here; moe_layer_stats has the misses
     timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
+    if (ps != cs && (hipEventRecord(L->ev_copied, ps) != hipSuccess ||
+                     hipStreamWaitEvent(cs, L->ev_copied, 0) != hipSuccess)) {
+      st = fail(MOE_ERR_HIP, "hand-over from the copy stream failed");
+      break;
+    }
     // at most min(T * top_k, E) experts; exactly top_k for one token
     const int n_max = std::min(T * L->k, L->E);
     st = run_ffn(L, p->dev, p->h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr,
@@ -779,11 +786,13 @@ moe_status moe_step_device(moe_layer* L, moe_plan* p, const float* logits, int32
   if (((uintptr_t)x & 15) || ((uintptr_t)out & 15) || ((uintptr_t)x_res & 7))
     return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned, x_res 8-byte aligned");
   if (x_res && L->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
-  return step_device_impl(L, p, logits, T, x, out, (uint16_t*)x_res);
+  return step_device_impl(L, p, logits, T, x, out, (uint16_t*)x_res, L->compute,
+                          stream_capturing(L->compute));
 }
 
 moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans, int32_t n,
-                                    const float* logits, int32_t T, void* x, float* out) {
+                                    const float* logits, int32_t T, void* x, float* out,
+                                    int32_t lookahead) {
   if (!layers || !plans || n < 1) return fail(MOE_ERR_INVALID_ARG, "need n_layers >= 1 layers and plans");
   if (!logits || !x || !out) return fail(MOE_ERR_INVALID_ARG, "bad buffers");
   if (((uintptr_t)x & 15) || ((uintptr_t)out & 15))
@@ -797,11 +806,31 @@ moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* p
     if (L->E != L0->E || L->k != L0->k || L->H != L0->H || L->fmt != L0->fmt ||
         L->compute != L0->compute)
       return fail(MOE_ERR_INVALID_ARG, "stack layers must share E, top_k, H, format and compute stream");
+    if (lookahead && L->copy != L0->copy)
+      return fail(MOE_ERR_INVALID_ARG, "lookahead needs one copy stream shared by the stack's layers");
   }
   if (L0->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
+  if (lookahead && L0->copy == L0->compute)
+    return fail(MOE_ERR_INVALID_ARG, "lookahead needs a copy stream distinct from the compute stream");
   const size_t lstride = (size_t)T * L0->E;
+  const hipStream_t cs = L0->compute;
+  const bool cap = stream_capturing(cs);
+  // Lookahead: routes and copies of every layer run in order on the copy
+  // stream, each layer's FFN on the compute stream after its copies, so
+  // layer l+1's copies overlap layer l's math. The copy stream first waits
+  // for the compute stream's earlier work (the previous token's FFNs still
+  // read plans and slots that these copies rewrite; it is also the fork
+  // point of a capture).
+  hipStream_t ps = cs;
+  if (lookahead) {
+    ps = L0->copy;
+    if (hipEventRecord(layers[0]->ev_routed, cs) != hipSuccess ||
+        hipStreamWaitEvent(ps, layers[0]->ev_routed, 0) != hipSuccess)
+      return fail(MOE_ERR_HIP, "fork to the copy stream failed");
+  }
   for (int l = 0; l < n; ++l) {
-    moe_status st = step_device_impl(layers[l], plans[l], logits + l * lstride, T, x, out, (uint16_t*)x);
+    moe_status st = step_device_impl(layers[l], plans[l], logits + l * lstride, T, x, out, (uint16_t*)x, ps,
+                                     cap);
     if (st) return st;
   }
   return MOE_OK;

@@ -255,14 +255,21 @@ moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits
                            int32_t num_tokens, const void* x, float* out, void* x_res);
 
 /* moe_stack_forward through device-resolved steps: for each layer l,
- * moe_step_device(layer l, plan l, logits[l], T, x, out, x_res = x), all on
- * the shared compute stream, with no host synchronisation (capturable). Same
- * requirements per layer as moe_step_device; logits device float32
- * [n_layers][T][E]; x bf16 [T][H] updated in place; out float32 [T][H] holds
- * the last layer's MoE output. */
+ * moe_step_device(layer l, plan l, logits[l], T, x, out, x_res = x), with no
+ * host synchronisation (capturable). Same requirements per layer as
+ * moe_step_device; logits device float32 [n_layers][T][E]; x bf16 [T][H]
+ * updated in place; out float32 [T][H] holds the last layer's MoE output.
+ *   lookahead: 0 = everything on the shared compute stream, layer after
+ *              layer; 1 = the route and page-in kernels of all layers run in
+ *              layer order on the copy stream (shared by the layers and
+ *              distinct from the compute stream) and each layer's FFN waits
+ *              for its own copies only, so layer l+1's copies overlap layer
+ *              l's math. Like moe_stack_forward's lookahead this is valid only
+ *              when the router logits do not depend on the previous layer's
+ *              output (given in advance), the caller's promise. */
 moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans,
                                     int32_t n_layers, const float* logits, int32_t num_tokens,
-                                    void* x, float* out);
+                                    void* x, float* out, int32_t lookahead);
 
 typedef struct moe_stats {
   int64_t steps;        /* moe_route calls with T > 0                          */

@@ -42,6 +42,7 @@ def _run_device(p, logits, x, sample, host_every=0):
     steps, B = logits.shape[0], logits.shape[1]
     lg, xd = _dev(logits), _dev(x)
     out = torch.empty(B, p.H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()  # inputs in place before the layer's streams read them
     worst, hits, misses = 0.0, 0, 0
     for t in range(steps):
         comp = bool(sample(t))
@@ -87,10 +88,15 @@ def test_tiny_f32_device_steps():
     p.close()
 
 
-def test_bf16_device_steps():
+@pytest.mark.parametrize("split", [False, True])
+def test_bf16_device_steps(split):
     cfg = W.CONFIGS[2]
-    say("case: device steps, bf16 layer K=40, 64 steps at batch 1")
-    p = _layer(cfg, 1)
+    say("case: device steps, bf16 layer K=40, 64 steps at batch 1, own copy stream=%s" % split)
+    streams = None
+    if split:  # a layer with a copy stream of its own: device steps stay on the compute stream
+        c = torch.cuda.Stream()
+        streams = (c, torch.cuda.Stream(), c)
+    p = _layer(cfg, 1, streams=streams)
     logits, x = gen.decode_inputs(cfg, 1, steps=64)
     worst, hits, misses = _run_device(p, logits, x, sample=lambda t: t % 8 == 0 or t == 63)
     st = p.gpu.stats()
@@ -134,23 +140,38 @@ def test_device_step_rejects_multi_wave_batches():
     p.close()
 
 
-def test_int4_stack_device():
-    cfg = W.CONFIGS[4]
-    n_layers, steps = 4, 12
-    say("case: int4 stack %d layers x %d tokens, device-resolved" % (n_layers, steps))
+def _int4_stack(cfg, n_layers, s, c):
     rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
     pool = gen.pool_records(cfg)
-    s = torch.cuda.Stream()
     hosts, layers, plans, refs = [], [], [], []
     for l in range(n_layers):
         h = ewp.HostStore(cfg.E, rec)
         gen.fill_layer_store(cfg, l, h.array, pool)
         slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, "cuda")
-        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, h, slots, state, s, s, s)
+        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, h, slots, state, s, c, s)
         hosts.append(h)
         layers.append(L)
         plans.append(ewp.Plan(L, 1))
         refs.append(PagedLayer(h.array, cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K))
+    return hosts, layers, plans, refs
+
+
+def _close_stack(hosts, layers, plans):
+    for p in plans:
+        p.close()
+    for L in layers:
+        L.close()
+    for h in hosts:
+        h.free()
+
+
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_int4_stack_device(lookahead):
+    cfg = W.CONFIGS[4]
+    n_layers, steps = 4, 12
+    say("case: int4 stack %d layers x %d tokens, device-resolved, lookahead=%s" % (n_layers, steps, lookahead))
+    s, c = torch.cuda.Stream(), torch.cuda.Stream()
+    hosts, layers, plans, refs = _int4_stack(cfg, n_layers, s, c)
     rng = np.random.default_rng(5)
     worst_hidden = 0.0
     for step in range(steps):
@@ -161,7 +182,7 @@ def test_int4_stack_device():
         out = torch.empty(1, cfg.H, dtype=torch.float32, device="cuda")
         lg = _dev(logits)
         torch.cuda.synchronize()  # inputs are in place before the stack's stream reads them
-        ewp.stack_forward_device(layers, plans, lg, x, out)
+        ewp.stack_forward_device(layers, plans, lg, x, out, lookahead=lookahead)
         torch.cuda.synchronize()
         xv = x_values(x0, cfg.fmt)
         for l in range(n_layers):
@@ -180,12 +201,52 @@ def test_int4_stack_device():
         worst_hidden = max(worst_hidden, float((np.abs(got - xv) / bound).max()))
         assert np.all(np.abs(got - xv) <= bound)
     say("worst hidden/bound %.3g" % worst_hidden)
-    for p in plans:
-        p.close()
-    for L in layers:
-        L.close()
-    for h in hosts:
-        h.free()
+    _close_stack(hosts, layers, plans)
+
+
+def test_int4_stack_device_lookahead_graph_replays_match_eager():
+    """A token through a 3-layer int4 stack with device lookahead (copy stream
+    forked from and joined to the compute stream) captured in a HIP graph;
+    6 replays, with eager input copies and synchronisations between them,
+    must equal an eager twin stack bit for bit (x, out, plans, table state)."""
+    cfg = W.CONFIGS[4]
+    n_layers, steps = 3, 6
+    say("case: int4 stack %d layers, device lookahead captured in a graph, %d replays" % (n_layers, steps))
+    sa, ca, sb, cb = (torch.cuda.Stream() for _ in range(4))
+    A = _int4_stack(cfg, n_layers, sa, ca)
+    B = _int4_stack(cfg, n_layers, sb, cb)
+    rng = np.random.default_rng(9)
+    sets = np.stack([np.stack([np.sort(rng.choice(cfg.E, cfg.top_k, replace=False))[None]
+                               for _ in range(n_layers)]) for _ in range(steps)])
+    logits = _dev(gen.logits_from_sets(rng, sets, cfg.E))                 # [steps][L][1][E]
+    x0 = _dev(gen.f32_to_bf16_bits(rng.standard_normal((steps, 1, cfg.H)).astype(np.float32)))
+    lg_buf = torch.zeros_like(logits[0])
+    xa = torch.zeros(1, cfg.H, dtype=torch.int16, device="cuda")
+    xb = torch.zeros_like(xa)
+    oa = torch.zeros(1, cfg.H, dtype=torch.float32, device="cuda")
+    ob = torch.zeros_like(oa)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=sb):
+        ewp.stack_forward_device(B[1], B[2], lg_buf, xb, ob, lookahead=True)
+    torch.cuda.synchronize()
+    for t in range(steps):
+        lg_buf.copy_(logits[t])
+        xb.copy_(x0[t])
+        xa.copy_(x0[t])
+        torch.cuda.synchronize()
+        g.replay()
+        ewp.stack_forward_device(A[1], A[2], logits[t], xa, oa, lookahead=True)
+        torch.cuda.synchronize()
+        assert torch.equal(xa, xb) and torch.equal(oa, ob), t
+        for l in range(n_layers):
+            for u, v in zip(A[2][l].read(), B[2][l].read()):
+                assert np.array_equal(u, v), (t, l)
+            for u, v in zip(A[1][l].get_state(), B[1][l].get_state()):
+                assert np.array_equal(np.asarray(u), np.asarray(v)), (t, l)
+    del g
+    _close_stack(A[0], A[1], A[2])
+    _close_stack(B[0], B[1], B[2])
 
 
 def test_bf16_device_step_graph_replays_match_eager():
@@ -202,8 +263,10 @@ def test_bf16_device_step_graph_replays_match_eager():
     s_eager, s_cap = torch.cuda.Stream(), torch.cuda.Stream()
     mk = []
     for s in (s_eager, s_cap):
+        # a copy stream of its own (device steps keep to the compute stream)
         slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, "cuda")
-        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, host, slots, state, s, s, s)
+        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, host, slots, state, s,
+                      torch.cuda.Stream(), s)
         mk.append((L, ewp.Plan(L, 1), slots, state))
     (La, Pa, _, _), (Lb, Pb, _, _) = mk
     logits, x = gen.decode_inputs(cfg, 1, steps=steps)
