@@ -21,6 +21,15 @@ expert that is not resident, once: (E - K) x slot cost.
 """
 
 
+def slots_for_budget(record_bytes, experts, layers, budget_bytes):
+    """Slots per layer that a device-memory budget holds, the same K in every
+    layer. [LRU] "How to use it": the expert cache is given as one budget (in
+    MiB); [PE] "What does a resident slot cost in context length?": a slot
+    costs its record bytes in each MoE layer. So K is the largest count with
+    K x layers x record bytes within the budget, and never more than E."""
+    return min(experts, budget_bytes // (layers * record_bytes))
+
+
 def kv_bytes_per_token(layers=48, kv_heads=4, head_dim=128, elem_bytes=2):
     return 2 * layers * kv_heads * head_dim * elem_bytes
 

@@ -2,6 +2,7 @@
 import json
 import os
 
+import numpy as np
 import pytest
 
 from oracle import sizing
@@ -77,3 +78,30 @@ def test_uniform_rate_table():
     assert round(100 * sizing.uniform_miss_rate(128, 40)) == 69
     assert round(100 * sizing.uniform_miss_rate(128, 26)) == 80
     assert round(100 * sizing.uniform_miss_rate(128, 92)) == 28
+
+
+def _largest_fit(rec, E, layers, budget):
+    # brute force: walk K up while one more slot per layer still fits
+    K = 0
+    while K < E and (K + 1) * layers * rec <= budget:
+        K += 1
+    return K
+
+
+def test_slots_for_budget_against_brute_force():
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        rec = int(rng.integers(1, 10_000_000))
+        E = int(rng.integers(1, 300))
+        layers = int(rng.integers(1, 64))
+        budget = int(rng.integers(0, 2 * E * layers * rec + 1))
+        assert sizing.slots_for_budget(rec, E, layers, budget) == _largest_fit(rec, E, layers, budget)
+
+
+def test_slots_for_budget_boundaries():
+    rec, layers = 2_506_752, 48          # int4 asym g128 record of the stack workload
+    exact = 92 * layers * rec
+    assert sizing.slots_for_budget(rec, 128, layers, exact) == 92
+    assert sizing.slots_for_budget(rec, 128, layers, exact - 1) == 91
+    assert sizing.slots_for_budget(rec, 128, layers, 10 ** 15) == 128   # never more than E
+    assert sizing.slots_for_budget(rec, 128, layers, 0) == 0
