@@ -90,6 +90,11 @@ EXPORTS = {
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_Timing)]),
     "moe_timing_floor": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]),
+    "moe_slots_for_budget": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int64]),
+    "moe_preflight": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                     ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_void_p]),
     "moe_step_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "moe_stack_forward_device": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
@@ -301,6 +306,34 @@ class Layer:
         _check(lib().moe_timing_read(self.handle, ctypes.byref(t)))
         return {name: {"count": t.count[i], "ms": t.ms[i], "bytes": t.bytes[i], "flops": t.flops[i]}
                 for i, name in enumerate(TIMERS)}
+
+
+class _Preflight(ctypes.Structure):
+    _fields_ = [("slot_mb", ctypes.c_double), ("kv_tokens_per_slot", ctypes.c_double),
+                ("batch_cap", ctypes.c_int32), ("all_miss_gb_per_token", ctypes.c_double),
+                ("max_miss", ctypes.c_double), ("random_miss", ctypes.c_double),
+                ("reuse_implied", ctypes.c_int32)]
+
+
+def slots_for_budget(fmt, hidden, intermediate, num_experts, layers, budget_bytes):
+    """Slots per layer that a device-memory budget holds (same K in every layer)."""
+    k = lib().moe_slots_for_budget(int(fmt), int(hidden), int(intermediate), int(num_experts), int(layers),
+                                   int(budget_bytes))
+    if k < 0:
+        _check(k)
+    return k
+
+
+def preflight(layers, experts, top_k, expert_mb, num_slots, link_gbps, tok_s, kv_bytes_per_token):
+    """The preflight numbers of the scheme: slot cost, KV tokens per slot, batch
+    cap, all-miss bytes per token, highest allowed and no-reuse miss rates."""
+    r = _Preflight()
+    _check(lib().moe_preflight(int(layers), int(experts), int(top_k), float(expert_mb), int(num_slots),
+                               float(link_gbps), float(tok_s), float(kv_bytes_per_token),
+                               ctypes.byref(r)))
+    d = {f: getattr(r, f) for f, _ in _Preflight._fields_}
+    d["reuse_implied"] = bool(d["reuse_implied"])
+    return d
 
 
 def timing_floor(stream=None, reps=100):

@@ -227,6 +227,38 @@ size_t moe_state_bytes(int32_t num_experts, int32_t num_slots) {
   return state_layout(num_experts, num_slots).total;
 }
 
+int32_t moe_slots_for_budget(int32_t format, int32_t hidden, int32_t intermediate, int32_t num_experts,
+                             int32_t layers, int64_t budget_bytes) {
+  const size_t rec = moe_record_bytes(format, hidden, intermediate);
+  if (rec == 0 || num_experts < 1 || layers < 1 || budget_bytes < 0) {
+    (void)fail(MOE_ERR_INVALID_ARG, "unsupported shape, num_experts or layers < 1, or negative budget");
+    return MOE_ERR_INVALID_ARG;
+  }
+  const uint64_t per_slot = (uint64_t)rec * (uint64_t)layers;  // one slot in every layer
+  const uint64_t k = (uint64_t)budget_bytes / per_slot;
+  return (int32_t)std::min<uint64_t>(k, (uint64_t)num_experts);
+}
+
+moe_status moe_preflight(int32_t layers, int32_t experts, int32_t top_k, double expert_mb, int32_t K,
+                         double link_gbps, double tok_s, double kv_bytes_per_token,
+                         moe_preflight_result* out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "null output");
+  if (layers < 1 || experts < 1 || top_k < 1 || K < 1 || K > experts)
+    return fail(MOE_ERR_INVALID_ARG, "layers, experts, top_k and K must be >= 1, K <= experts");
+  if (!(expert_mb > 0) || !(link_gbps > 0) || !(tok_s > 0) || !(kv_bytes_per_token > 0))
+    return fail(MOE_ERR_INVALID_ARG, "expert_mb, link_gbps, tok_s and KV bytes must be positive");
+  moe_preflight_result r;
+  r.slot_mb = expert_mb * layers;
+  r.kv_tokens_per_slot = r.slot_mb * 1e6 / kv_bytes_per_token;
+  r.batch_cap = K / top_k;
+  r.all_miss_gb_per_token = layers * top_k * expert_mb / 1e3;
+  r.max_miss = link_gbps / (tok_s * r.all_miss_gb_per_token);
+  r.random_miss = 1.0 - (double)K / experts;
+  r.reuse_implied = r.max_miss < 0.8 * r.random_miss ? 1 : 0;
+  *out = r;
+  return MOE_OK;
+}
+
 void* moe_host_alloc(size_t bytes) {
   void* p = nullptr;
   hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);

@@ -92,6 +92,37 @@ size_t moe_record_bytes(int32_t format, int32_t hidden, int32_t intermediate);
  * each array starting on an 8-byte boundary. */
 size_t moe_state_bytes(int32_t num_experts, int32_t num_slots);
 
+/* Slots per layer for a device-memory budget, the same K in every layer
+ * ([LRU] "How to use it": the expert cache is sized as one memory budget;
+ * [PE] "What does a resident slot cost in context length?": a slot costs its
+ * record bytes in each MoE layer): the largest K <= num_experts with
+ * K * layers * moe_record_bytes(format, hidden, intermediate) <= budget_bytes.
+ * Host-only. Returns K >= 0, or MOE_ERR_INVALID_ARG for an unsupported
+ * format/shape, num_experts or layers < 1, or a negative budget. */
+int32_t moe_slots_for_budget(int32_t format, int32_t hidden, int32_t intermediate,
+                             int32_t num_experts, int32_t layers, int64_t budget_bytes);
+
+/* Preflight arithmetic ([PE] "A preflight script before you turn it on"),
+ * host-only. Inputs: MoE layers, experts per layer, top_k, per-expert MB
+ * (1e6 bytes), slots K, a measured host-link GB/s, a measured decode tok/s and
+ * the KV-cache bytes per token. */
+typedef struct moe_preflight_result {
+  double slot_mb;                /* expert_mb * layers: one slot in every layer   */
+  double kv_tokens_per_slot;     /* slot bytes / KV bytes per token               */
+  int32_t batch_cap;             /* K / top_k: the largest batch that is one wave */
+  double all_miss_gb_per_token;  /* layers * top_k * expert_mb / 1e3              */
+  double max_miss;               /* link GB/s / (tok/s * all-miss GB per token):
+                                    the highest miss rate the speed allows        */
+  double random_miss;            /* 1 - K / E: the miss rate without reuse        */
+  int32_t reuse_implied;         /* max_miss < 0.8 * random_miss                  */
+} moe_preflight_result;
+
+/* MOE_ERR_INVALID_ARG for a null out, layers, experts, top_k or K < 1, K > E,
+ * or a non-positive expert_mb, link_gbps, tok_s or kv_bytes_per_token. */
+moe_status moe_preflight(int32_t layers, int32_t experts, int32_t top_k, double expert_mb,
+                         int32_t num_slots, double link_gbps, double tok_s,
+                         double kv_bytes_per_token, moe_preflight_result* out);
+
 typedef struct moe_layer_desc {
   int32_t num_experts;   /* E, 1..MOE_MAX_EXPERTS                              */
   int32_t top_k;         /* k, 1..min(E, MOE_MAX_TOP_K)                        */

@@ -58,3 +58,52 @@ def test_host_only_queries():
     assert ewp.record_bytes(9, 2048, 768) == 0
     assert ewp.state_bytes(128, 40) == 40 * 4 + 128 * 4 + 40 * 8 + 8
     assert ewp.lib().moe_last_error() is not None
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_slots_for_budget_matches_oracle():
+    """Host-only sizing call against the oracle's definition."""
+    import numpy as np
+    import expert_weight_paging_amd as ewp
+    from oracle import sizing
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        fmt = int(rng.integers(1, 4))
+        E, layers = int(rng.integers(1, 257)), int(rng.integers(1, 97))
+        rec = ewp.record_bytes(fmt, 2048, 768)
+        budget = int(rng.integers(0, 2 * E * layers * rec + 1))
+        assert ewp.slots_for_budget(fmt, 2048, 768, E, layers, budget) == \
+            sizing.slots_for_budget(rec, E, layers, budget)
+    with pytest.raises(ewp.MoeError):
+        ewp.slots_for_budget(1, 2048, 768, 128, 48, -1)
+    with pytest.raises(ewp.MoeError):
+        ewp.slots_for_budget(2, 2000, 768, 128, 48, 1 << 30)   # unsupported FP8 shape
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_preflight_matches_oracle():
+    """Host-only preflight call against the oracle (pinned to the printed
+    worked example in tests/golden/preflight.json) and on random inputs."""
+    import json
+    import numpy as np
+    import expert_weight_paging_amd as ewp
+    from oracle import sizing
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "preflight.json")))
+    kv = sizing.kv_bytes_per_token(**g["kv"])
+    rng = np.random.default_rng(8)
+    cases = [(s["layers"], s["experts"], s["top_k"], s["expert_mb"], s["K"], s["link_gbps"], s["tok_s"])
+             for s in g["setups"]]
+    for _ in range(100):
+        E = int(rng.integers(2, 300))
+        cases.append((int(rng.integers(1, 96)), E, int(rng.integers(1, min(E, 32) + 1)),
+                      float(rng.uniform(0.1, 20)), int(rng.integers(1, E + 1)),
+                      float(rng.uniform(1, 100)), float(rng.uniform(1, 500))))
+    for c in cases:
+        got = ewp.preflight(*c, kv)
+        ref = sizing.preflight(*c, kv)
+        for key in ("slot_mb", "kv_tokens_per_slot", "all_miss_gb_per_token", "max_miss", "random_miss"):
+            assert got[key] == pytest.approx(ref[key], rel=1e-12), (c, key)
+        assert got["batch_cap"] == ref["batch_cap"]
+        assert got["reuse_implied"] == (ref["verdict"] == "reuse implied")
+    with pytest.raises(ewp.MoeError):
+        ewp.preflight(48, 128, 8, 2.43, 129, 50.0, 205.6, kv)   # K > E
