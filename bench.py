@@ -50,10 +50,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+# source file of each kernel whose counters are stored (plus the shared headers)
+KERNEL_SOURCE = {"ffn_up_kernel": "ffn_gemv.hip", "ffn_down_kernel": "ffn_gemv.hip",
+                 "grouped_gemm_kernel<true>": "ffn_gemm.hip", "grouped_gemm_kernel<false>": "ffn_gemm.hip",
+                 "combine_kernel": "ffn_gemm.hip", "route_plan_small_kernel": "plan.hip",
+                 "page_in_kernel": "page_in.hip"}
+
+
+def kernel_source_hash(kernel_name):
+    """Hash of the source that defines a kernel and of the shared headers: a
+    stored traffic figure is used only while these are unchanged."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "expert_weight_paging_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in (KERNEL_SOURCE[kernel_name], "internal.h", "wave.h"):
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -61,22 +70,19 @@ def kernel_source_hash():
 
 def traffic_from_profiles(kernel_name, workload):
     """HBM bytes per launch from the committed PMC summary, only if it was taken
-    on the current kernel sources (else null)."""
+    on the current source of that kernel (else null)."""
     p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("source_hash") != kernel_source_hash():
-        return None
     k = d.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_name)
-    return None if not k else k.get("bytes_per_launch")
+    if not k or kernel_name not in KERNEL_SOURCE or k.get("source_hash") != kernel_source_hash(kernel_name):
+        return None
+    return k.get("bytes_per_launch")
 
 
-KERNEL_KEYS = (("ffn_up_kernel", "ffn_up_kernel"), ("ffn_down_kernel", "ffn_down_kernel"),
-               ("grouped_gemm_kernel<true>", "grouped_gemm_kernel<true>"),
-               ("grouped_gemm_kernel<false>", "grouped_gemm_kernel<false>"),
-               ("route_plan_small_kernel", "route_plan_small_kernel"), ("combine_kernel", "combine_kernel"))
+KERNEL_KEYS = tuple((k, k) for k in KERNEL_SOURCE)
 
 
 def ingest_pmc(fetch_csv, write_csv, workload):
@@ -86,7 +92,7 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     maps its reading for the run's 1 GiB device-to-device copy (the copy in
     measured_peaks) onto 1 GiB. Writes profiles/pmc_traffic.json, keyed by the
     hash of the kernel sources, so bench.py drops the figure once a kernel
-    changes."""
+    changes (each kernel's entry carries the hash of its own source)."""
     import csv
     def load(path, counter):
         per = {}
@@ -114,15 +120,14 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     if os.path.exists(p):
         with open(p) as f:
             d = json.load(f)
-    h = kernel_source_hash()
-    if d.get("source_hash") != h:
-        d = {"source_hash": h, "workloads": {}}
+    d = {"workloads": d.get("workloads", {})}
     w = {}
     for key in sorted(set(fetch) & set(write)):
         fk = sum(fetch[key]) / len(fetch[key]) * ff
         wk = sum(write[key]) / len(write[key]) * wf
         w[key] = {"bytes_per_launch": round((fk + wk) * 1024.0, 1), "fetch_bytes": round(fk * 1024.0, 1),
-                  "write_bytes": round(wk * 1024.0, 1), "launches": len(fetch[key])}
+                  "write_bytes": round(wk * 1024.0, 1), "launches": len(fetch[key]),
+                  "source_hash": kernel_source_hash(key)}
     d["workloads"][workload] = {"kernels": w, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
     with open(p, "w") as f:
         json.dump(d, f, indent=1, sort_keys=True)
@@ -534,8 +539,12 @@ def main():
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs of this workload "
                          "(FETCH_SIZE, WRITE_SIZE) into profiles/pmc_traffic.json")
     args = ap.parse_args()
+    variant = args.workload + "".join(
+        s for s, on in ((" lookahead", args.lookahead), (" uniform", args.routing != "correlated"),
+                        (" batch=%d" % args.batch, args.batch != 1), (" device", args.device and not args.graph),
+                        (" graph", args.graph)) if on)
     if args.ingest_pmc:
-        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], variant)
         return
     if args.graph:
         args.device = True
@@ -566,10 +575,6 @@ def main():
     res = fn(args, torch, dev)
     log("timed %d steps: %.3f ms/step" % (args.steps, res["ms_per_step"]))
     tm, st, cfg = res["timing"], res["stats"], res["cfg"]
-    variant = args.workload + "".join(
-        s for s, on in ((" lookahead", args.lookahead), (" uniform", args.routing != "correlated"),
-                        (" batch=%d" % args.batch, args.batch != 1), (" device", args.device and not args.graph),
-                        (" graph", args.graph)) if on)
     pin = tm["page_in"]
     line = {
         "metric": METRIC,
@@ -591,7 +596,9 @@ def main():
                    "lookahead": bool(args.lookahead), "parallelism": "single GPU"},
         "roofline": roofline(res, args.workload, variant),
         "kernels_us": {k: round(v["ms"] / v["count"] * 1e3, 3) for k, v in tm.items() if v["count"]},
-        "page_in": {"GBps": round(pin["bytes"] / max(pin["ms"], 1e-9) / 1e6, 2),
+        # device-resolved copies are timed without their byte count (the host does not see
+        # the plan); the timed pass pages the same bytes as the counted one
+        "page_in": {"GBps": round((pin["bytes"] or st["bytes_paged"]) / max(pin["ms"], 1e-9) / 1e6, 2),
                     "waves_with_copies": pin["count"], "bytes_per_step": st["bytes_paged"] / args.steps},
         "hit_rate": round(st["hits"] / max(st["refs"], 1), 4),
         "miss_rate_per_activation": round(st["misses"] / max(st["activations"], 1), 4),
