@@ -40,10 +40,12 @@ Pins (tests/test_oracle_*.py, all ``-m "not gpu"``):
              uniform-routing miss rate 1-K/E and the correlated-routing closed
              form;
   formats -- all 256 FP8 e4m3fn codes against torch.float8_e4m3fn, bf16 against
-             torch.bfloat16, hand-packed int4 words;
+             torch.bfloat16, hand-packed int4 words; the sixteen E2M1 values and
+             the E8M0 scale bytes of MXFP4 listed, a byte-by-byte MXFP4 record;
   expert  -- SwiGLU against torch.nn.functional.silu / F.linear in float64;
   layer   -- paged output == unpaged output bitwise;
   stack   -- bf16 round-to-nearest-even against torch.bfloat16 conversion;
-  sizing  -- the worked example the [PE] preflight section prints, reproduced.
+  sizing  -- the worked example the [PE] preflight section prints, reproduced;
+             slots for a memory budget against a brute-force search.
 No oracle function is "parity unpinned".
 """

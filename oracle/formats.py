@@ -27,11 +27,18 @@ Formats (readings, the design doc lists them):
           along the reduction dim, the low nibble holding the lower index.
           Tables: scales W13 [2I][H/128], scales W_d [H][I/128], zeros W13
           [2I][H/128], zeros W_d [H][I/128].
+  mxfp4 : OCP microscaling FP4: blocks of 32 consecutive weights along the
+          reduction dim share one E8M0 scale byte (2^(byte - 127), 255 = NaN);
+          each weight is an E2M1 code (sign 1 bit, exponent 2 bits with bias
+          1, mantissa 1 bit; exponent 0 is subnormal: m/2); two codes per byte,
+          the low nibble holding the lower index. Tables: scales W13
+          [2I][H/32], scales W_d [H][I/32]. ([PE] "What does Paged Experts
+          actually do?" lists MXFP4 among the formats of the follow-up work.)
 """
 import numpy as np
 
-F32, BF16, FP8, INT4 = 0, 1, 2, 3
-NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3_b128", INT4: "int4_asym_g128"}
+F32, BF16, FP8, INT4, MXFP4 = 0, 1, 2, 3, 4
+NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3_b128", INT4: "int4_asym_g128", MXFP4: "mxfp4_e2m1_b32"}
 
 
 def _sections(fmt, H, I):
@@ -49,6 +56,9 @@ def _sections(fmt, H, I):
         return [("w13", np.uint32, (R13, C13 // 8)), ("wd", np.uint32, (Rd, Cd // 8)),
                 ("s13", np.float16, (R13, C13 // 128)), ("sd", np.float16, (Rd, Cd // 128)),
                 ("z13", np.float16, (R13, C13 // 128)), ("zd", np.float16, (Rd, Cd // 128))]
+    if fmt == MXFP4:
+        return [("w13", np.uint8, (R13, C13 // 2)), ("wd", np.uint8, (Rd, Cd // 2)),
+                ("s13", np.uint8, (R13, C13 // 32)), ("sd", np.uint8, (Rd, Cd // 32))]
     raise ValueError("unknown format %r" % (fmt,))
 
 
@@ -108,6 +118,39 @@ def int4_unpack(words):
     return ((w[:, :, None] >> shifts[None, None, :]) & 0xF).reshape(R, W * 8)
 
 
+def e2m1_to_f64(codes):
+    """OCP E2M1 codes (0..15) -> float64, from the definition of the encoding:
+    sign 1 bit, exponent 2 bits (bias 1), mantissa 1 bit; exponent 0 is
+    subnormal, m/2; exponent 1..3 is (1 + m/2) * 2^(e-1). No infinities or NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, m / 2.0, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(s == 1, -mag, mag)
+
+
+def e8m0_to_f64(b):
+    """OCP E8M0 scale bytes -> float64: 2^(b - 127); 255 is NaN."""
+    b = np.asarray(b).astype(np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b - 127.0))
+
+
+def nibbles_unpack(b):
+    """uint8 [R][C/2] -> codes int64 [R][C]; byte j holds codes 2j (low nibble) and 2j+1."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    R, B = b.shape
+    out = np.empty((R, 2 * B), dtype=np.int64)
+    out[:, 0::2] = b & 0xF
+    out[:, 1::2] = b >> 4
+    return out
+
+
+def _dequant_mxfp4(codes, scales):
+    v = e2m1_to_f64(nibbles_unpack(codes))
+    return v * np.repeat(e8m0_to_f64(scales), 32, axis=1)
+
+
 def _dequant_fp8(q, scales):
     R, C = q.shape
     v = fp8_e4m3fn_to_f64(q)
@@ -134,6 +177,8 @@ def decode_record(rec, fmt, H, I):
     elif fmt == INT4:
         w13 = _dequant_int4(sec["w13"], sec["s13"], sec["z13"])
         wd = _dequant_int4(sec["wd"], sec["sd"], sec["zd"])
+    elif fmt == MXFP4:
+        w13, wd = _dequant_mxfp4(sec["w13"], sec["s13"]), _dequant_mxfp4(sec["wd"], sec["sd"])
     else:
         raise ValueError(fmt)
     return w13[:I], w13[I:], wd

@@ -101,3 +101,67 @@ def test_generator_roundtrip(fmt, tol):
             assert np.all(err <= bound)
     # padding is zero
     assert not rec[formats.payload_bytes(fmt, H, I):].any()
+
+
+def test_e2m1_value_table():
+    """The sixteen E2M1 values of the OCP microscaling FP4 element type, listed
+    (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; code 8 is negative zero)."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+             -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    got = formats.e2m1_to_f64(np.arange(16))
+    assert np.array_equal(got, np.array(table))
+    assert np.signbit(got[8])
+
+
+def test_e8m0_scale_bytes():
+    got = formats.e8m0_to_f64(np.array([0, 1, 126, 127, 128, 254, 255]))
+    assert np.array_equal(got[:6], [2.0 ** -127, 2.0 ** -126, 0.5, 1.0, 2.0, 2.0 ** 127])
+    assert np.isnan(got[6])
+
+
+def test_mxfp4_hand_built_record():
+    """A record written byte by byte: nibble order, block scales and sections."""
+    H, I = 64, 32                       # W13 [64][64], W_d [64][32]
+    rec = np.zeros(formats.record_stride(formats.MXFP4, H, I), np.uint8)
+    sec = formats.split_record(rec, formats.MXFP4, H, I)
+    sec["w13"][0, 0] = 0x21             # codes 1 (low nibble) and 2 -> 0.5, 1.0
+    sec["w13"][0, 16] = 0xF7            # element 32: code 7 (6.0), element 33: code 15 (-6.0)
+    sec["s13"][0, 0] = 128              # block 0 of row 0 scaled by 2
+    sec["s13"][0, 1] = 125              # block 1 scaled by 1/4
+    sec["s13"][1:, :] = 127
+    sec["wd"][5, 3] = 0x9A              # W_d row 5, elements 6 and 7: code 10 (-1.0), code 9 (-0.5)
+    sec["sd"][:, :] = 127
+    sec["sd"][5, 0] = 129               # x4
+    g, u, d = formats.decode_record(rec, formats.MXFP4, H, I)
+    assert g[0, 0] == 1.0 and g[0, 1] == 2.0 and g[0, 2] == 0.0
+    assert g[0, 32] == 1.5 and g[0, 33] == -1.5
+    assert d[5, 6] == -4.0 and d[5, 7] == -2.0 and d[5, 8] == 0.0
+    assert np.count_nonzero(g) == 4 and np.count_nonzero(u) == 0 and np.count_nonzero(d) == 2
+    # payload: 3HI/2 code bytes + one scale byte per 32 weights
+    assert formats.payload_bytes(formats.MXFP4, 2048, 768) == 2359296 + 147456
+
+
+def test_mxfp4_generator_roundtrip():
+    """Records the generator packs decode to the packed values within two units
+    of the block scale: the shared exponent floor(log2(amax)) - 2 puts the block
+    maximum in [4, 8) units, so values above 6 units saturate at 6 (error < 2),
+    and below that the widest step (4 -> 6) rounds with error <= 1."""
+    H, I = 256, 384
+    rng = np.random.default_rng(12)
+    w13 = (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32)
+    wd = (rng.standard_normal((H, I)) * 0.02).astype(np.float32)
+    w13[:2, :40] = 0.0
+    rec = gen.encode_record(formats.MXFP4, w13, wd)
+    assert rec.size == gen.record_stride(formats.MXFP4, H, I) == formats.record_stride(formats.MXFP4, H, I)
+    g, u, d = formats.decode_record(rec, formats.MXFP4, H, I)
+    for got, ref in ((g, w13[:I]), (u, w13[I:]), (d, wd)):
+        ref = ref.astype(np.float64)
+        R, C = ref.shape
+        amax = np.abs(ref.reshape(R, C // 32, 32)).max(axis=2)
+        scale = np.exp2(np.floor(np.log2(np.maximum(amax, 1e-38))) - 2)
+        unit = np.repeat(np.where(amax > 0, scale, 0.0), 32, axis=1)
+        small = np.abs(ref) <= 6 * unit
+        assert np.all(np.abs(got - ref)[small] <= unit[small] * 1.0 + 1e-12)
+        bound = unit * 2.0 + 1e-12
+        assert np.all(np.abs(got - ref) <= bound)
+        assert np.all(got[ref == 0] == 0)

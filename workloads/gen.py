@@ -3,7 +3,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-F32, BF16, FP8, INT4 = 0, 1, 2, 3
+F32, BF16, FP8, INT4, MXFP4 = 0, 1, 2, 3, 4
 ROUTE_SHIFT = np.float32(16.0)
 
 
@@ -38,6 +38,8 @@ CONFIGS = {
     3: Config(3, "layer-fp8", FP8, 128, 8, 2048, 768, 40, 1, 256, (1, 2, 4, 5, 6, 8), "correlated", 0.75, 0.02, False),
     4: Config(4, "stack48-int4", INT4, 128, 8, 2048, 768, 92, 48, 256, (1,), "correlated", 0.75, 0.02, False),
     5: Config(5, "prefill48-bf16", BF16, 128, 8, 2048, 768, 92, 48, 1, (2048,), "uniform", 0.0, 0.02, True, tokens=2048),
+    # the next format row: the bf16 layer's shape and routing with MXFP4 experts
+    6: Config(6, "layer-mxfp4", MXFP4, 128, 8, 2048, 768, 40, 1, 256, (1,), "correlated", 0.75, 0.02, False),
 }
 
 
@@ -102,6 +104,8 @@ def _payload(fmt, H, I):
         return 3 * H * I + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128))
     if fmt == INT4:
         return 3 * H * I // 2 + 2 * 2 * (2 * I * (H // 128) + H * (I // 128))
+    if fmt == MXFP4:
+        return 3 * H * I // 2 + (2 * I * (H // 32) + H * (I // 32))
     raise ValueError(fmt)
 
 
@@ -138,6 +142,28 @@ def _int4_groups(w):
     return words, s, z
 
 
+# magnitudes of the E2M1 codes 0..7 and the midpoints between neighbours
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+
+
+def _mxfp4_blocks(w):
+    """w float32 [R][C] -> (code bytes uint8 [R][C/2], scale bytes uint8 [R][C/32]).
+
+    Per block of 32 along a row: shared exponent floor(log2(amax)) - 2 (the
+    largest E2M1 magnitude is 6 = 1.5 * 2^2), scale byte exponent + 127;
+    each weight is rounded to the nearest E2M1 magnitude (saturating at 6)."""
+    R, C = w.shape
+    g = w.reshape(R, C // 32, 32).astype(np.float32)
+    amax = np.abs(g).max(axis=2)
+    e = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, np.float32(1e-38)))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int32)
+    scaled = g / np.exp2(e.astype(np.float32))[:, :, None]
+    idx = np.searchsorted(_E2M1_MID, np.abs(scaled)).astype(np.uint8)   # 0..7
+    code = (idx | ((scaled < 0) & (idx > 0)).astype(np.uint8) << 3).reshape(R, C)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def encode_record(fmt, w13, wd):
     """Pack one expert: w13 [2I][H] (gate rows then up rows), wd [H][I] -> uint8 [stride].
 
@@ -160,6 +186,10 @@ def encode_record(fmt, w13, wd):
         p13, s13, z13 = _int4_groups(np.asarray(w13, np.float32))
         pd, sd, zd = _int4_groups(np.asarray(wd, np.float32))
         parts = [p13, pd, s13, sd, z13, zd]
+    elif fmt == MXFP4:
+        p13, s13 = _mxfp4_blocks(np.asarray(w13, np.float32))
+        pd, sd = _mxfp4_blocks(np.asarray(wd, np.float32))
+        parts = [p13, pd, s13, sd]
     else:
         raise ValueError(fmt)
     raw = np.concatenate([np.ascontiguousarray(p).view(np.uint8).ravel() for p in parts])
