@@ -10,6 +10,8 @@ hidden 2048, MoE intermediate 768):
                misses (pinned host -> slots, copy stream) -> expert FFN over
                the slots (compute stream), every wave.
   decode-fp8   the same layer with block-FP8 experts, --batch B
+  decode-mxfp4 the same layer with MXFP4 experts (E2M1 weights, one E8M0
+               scale per 32), --batch B
   stack-int4   48 int4 layers, K=92 each, batch-1 decode; a step is one token
                through all 48 layers with the bf16 residual; --routing
                uniform for the control run; --lookahead to route/page-in
@@ -43,7 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode tok/s at batch 1 (Qwen3-30B-A3B shapes) + achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-FMT_NAME = {0: "f32", 1: "bf16", 2: "fp8", 3: "int4"}
+FMT_NAME = {0: "f32", 1: "bf16", 2: "fp8", 3: "int4", 4: "mxfp4"}
 
 
 def log(*a):
@@ -195,7 +197,7 @@ def bench_decode(args, torch, dev):
     import workloads as W
     from workloads import gen
 
-    cfg = W.CONFIGS[2 if args.workload == "decode-bf16" else 3]
+    cfg = W.CONFIGS[{"decode-bf16": 2, "decode-fp8": 3, "decode-mxfp4": 6}[args.workload]]
     B = args.batch
     rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
     log("building pinned store: %d experts x %d B" % (cfg.E, rec))
@@ -524,7 +526,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode-bf16",
-                    choices=["decode-bf16", "decode-fp8", "stack-int4", "prefill-bf16"])
+                    choices=["decode-bf16", "decode-fp8", "decode-mxfp4", "stack-int4", "prefill-bf16"])
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--routing", default="correlated", choices=["correlated", "uniform"])
     ap.add_argument("--lookahead", action="store_true")
@@ -560,7 +562,8 @@ def main():
         print("bench.py measures one GPU only: the Paged Experts path is single-GPU and this "
               "build has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    defaults = {"decode-bf16": (256, 32), "decode-fp8": (256, 32), "stack-int4": (128, 16),
+    defaults = {"decode-bf16": (256, 32), "decode-fp8": (256, 32), "decode-mxfp4": (256, 32),
+                "stack-int4": (128, 16),
                 "prefill-bf16": (3, 1)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps
     args.warmup = defaults[1] if args.warmup is None else args.warmup
@@ -570,7 +573,8 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
-    fn = {"decode-bf16": bench_decode, "decode-fp8": bench_decode, "stack-int4": bench_stack,
+    fn = {"decode-bf16": bench_decode, "decode-fp8": bench_decode, "decode-mxfp4": bench_decode,
+          "stack-int4": bench_stack,
           "prefill-bf16": bench_prefill}[args.workload]
     res = fn(args, torch, dev)
     log("timed %d steps: %.3f ms/step" % (args.steps, res["ms_per_step"]))

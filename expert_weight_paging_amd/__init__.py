@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoepage.so")
 
-FMT_F32, FMT_BF16, FMT_FP8, FMT_INT4 = 0, 1, 2, 3
+FMT_F32, FMT_BF16, FMT_FP8, FMT_INT4, FMT_MXFP4 = 0, 1, 2, 3, 4
 MAX_GEMV_TOKENS = 64
 TIMERS = ("route", "ffn_up", "ffn_down", "gemm_up", "gemm_down", "combine", "page_in")
 

@@ -186,6 +186,7 @@ double up_weight_bytes(const moe_layer* L) {
   double b = (double)(r.wd - r.w13);
   if (L->fmt == MOE_FMT_FP8_E4M3_B128) b += (double)(r.sd - r.s13);
   if (L->fmt == MOE_FMT_INT4_ASYM_G128) b += (double)(r.sd - r.s13) + (double)(r.zd - r.z13);
+  if (L->fmt == MOE_FMT_MXFP4_B32) b += (double)(r.sd - r.s13);
   return b;
 }
 double down_weight_bytes(const moe_layer* L) {
@@ -193,6 +194,7 @@ double down_weight_bytes(const moe_layer* L) {
   double b = (double)(r.s13 - r.wd);
   if (L->fmt == MOE_FMT_FP8_E4M3_B128) b += (double)(r.payload - r.sd);
   if (L->fmt == MOE_FMT_INT4_ASYM_G128) b += (double)(r.z13 - r.sd) + (double)(r.payload - r.zd);
+  if (L->fmt == MOE_FMT_MXFP4_B32) b += (double)(r.payload - r.sd);
   return b;
 }
 
@@ -216,7 +218,7 @@ extern "C" {
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 size_t moe_record_bytes(int32_t format, int32_t hidden, int32_t intermediate) {
-  if (format < MOE_FMT_F32 || format > MOE_FMT_INT4_ASYM_G128) return 0;
+  if (format < MOE_FMT_F32 || format > MOE_FMT_MXFP4_B32) return 0;
   if (hidden <= 0 || intermediate <= 0) return 0;
   if (!ffn_shape_supported(format, hidden, intermediate)) return 0;
   return rec_layout(format, hidden, intermediate).stride;
@@ -283,7 +285,7 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
     return fail(MOE_ERR_INVALID_ARG, "top_k must be in 1..min(E, 32)");
   if (d->num_slots < 1 || d->num_slots > d->num_experts)
     return fail(MOE_ERR_INVALID_ARG, "num_slots K must be in 1..E");
-  if (d->format < MOE_FMT_F32 || d->format > MOE_FMT_INT4_ASYM_G128)
+  if (d->format < MOE_FMT_F32 || d->format > MOE_FMT_MXFP4_B32)
     return fail(MOE_ERR_FORMAT, "unknown expert format");
   if (!ffn_shape_supported(d->format, d->hidden, d->intermediate))
     return fail(MOE_ERR_FORMAT, "hidden/intermediate not supported for this format");

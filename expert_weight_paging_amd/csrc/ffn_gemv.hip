@@ -61,6 +61,40 @@ template <> struct Fmt<MOE_FMT_F32> { static constexpr int CV1 = 4, CB2 = 16, CV
 template <> struct Fmt<MOE_FMT_BF16> { static constexpr int CV1 = 8, CB2 = 8, CV2 = 4; };
 template <> struct Fmt<MOE_FMT_FP8_E4M3_B128> { static constexpr int CV1 = 16, CB2 = 4, CV2 = 4; };
 template <> struct Fmt<MOE_FMT_INT4_ASYM_G128> { static constexpr int CV1 = 32, CB2 = 4, CV2 = 8; };
+template <> struct Fmt<MOE_FMT_MXFP4_B32> { static constexpr int CV1 = 32, CB2 = 4, CV2 = 8; };
+
+// MXFP4: one word of 8 E2M1 codes (byte b = codes 2b, 2b+1) -> the same values
+// as e4m3 bytes, converted in hardware. Every E2M1 value is exact in e4m3: a
+// byte permute maps the 3 magnitude bits through the table {0, 0.5, 1, 1.5,
+// 2, 3, 4, 6} (as e4m3: 00 30 38 3C 40 44 48 4C) and the sign bit moves from
+// bit 3 to bit 7 of each byte. Returns the codes 0,2,4,6 (ev) and 1,3,5,7 (od).
+__device__ inline void e2m1x8_to_e4m3(uint32_t w, uint32_t* ev, uint32_t* od) {
+  const uint32_t lo = 0x3C383000u, hi = 0x4C484440u;
+  const uint32_t e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
+  *ev = __builtin_amdgcn_perm(hi, lo, e & 0x07070707u) | ((e & 0x08080808u) << 4);
+  *od = __builtin_amdgcn_perm(hi, lo, o & 0x07070707u) | ((o & 0x08080808u) << 4);
+}
+
+__device__ inline float e8m0_to_float(uint8_t b) {  // 2^(b - 127); 255 is NaN
+  return b == 255 ? __uint_as_float(0x7FC00000u)
+                  : (b == 0 ? 5.877471754111438e-39f : __uint_as_float((uint32_t)b << 23));
+}
+
+// Raw sum of e2m1(q) * x over 8 codes (one word) and the matching activations.
+__device__ inline float dot_e2m1x8(uint32_t w, const float* x, float acc) {
+  uint32_t ev, od;
+  e2m1x8_to_e4m3(w, &ev, &od);
+  const f32x2 a = fp8x2<false>(ev), b = fp8x2<true>(ev), c = fp8x2<false>(od), d = fp8x2<true>(od);
+  acc = fmaf(a.x, x[0], acc);
+  acc = fmaf(c.x, x[1], acc);
+  acc = fmaf(a.y, x[2], acc);
+  acc = fmaf(c.y, x[3], acc);
+  acc = fmaf(b.x, x[4], acc);
+  acc = fmaf(d.x, x[5], acc);
+  acc = fmaf(b.y, x[6], acc);
+  acc = fmaf(d.y, x[7], acc);
+  return acc;
+}
 
 // Load CV1 activations starting at column col, as float.
 template <int F, typename XT>
@@ -108,6 +142,9 @@ __device__ inline float dot1(const uint4 w, const float* x, float* xsum) {
       acc = fmaf(b.x, x[4 * i + 2], acc);
       acc = fmaf(b.y, x[4 * i + 3], acc);
     }
+  } else if constexpr (F == MOE_FMT_MXFP4_B32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = dot_e2m1x8(wv[i], x + 8 * i, acc);
   } else {
     // int4: handled by dot1_int4 (fp16 pair path)
   }
@@ -229,6 +266,18 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
         zu[r][j] = half_to_float(z13[(size_t)(I + i) * ng + g]);
       }
     }
+  } else if constexpr (F == MOE_FMT_MXFP4_B32) {
+    const uint8_t* s13 = rec + L.s13;  // one scale byte per chunk of 32
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int i = min(i0 + r, I - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = min(lane + kWave * j, nch - 1);
+        sg[r][j] = e8m0_to_float(s13[(size_t)i * nch + c]);
+        su[r][j] = e8m0_to_float(s13[(size_t)(I + i) * nch + c]);
+      }
+    }
   }
 
   const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
@@ -265,7 +314,7 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
           float xs = 0.f;
           const float dg = dot1<F>(wg[r][j], xv[j], &xs);
           const float du = dot1<F>(wu[r][j], xv[j], &xs);
-          if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+          if constexpr (F == MOE_FMT_FP8_E4M3_B128 || F == MOE_FMT_MXFP4_B32) {
             g = fmaf(dg, sg[r][j], g);
             u = fmaf(du, su[r][j], u);
           } else {
@@ -315,6 +364,8 @@ __device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
     acc = fmaf(a.y, h[1], acc);
     acc = fmaf(b.x, h[2], acc);
     acc = fmaf(b.y, h[3], acc);
+  } else if constexpr (F == MOE_FMT_MXFP4_B32) {
+    acc = dot_e2m1x8(w[0], h, acc);
   } else {
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc = fmaf((float)((w[0] >> (4 * n)) & 0xFu), h[n], acc);
@@ -388,6 +439,16 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
           sc[r][j] = half_to_float(sd[row * ng + g]);
           zc[r][j] = half_to_float(zd[row * ng + g]);
         }
+    } else if constexpr (F == MOE_FMT_MXFP4_B32) {
+      const uint8_t* sd = rec + L.sd;  // one scale byte per 32 weights = 4 chunks
+      const int nb = I / 32;
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = min(lane + kWave * j, nch - 1);
+          sc[r][j] = e8m0_to_float(sd[(size_t)min(r0 + r, H - 1) * nb + (c * CV2) / 32]);
+        }
     }
     const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
     for (int q = p0; q < p1; ++q) {
@@ -426,7 +487,7 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
           const float hs = hsum[j];
           float unused = 0.f;
           const float d = dot2<F>(cur[r][j], hv[j], &unused);
-          if constexpr (F == MOE_FMT_FP8_E4M3_B128) y = fmaf(d, sc[r][j], y);
+          if constexpr (F == MOE_FMT_FP8_E4M3_B128 || F == MOE_FMT_MXFP4_B32) y = fmaf(d, sc[r][j], y);
           else if constexpr (F == MOE_FMT_INT4_ASYM_G128) y = fmaf(sc[r][j], d - zc[r][j] * hs, y);
           else y += d;
         }
@@ -465,8 +526,12 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
 
 // Work per wavefront scaled so that each moves about the same bytes whatever
 // the weight format: h rows per wavefront (up), output rows per workgroup (down).
-template <int F> constexpr int rpw() { return F == MOE_FMT_INT4_ASYM_G128 ? 4 : F == MOE_FMT_FP8_E4M3_B128 ? 2 : 1; }
-template <int F> constexpr int rw() { return F == MOE_FMT_INT4_ASYM_G128 ? 8 : F == MOE_FMT_FP8_E4M3_B128 ? 8 : 4; }
+template <int F> constexpr int rpw() {
+  return (F == MOE_FMT_INT4_ASYM_G128 || F == MOE_FMT_MXFP4_B32) ? 4 : F == MOE_FMT_FP8_E4M3_B128 ? 2 : 1;
+}
+template <int F> constexpr int rw() {
+  return (F == MOE_FMT_INT4_ASYM_G128 || F == MOE_FMT_MXFP4_B32 || F == MOE_FMT_FP8_E4M3_B128) ? 8 : 4;
+}
 
 template <int F, typename XT>
 hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
@@ -517,11 +582,13 @@ bool ffn_shape_supported(int fmt, int H, int I) {
     case MOE_FMT_BF16: cv1 = 8; cv2 = 4; break;
     case MOE_FMT_FP8_E4M3_B128: cv1 = 16; cv2 = 4; break;
     case MOE_FMT_INT4_ASYM_G128: cv1 = 32; cv2 = 8; break;
+    case MOE_FMT_MXFP4_B32: cv1 = 32; cv2 = 8; break;
     default: return false;
   }
   if (fmt == MOE_FMT_FP8_E4M3_B128 || fmt == MOE_FMT_INT4_ASYM_G128) {
     if (H % 128 || I % 128) return false;
   }
+  if (fmt == MOE_FMT_MXFP4_B32 && (H % 32 || I % 32)) return false;  // whole scale blocks
   if (H % cv1 || I % cv2) return false;
   return nj_of(H / cv1) && nj_of(I / cv2);
 }
@@ -533,6 +600,7 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s) {
     case MOE_FMT_BF16: return up_dispatch<MOE_FMT_BF16, uint16_t>(a, s);
     case MOE_FMT_FP8_E4M3_B128: return up_dispatch<MOE_FMT_FP8_E4M3_B128, uint16_t>(a, s);
     case MOE_FMT_INT4_ASYM_G128: return up_dispatch<MOE_FMT_INT4_ASYM_G128, uint16_t>(a, s);
+    case MOE_FMT_MXFP4_B32: return up_dispatch<MOE_FMT_MXFP4_B32, uint16_t>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -543,6 +611,7 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) {
     case MOE_FMT_BF16: return down_dispatch<MOE_FMT_BF16>(a, s);
     case MOE_FMT_FP8_E4M3_B128: return down_dispatch<MOE_FMT_FP8_E4M3_B128>(a, s);
     case MOE_FMT_INT4_ASYM_G128: return down_dispatch<MOE_FMT_INT4_ASYM_G128>(a, s);
+    case MOE_FMT_MXFP4_B32: return down_dispatch<MOE_FMT_MXFP4_B32>(a, s);
   }
   return hipErrorInvalidValue;
 }

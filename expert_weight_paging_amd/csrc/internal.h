@@ -63,6 +63,7 @@ __host__ __device__ inline int fmt_elem_bits(int fmt) {
     case MOE_FMT_BF16: return 16;
     case MOE_FMT_FP8_E4M3_B128: return 8;
     case MOE_FMT_INT4_ASYM_G128: return 4;
+    case MOE_FMT_MXFP4_B32: return 4;
   }
   return 0;
 }
@@ -91,6 +92,11 @@ __host__ __device__ inline RecLayout rec_layout(int fmt, int H, int I) {
     r.z13 = r.sd + 2 * gd;
     r.zd = r.z13 + 2 * g13;
     end = r.zd + 2 * gd;
+  } else if (fmt == MOE_FMT_MXFP4_B32) {
+    r.s13 = end;                                   // E8M0 bytes, one per 32 weights
+    r.sd = r.s13 + (size_t)2 * I * (H / 32);
+    end = r.sd + (size_t)H * (I / 32);
+    r.z13 = r.zd = end;
   }
   r.payload = end;
   r.stride = (end + 255) / 256 * 256;

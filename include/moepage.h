@@ -56,7 +56,8 @@ typedef enum moe_status {
 } moe_status;
 
 /* Expert weight formats ([PE] "What does Paged Experts actually do?": bf16,
- * block-FP8 and GPTQ-style int4 experts). Record layout of one expert, in this
+ * block-FP8 and GPTQ-style int4 experts; MXFP4 is among the formats it lists
+ * for the follow-up work). Record layout of one expert, in this
  * order (reduction dimension contiguous in every matrix):
  *   W13 = [W_gate; W_up]  2I x H      W_d  H x I
  *   MOE_FMT_F32            : float32 weights
@@ -68,6 +69,11 @@ typedef enum moe_status {
  *                            nibble = lower index), then float16 scales W13
  *                            [2I][H/128], W_d [H][I/128], then float16 zeros
  *                            in the same shapes; w = (q - z) * s
+ *   MOE_FMT_MXFP4_B32      : OCP microscaling FP4: E2M1 codes, two per byte
+ *                            (low nibble = lower index), then one E8M0 scale
+ *                            byte per 32 weights along the reduction dim:
+ *                            W13 [2I][H/32], W_d [H][I/32];
+ *                            w = e2m1(q) * 2^(scale - 127)
  * All per-expert tensors live in the one record, so one page-in moves all of
  * them ([PE] "Can paging change the model's outputs?": a tensor left unpaged
  * makes a paged-in expert run with another expert's values). The record
@@ -76,7 +82,8 @@ typedef enum moe_format {
   MOE_FMT_F32 = 0,
   MOE_FMT_BF16 = 1,
   MOE_FMT_FP8_E4M3_B128 = 2,
-  MOE_FMT_INT4_ASYM_G128 = 3
+  MOE_FMT_INT4_ASYM_G128 = 3,
+  MOE_FMT_MXFP4_B32 = 4
 } moe_format;
 
 /* Limits of this implementation (checked at init). */

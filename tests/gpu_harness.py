@@ -14,7 +14,7 @@ import expert_weight_paging_amd as ewp
 from oracle.layer import PagedLayer
 from workloads import gen
 
-TOL = {gen.F32: 1e-5, gen.BF16: 2e-2, gen.FP8: 5e-2, gen.INT4: 5e-2}
+TOL = {gen.F32: 1e-5, gen.BF16: 2e-2, gen.FP8: 5e-2, gen.INT4: 5e-2, gen.MXFP4: 5e-2}
 
 
 def say(*a):

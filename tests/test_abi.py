@@ -48,13 +48,16 @@ def test_host_only_queries():
     """Pure host functions of the ABI (no GPU needed)."""
     import expert_weight_paging_amd as ewp
     from workloads import gen
-    for fmt in (0, 1, 2, 3):
+    for fmt in (0, 1, 2, 3, 4):
         for H, I in ((2048, 768), (256, 384)):
             assert ewp.record_bytes(fmt, H, I) == gen.record_stride(fmt, H, I)
     assert ewp.record_bytes(1, 2048, 768) == 9437184
     assert ewp.record_bytes(2, 2048, 768) == 4719872          # 4,719,744 payload, 256-aligned
     assert ewp.record_bytes(3, 2048, 768) == 2506752
     assert ewp.record_bytes(2, 2000, 768) == 0                 # FP8 needs multiples of 128
+    assert ewp.record_bytes(4, 2048, 768) == 2506752           # MXFP4: 4.25 bits a weight
+    assert ewp.record_bytes(4, 2016, 768) == 2016 * 768 * 3 // 2 + 2016 * 768 * 3 // 32
+    assert ewp.record_bytes(4, 2000, 768) == 0                 # MXFP4 needs multiples of 32
     assert ewp.record_bytes(9, 2048, 768) == 0
     assert ewp.state_bytes(128, 40) == 40 * 4 + 128 * 4 + 40 * 8 + 8
     assert ewp.lib().moe_last_error() is not None
@@ -68,7 +71,7 @@ def test_slots_for_budget_matches_oracle():
     from oracle import sizing
     rng = np.random.default_rng(7)
     for _ in range(200):
-        fmt = int(rng.integers(1, 4))
+        fmt = int(rng.integers(1, 5))
         E, layers = int(rng.integers(1, 257)), int(rng.integers(1, 97))
         rec = ewp.record_bytes(fmt, 2048, 768)
         budget = int(rng.integers(0, 2 * E * layers * rec + 1))

@@ -63,3 +63,37 @@ def test_int4_layer():
     worst = p.run(logits, x, sample=lambda t: t % 8 == 0 or t == 63)
     say("int4 worst rel err", worst)
     p.close()
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_mxfp4_layer(B):
+    cfg = W.CONFIGS[6]
+    steps = 64 if B == 1 else 24
+    say("case: mxfp4 layer E=128 k=8 H=2048 I=768 K=40, B=%d, %d steps" % (B, steps))
+    p = _layer(cfg, B)
+    logits, x = gen.decode_inputs(cfg, B, steps=steps)
+    worst = p.run(logits, x, sample=lambda t: t % 8 == 0 or t == steps - 1)
+    st = p.gpu.stats()
+    say("mxfp4 B=%d worst rel err %.3g stats %s" % (B, worst, st))
+    assert st["steps"] == steps and st["misses"] + st["hits"] == st["refs"]
+    p.close()
+
+
+def test_mxfp4_small_ragged_shape():
+    """H and I multiples of the 32-value scale block but not of 64 or 128:
+    a partial wavefront of chunks in the up projection and a short down row."""
+    E, k, H, I, K, B = 8, 2, 96, 160, 4, 3
+    say("case: mxfp4 E=8 k=2 H=96 I=160 K=4 B=3, 12 steps")
+    rng = np.random.default_rng(11)
+    recs = [gen.encode_record(gen.MXFP4, (rng.standard_normal((2 * I, H)) * 0.1).astype(np.float32),
+                              (rng.standard_normal((H, I)) * 0.1).astype(np.float32)) for _ in range(E)]
+
+    def fill(a):
+        for e in range(E):
+            a[e] = recs[e]
+    p = PairedLayer(E, k, H, I, K, gen.MXFP4, fill, max_tokens=B)
+    logits = rng.standard_normal((12, B, E)).astype(np.float32)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((12, B, H)).astype(np.float32))
+    worst = p.run(logits, x, check_state_every=1)
+    say("mxfp4 small worst rel err %.3g" % worst)
+    p.close()

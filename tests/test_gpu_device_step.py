@@ -116,6 +116,18 @@ def test_fp8_device_steps(B):
     p.close()
 
 
+def test_mxfp4_device_steps():
+    cfg = W.CONFIGS[6]
+    say("case: device steps, mxfp4 layer K=40, 32 steps at batch 1")
+    p = _layer(cfg, 1)
+    logits, x = gen.decode_inputs(cfg, 1, steps=32)
+    worst, hits, misses = _run_device(p, logits, x, sample=lambda t: t % 4 == 0 or t == 31)
+    st = p.gpu.stats()
+    say("worst rel err %.3g hits %d misses %d" % (worst, hits, misses))
+    assert st["hits"] == hits and st["misses"] == misses
+    p.close()
+
+
 def test_int4_device_steps_interleaved_with_host_steps():
     cfg = W.CONFIGS[4]
     say("case: int4 layer K=92, 40 steps, every third one host-driven")
