@@ -21,7 +21,10 @@ hidden 2048, MoE intermediate 768):
 Modes of the decode workloads: --device runs device-resolved single-wave
 steps (the plan stays on the GPU, a copy kernel pages the misses in, no host
 synchronisation); with stack-int4, --graph also captures one token through
-the 48 layers in a HIP graph and replays it per token.
+the 48 layers in a HIP graph and replays it per token. Batches beyond one
+wave: --waves expert (default, host-driven expert-partitioned waves) or
+--waves token (groups of K // top_k tokens, each a device-resolved step);
+--slots K overrides the decode workloads' slot count (the 4-request cliff).
 Inputs (router logits, hidden states) are resident in HBM before the timed
 region; expert stores live in pinned host memory by design of the method.
 
@@ -203,10 +206,12 @@ def bench_decode(args, torch, dev):
     log("building pinned store: %d experts x %d B" % (cfg.E, rec))
     host = ewp.HostStore(cfg.E, rec)
     gen.expert_store(cfg, out=host.array)
-    slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, dev)
+    K = args.slots or cfg.K
+    slots, state = ewp.alloc_layer_buffers(cfg.E, K, rec, dev)
     compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
-    layer = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, host, slots, state,
+    layer = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt, host, slots, state,
                       compute, copy, compute)
+    G = min(K // cfg.top_k, B, 64)
     plan = ewp.Plan(layer, B)
     total = args.warmup + args.steps
     logits, x = gen.decode_inputs(cfg, B, steps=total)
@@ -216,7 +221,9 @@ def bench_decode(args, torch, dev):
 
     def run(t0, n):
         for t in range(t0, t0 + n):
-            if args.device:
+            if args.waves == "token":
+                layer.step_token_waves(plan, lg_d[t], x_d[t], out)
+            elif args.device:
                 layer.step_device(plan, lg_d[t], x_d[t], out)
             else:
                 layer.step(plan, lg_d[t], x_d[t], out)
@@ -243,23 +250,27 @@ def bench_decode(args, torch, dev):
     d = {k: s1[k] - s0[k] for k in s1}
     res = {"value": args.steps * B / el, "ms_per_step": el / args.steps * 1e3, "timing": tm,
            "floor_us": floor_us,
-           "stats": d, "cfg": cfg, "B": B,
+           "stats": d, "cfg": cfg, "B": B, "K": K,
            "workload": "one Qwen3-30B-A3B-shaped MoE layer, %s experts, E=%d top_k=%d hidden=%d "
                        "intermediate=%d, K=%d resident slots, decode at batch %d, correlated routing "
                        "p=%.2f, cold table%s" % (FMT_NAME[cfg.fmt], cfg.E, cfg.top_k, cfg.H, cfg.I,
-                                                cfg.K, B, cfg.p_keep,
-                                                ", " + mode_name(args) if args.device else "")}
+                                                K, B, cfg.p_keep,
+                                                ", " + mode_name(args) if (args.device or args.waves == "token") else "")}
 
     def cpu(budget):
         from oracle.layer import PagedLayer
-        ref = PagedLayer(np.array(host.array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K)
+        ref = PagedLayer(np.array(host.array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, K)
         # a longer decode sequence from the same seeded generator (same recipe),
         # so that the sample holds about `budget` seconds of oracle work
         lg_c, x_c = gen.decode_inputs(cfg, B, steps=max(total, 4096))
         n = 0
         t0 = time.perf_counter()
         while n < len(lg_c) and (time.perf_counter() - t0) < budget:
-            ref.step(lg_c[n], gen.bf16_bits_to_f32(x_c[n]).astype(np.float64))
+            xv = gen.bf16_bits_to_f32(x_c[n]).astype(np.float64)
+            if args.waves == "token":
+                ref.step_token_waves(lg_c[n], xv, G)
+            else:
+                ref.step(lg_c[n], xv)
             n += 1
         el = time.perf_counter() - t0
         return {"value": n * B / el, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
@@ -298,6 +309,9 @@ def build_stack(cfg, dev, torch, max_tokens, initial_fill):
 
 
 def mode_name(args):
+    if args.waves == "token":
+        return ("token-partitioned waves: groups of K // top_k tokens, each a device-resolved "
+                "single-wave step (kernel page-in, no host synchronisation)")
     la = ", routes and copies ahead on the copy stream (lookahead)" if args.lookahead else ""
     if args.graph:
         return "device-resolved steps (kernel page-in) captured in one HIP graph per token" + la
@@ -534,6 +548,10 @@ def main():
                     help="device-resolved single-wave steps (kernel page-in, no host sync)")
     ap.add_argument("--graph", action="store_true",
                     help="stack-int4 only: device-resolved token captured in a HIP graph")
+    ap.add_argument("--waves", default="expert", choices=["expert", "token"],
+                    help="decode batches beyond one wave: expert-partitioned waves (host-driven, "
+                         "default) or groups of K // top_k tokens as device-resolved steps")
+    ap.add_argument("--slots", type=int, default=None, help="decode workloads: K instead of the config's")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
@@ -544,7 +562,8 @@ def main():
     variant = args.workload + "".join(
         s for s, on in ((" lookahead", args.lookahead), (" uniform", args.routing != "correlated"),
                         (" batch=%d" % args.batch, args.batch != 1), (" device", args.device and not args.graph),
-                        (" graph", args.graph)) if on)
+                        (" graph", args.graph), (" waves=token", args.waves == "token"),
+                        (" K=%s" % args.slots, args.slots is not None)) if on)
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], variant)
         return
@@ -557,6 +576,12 @@ def main():
                         (args.lookahead and args.workload != "stack-int4")):
         print("--device runs single-wave decode steps: not with prefill-bf16; --lookahead only "
               "with stack-int4", file=sys.stderr)
+        sys.exit(2)
+    if (args.waves == "token" or args.slots) and not args.workload.startswith("decode"):
+        print("--waves token and --slots apply to the decode workloads", file=sys.stderr)
+        sys.exit(2)
+    if args.waves == "token" and args.device:
+        print("--waves token already runs device-resolved steps", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Paged Experts path is single-GPU and this "
@@ -595,7 +620,7 @@ def main():
         "data": "synthetic (seeded; %s routing, weights N(0,0.02))"
                 % ("correlated p=0.75" if cfg.routing == "correlated" and args.routing == "correlated"
                    else "uniform"),
-        "config": {"workload": res["workload"], "batch": res["B"], "num_slots": cfg.K,
+        "config": {"workload": res["workload"], "batch": res["B"], "num_slots": res.get("K", cfg.K),
                    "experts": cfg.E, "top_k": cfg.top_k, "layers": cfg.layers,
                    "lookahead": bool(args.lookahead), "parallelism": "single GPU"},
         "roofline": roofline(res, args.workload, variant),

@@ -97,6 +97,8 @@ EXPORTS = {
                                      ctypes.c_void_p]),
     "moe_step_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "moe_step_token_waves": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "moe_stack_forward_device": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
@@ -278,6 +280,19 @@ class Layer:
         _check(lib().moe_step_device(self.handle, plan.handle, _ptr(logits), int(T), _ptr(x), _ptr(out),
                                      _ptr(x_res)))
         plan.dev_tokens = int(T)
+
+    def group_tokens(self, plan):
+        """Tokens per group of step_token_waves: min(K // top_k, max_tokens, 64)."""
+        return min(self.K // self.top_k, plan.max_tokens, 64)
+
+    def step_token_waves(self, plan, logits, x, out, x_res=None, num_tokens=None):
+        """Token-partitioned waves: groups of group_tokens(plan) consecutive
+        tokens, each one device-resolved single-wave step, no host sync."""
+        T = logits.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moe_step_token_waves(self.handle, plan.handle, _ptr(logits), int(T), _ptr(x), _ptr(out),
+                                          _ptr(x_res)))
+        G = self.group_tokens(plan)
+        plan.dev_tokens = int(T) - (int(T) - 1) // G * G  # the last group's size
 
     def reset(self):
         _check(lib().moe_layer_reset(self.handle))

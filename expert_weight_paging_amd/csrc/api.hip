@@ -824,6 +824,31 @@ moe_status moe_step_device(moe_layer* L, moe_plan* p, const float* logits, int32
                           stream_capturing(L->compute));
 }
 
+moe_status moe_step_token_waves(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
+                                float* out, void* x_res) {
+  if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
+  const int G = std::min({L->K / L->k, p->max_tokens, (int)MOE_MAX_GEMV_TOKENS});
+  if (G < 1) return fail(MOE_ERR_INVALID_ARG, "K < top_k: no group of tokens fits one wave");
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 1");
+  if (!logits || !x || !out) return fail(MOE_ERR_INVALID_ARG, "null logits, x or out");
+  if (((uintptr_t)x & 15) || ((uintptr_t)out & 15) || ((uintptr_t)x_res & 7))
+    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned, x_res 8-byte aligned");
+  if (x_res && L->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
+  moe_status st = step_device_check(L, p, std::min(G, T));
+  if (st) return st;
+  const size_t xe = L->fmt == MOE_FMT_F32 ? 4 : 2, H = (size_t)L->H;
+  const bool cap = stream_capturing(L->compute);
+  // consecutive groups of G tokens, one device-resolved single-wave step each,
+  // in token order on the compute stream (every group reuses the plan buffers)
+  for (int32_t t0 = 0; t0 < T; t0 += G) {
+    const int32_t n = std::min(G, T - t0);
+    st = step_device_impl(L, p, logits + (size_t)t0 * L->E, n, (const uint8_t*)x + t0 * H * xe,
+                          out + t0 * H, x_res ? (uint16_t*)x_res + t0 * H : nullptr, L->compute, cap);
+    if (st) return st;
+  }
+  return MOE_OK;
+}
+
 moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans, int32_t n,
                                     const float* logits, int32_t T, void* x, float* out,
                                     int32_t lookahead) {

@@ -292,6 +292,26 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
 moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits,
                            int32_t num_tokens, const void* x, float* out, void* x_res);
 
+/* Token-partitioned waves: a batch larger than one wave allows, served as
+ * consecutive groups of G = min(K / top_k, max_tokens, MOE_MAX_GEMV_TOKENS)
+ * tokens, each group one device-resolved single-wave step (moe_step_device on
+ * tokens [g*G, g*G + G) of logits, x, out and x_res), in token order on the
+ * compute stream, with no host synchronisation ([PE] "What happens with more
+ * than one request?": a decode batch of up to K // top_k requests is one
+ * wave, the captured case; larger batches need several waves, each with its
+ * own page-in). Against moe_route's expert-partitioned waves this pages an
+ * expert shared by two groups once per group if it was evicted in between
+ * (never fewer page-ins, often more), but needs no host round trip.
+ *   logits: device float32 [T][E]; x: device bf16 [T][H] (fp32 for the f32
+ *           format); out: device float32 [T][H], overwritten; x_res: NULL or
+ *           device bf16 [T][H] (as in moe_step_device)
+ * Requirements: T >= 1, K >= top_k, and the moe_step_device requirements
+ * for the first group. The plan's device arrays afterwards describe the last
+ * group. Errors: as moe_step_device; a failure leaves the groups before it
+ * enqueued. */
+moe_status moe_step_token_waves(moe_layer* layer, moe_plan* plan, const float* logits,
+                                int32_t num_tokens, const void* x, float* out, void* x_res);
+
 /* moe_stack_forward through device-resolved steps: for each layer l,
  * moe_step_device(layer l, plan l, logits[l], T, x, out, x_res = x), with no
  * host synchronisation (capturable). Same requirements per layer as

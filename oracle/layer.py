@@ -95,6 +95,27 @@ class PagedLayer:
                     self._apply(self._slot_weights(s), e, ids, w, x, out)
         return out, ids, w, plan
 
+    def step_token_waves(self, logits, x, group, compute=True):
+        """Token-partitioned waves. [PE] "What happens with more than one
+        request?": a decode step is one wave when tokens x top_k <= K, so up to
+        K // top_k tokens always fit one; a larger batch is served here as
+        consecutive groups of `group` (<= K // top_k) tokens in token order,
+        each group a step of its own (own routing of its rows, own LRU tick,
+        own page-ins). Returns (out [B,H] or None, ids [B,k], w [B,k],
+        list of the groups' plans)."""
+        if not 1 <= group <= self.K // self.top_k:
+            raise ValueError("group must be in 1..K // top_k")
+        B = np.asarray(logits).shape[0]
+        outs, ids, ws, plans = [], [], [], []
+        for t0 in range(0, B, group):
+            o, i, w, p = self.step(logits[t0:t0 + group], x[t0:t0 + group], compute)
+            outs.append(o)
+            ids.append(i)
+            ws.append(w)
+            plans.append(p)
+        out = np.concatenate(outs) if compute else None
+        return out, np.concatenate(ids), np.concatenate(ws), plans
+
     @staticmethod
     def _apply(weights, e, ids, w, x, out):
         """out[t] += w_tj * expert_e(x_t) for every (t, j) routed to expert e."""

@@ -128,6 +128,46 @@ def test_mxfp4_device_steps():
     p.close()
 
 
+@pytest.mark.parametrize("cid,B,K", [(1, 5, 4), (3, 6, 40), (3, 8, 40), (3, 4, 24)])
+def test_token_waves(cid, B, K):
+    """Batches beyond one wave as groups of K // top_k tokens, each a
+    device-resolved single-wave step, against the oracle's token waves."""
+    cfg = W.CONFIGS[cid]
+    steps = 16
+    say("case: token waves, %s B=%d K=%d, %d steps" % (cfg.name, B, K, steps))
+    p = _layer(cfg, B, K=K)
+    G = p.gpu.group_tokens(p.plan)
+    assert G == K // cfg.top_k
+    logits, x = gen.decode_inputs(cfg, B, steps=steps)
+    lg, xd = _dev(logits), _dev(x)
+    out = torch.empty(B, p.H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    hits = misses = 0
+    worst = 0.0
+    for t in range(steps):
+        comp = t % 3 == 0 or t == steps - 1
+        p.gpu.step_token_waves(p.plan, lg[t], xd[t], out)
+        o_ref, ids_ref, w_ref, plans = p.ref.step_token_waves(logits[t], x_values(x[t], p.fmt), G, compute=comp)
+        assert len(plans) == -(-B // G)
+        hits += sum(len(q.hits) for q in plans)
+        misses += sum(len(q.missed) for q in plans)
+        last = (len(plans) - 1) * G
+        _check_device_plan(p, ids_ref[last:], w_ref[last:], plans[-1])
+        if comp:
+            torch.cuda.synchronize()
+            e = rel_err(out.cpu().numpy(), o_ref)
+            worst = max(worst, e)
+            assert e <= TOL[p.fmt], (t, e)
+        if (t + 1) % 4 == 0:
+            p.check_state()
+    torch.cuda.synchronize()
+    p.check_state()
+    st = p.gpu.stats()
+    say("worst rel err %.3g hits %d misses %d" % (worst, hits, misses))
+    assert st["hits"] == hits and st["misses"] == misses
+    p.close()
+
+
 def test_int4_device_steps_interleaved_with_host_steps():
     cfg = W.CONFIGS[4]
     say("case: int4 layer K=92, 40 steps, every third one host-driven")
