@@ -6,9 +6,8 @@ Workloads (synthetic, seeded, Qwen3-30B-A3B shapes: 128 experts, top-8,
 hidden 2048, MoE intermediate 768):
   decode-bf16  (default) one bf16 MoE layer, K=40 slots, batch-1 decode,
                correlated routing p=0.75, cold table. A step is one token:
-               router -> slot plan (host sees the plan) -> page-in of the
-               misses (pinned host -> slots, copy stream) -> expert FFN over
-               the slots (compute stream), every wave.
+               router -> slot plan -> page-in of the misses (pinned host ->
+               slots) -> expert FFN over the slots, every wave.
   decode-fp8   the same layer with block-FP8 experts, --batch B
   decode-mxfp4 the same layer with MXFP4 experts (E2M1 weights, one E8M0
                scale per 32), --batch B
@@ -18,10 +17,13 @@ hidden 2048, MoE intermediate 768):
                layer l+1 while layer l computes
   prefill-bf16 one 2048-token chunk through 48 bf16 layers, K=92, warm
                tables, uniform routing; a step is one chunk
-Modes of the decode workloads: --device runs device-resolved single-wave
-steps (the plan stays on the GPU, a copy kernel pages the misses in, no host
-synchronisation); with stack-int4, --graph also captures one token through
-the 48 layers in a HIP graph and replays it per token. Batches beyond one
+Modes. By default a decode step whose batch fits one wave (B * top_k <= K)
+is device-resolved (the plan stays on the GPU, a copy kernel pages the misses
+in through the host store's device mapping, no host synchronisation), and a
+stack token is one HIP graph of such steps through the 48 layers, replayed
+per token. --host forces host-driven steps (the host reads the plan and
+issues DMA copies on a copy stream while the resident experts compute);
+--device asks for device-resolved steps without the graph. Batches beyond one
 wave: --waves expert (default, host-driven expert-partitioned waves) or
 --waves token (groups of K // top_k tokens, each a device-resolved step);
 --slots K overrides the decode workloads' slot count (the 4-request cliff).
@@ -48,6 +50,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode tok/s at batch 1 (Qwen3-30B-A3B shapes) + achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+DECODE_CONFIG = {"decode-bf16": 2, "decode-fp8": 3, "decode-mxfp4": 6}
 FMT_NAME = {0: "f32", 1: "bf16", 2: "fp8", 3: "int4", 4: "mxfp4"}
 
 
@@ -200,7 +203,7 @@ def bench_decode(args, torch, dev):
     import workloads as W
     from workloads import gen
 
-    cfg = W.CONFIGS[{"decode-bf16": 2, "decode-fp8": 3, "decode-mxfp4": 6}[args.workload]]
+    cfg = W.CONFIGS[DECODE_CONFIG[args.workload]]
     B = args.batch
     rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
     log("building pinned store: %d experts x %d B" % (cfg.E, rec))
@@ -306,6 +309,22 @@ def build_stack(cfg, dev, torch, max_tokens, initial_fill):
         % (cfg.layers, cfg.layers * cfg.E * rec / 1e9, cfg.layers * cfg.K * rec / 1e9,
            time.perf_counter() - t0))
     return hosts, layers, plans, pool, compute
+
+
+def resolve_default_mode(args):
+    """Without a mode flag, a decode step whose batch fits one wave (B * top_k <= K)
+    runs as a device-resolved step, the stack as one HIP graph per token (the
+    captured single-wave path); batches beyond one wave, --lookahead and
+    prefill run host-driven."""
+    if args.host or args.device or args.graph or args.waves == "token":
+        return
+    import workloads as W
+    if args.workload.startswith("decode"):
+        cfg = W.CONFIGS[DECODE_CONFIG[args.workload]]
+        if args.batch * cfg.top_k <= (args.slots or cfg.K):
+            args.device = True
+    elif args.workload == "stack-int4" and not args.lookahead:
+        args.graph = True
 
 
 def mode_name(args):
@@ -546,6 +565,9 @@ def main():
     ap.add_argument("--lookahead", action="store_true")
     ap.add_argument("--device", action="store_true",
                     help="device-resolved single-wave steps (kernel page-in, no host sync)")
+    ap.add_argument("--host", action="store_true",
+                    help="host-driven steps (the host reads each plan and issues DMA page-ins) even "
+                         "when the batch fits one wave")
     ap.add_argument("--graph", action="store_true",
                     help="stack-int4 only: device-resolved token captured in a HIP graph")
     ap.add_argument("--waves", default="expert", choices=["expert", "token"],
@@ -559,6 +581,10 @@ def main():
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs of this workload "
                          "(FETCH_SIZE, WRITE_SIZE) into profiles/pmc_traffic.json")
     args = ap.parse_args()
+    if args.host and (args.device or args.graph or args.waves == "token"):
+        print("--host excludes --device, --graph and --waves token", file=sys.stderr)
+        sys.exit(2)
+    resolve_default_mode(args)
     variant = args.workload + "".join(
         s for s, on in ((" lookahead", args.lookahead), (" uniform", args.routing != "correlated"),
                         (" batch=%d" % args.batch, args.batch != 1), (" device", args.device and not args.graph),

@@ -47,6 +47,17 @@ __device__ inline f32x2 fp8x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + lo(w)*lo(x) + hi(w)*hi(x) over two packed bf16 pairs (products exact
+// in fp32; one fp32 accumulation per pair).
+__device__ inline float dot2_bf16(uint32_t w, uint32_t x, float acc) {
+  bf16x2_t a, b;
+  __builtin_memcpy(&a, &w, 4);
+  __builtin_memcpy(&b, &x, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+
 __device__ inline float half_to_float(uint16_t h) {
   _Float16 v;
   __builtin_memcpy(&v, &h, 2);
@@ -282,6 +293,39 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
 
   const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
   const XT* xbase = (const XT*)a.x;
+  if constexpr (F == MOE_FMT_BF16 && sizeof(XT) == 2) {
+    // bf16 weights and activations: dot the packed pairs directly (8 values
+    // per 16-byte chunk in 4 words), activations never widened to fp32
+    for (int q = p0; q < p1; ++q) {
+      const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
+      uint4 xw[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = lane + kWave * j;
+        xw[j] = c < nch ? *(const uint4*)((const uint16_t*)xbase + (size_t)t * H + c * CV1)
+                        : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          g = dot2_bf16(wg[r][j].x, xw[j].x, g);
+          g = dot2_bf16(wg[r][j].y, xw[j].y, g);
+          g = dot2_bf16(wg[r][j].z, xw[j].z, g);
+          g = dot2_bf16(wg[r][j].w, xw[j].w, g);
+          u = dot2_bf16(wu[r][j].x, xw[j].x, u);
+          u = dot2_bf16(wu[r][j].y, xw[j].y, u);
+          u = dot2_bf16(wu[r][j].z, xw[j].z, u);
+          u = dot2_bf16(wu[r][j].w, xw[j].w, u);
+        }
+        g = wave_sum(g);
+        u = wave_sum(u);
+        if (lane == 0 && i0 + r < I) a.h[(size_t)q * I + i0 + r] = g / (1.f + __expf(-g)) * u;
+      }
+    }
+    return;
+  }
   for (int q = p0; q < p1; ++q) {
     // with one token every pair is token 0: no dependent pair-list load
     const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
