@@ -84,10 +84,12 @@ def traffic_from_profiles(kernel_name, workload):
         return None
     with open(p) as f:
         d = json.load(f)
-    k = d.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_name)
-    if not k or kernel_name not in KERNEL_SOURCE or k.get("source_hash") != kernel_source_hash(kernel_name):
-        return None
-    return k.get("bytes_per_launch")
+    # a graph replays the device-resolved launches unchanged: same bytes per launch
+    for key in (workload, workload.replace(" graph", " device")):
+        k = d.get("workloads", {}).get(key, {}).get("kernels", {}).get(kernel_name)
+        if k and kernel_name in KERNEL_SOURCE and k.get("source_hash") == kernel_source_hash(kernel_name):
+            return k.get("bytes_per_launch")
+    return None
 
 
 KERNEL_KEYS = tuple((k, k) for k in KERNEL_SOURCE)

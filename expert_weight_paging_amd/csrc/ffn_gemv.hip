@@ -349,6 +349,16 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
       float g = 0.f, u = 0.f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
+        // FP8 and MXFP4: opaque to the compiler at each use, which stops the
+        // weight-to-float conversions from being hoisted out of the pair loop
+        // (that would keep every converted value of the wavefront's rows live
+        // at once: spills, one wavefront per SIMD); at one pair per expert
+        // nothing is recomputed, and each use waits only for its own load.
+        // (int4 measured faster without it.)
+        if constexpr (F == MOE_FMT_FP8_E4M3_B128 || F == MOE_FMT_MXFP4_B32) {
+          asm volatile("" : "+v"(wg[r][j].x), "+v"(wg[r][j].y), "+v"(wg[r][j].z), "+v"(wg[r][j].w));
+          asm volatile("" : "+v"(wu[r][j].x), "+v"(wu[r][j].y), "+v"(wu[r][j].z), "+v"(wu[r][j].w));
+        }
         if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
           const float dg = dot1_int4(wg[r][j], xp[j]);
           const float du = dot1_int4(wu[r][j], xp[j]);
@@ -530,6 +540,9 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
         for (int j = 0; j < NJ; ++j) {
           const float hs = hsum[j];
           float unused = 0.f;
+#pragma unroll
+          for (int n = 0; n < NW; ++n)  // no hoisting of conversions (as in the up kernel)
+            asm volatile("" : "+v"(cur[r][j][n]));
           const float d = dot2<F>(cur[r][j], hv[j], &unused);
           if constexpr (F == MOE_FMT_FP8_E4M3_B128 || F == MOE_FMT_MXFP4_B32) y = fmaf(d, sc[r][j], y);
           else if constexpr (F == MOE_FMT_INT4_ASYM_G128) y = fmaf(sc[r][j], d - zc[r][j] * hs, y);
