@@ -385,13 +385,9 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
       running += __popcll(mask);
     }
   }
-  if (dstats && threadIdx.x == 0 && T > 0) {
-    dstats[0] += 1;
-    dstats[1] += D;
-    dstats[2] += P;
-    dstats[3] += nH;
-    dstats[4] += D - nH;
-    dstats[5] += nw;
+  if (dstats && threadIdx.x < 6 && T > 0) {  // no-return atomic adds: no read round trip
+    const long long v[6] = {1, D, P, nH, D - nH, nw};
+    __hip_atomic_fetch_add(dstats + threadIdx.x, v[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
