@@ -119,6 +119,16 @@ def test_e8m0_scale_bytes():
     assert np.isnan(got[6])
 
 
+def test_e8m0_all_bytes_vs_torch():
+    """Every E8M0 byte against torch's float8_e8m0fnu conversion (a library
+    routine written from the same OCP definition)."""
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).float().double().numpy()
+    got = formats.e8m0_to_f64(b)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[:255], ref[:255])
+
+
 def test_mxfp4_hand_built_record():
     """A record written byte by byte: nibble order, block scales and sections."""
     H, I = 64, 32                       # W13 [64][64], W_d [64][32]
