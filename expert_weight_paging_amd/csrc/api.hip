@@ -82,6 +82,7 @@ struct moe_plan {
   uint16_t* hb;       // GEMM scratch (h high part)
   uint16_t* hb_lo;    // GEMM scratch (h low part)
   float* y;           // GEMM scratch
+  uint8_t* wdq;       // GEMM scratch, quantised formats: the wave's records as bf16
   int gemv_pairs;     // capacity of h in pairs
   hipEvent_t ev_consumed;
   bool consumed_recorded;
@@ -202,7 +203,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res = nullptr,
-                   const int32_t* n_dev = nullptr);
+                   const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr);
 
 moe_status self_check(moe_layer* L);
 
@@ -379,9 +380,10 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   *out = nullptr;
   if (max_tokens < 1) return fail(MOE_ERR_INVALID_ARG, "max_tokens must be >= 1");
   const bool gemm = max_tokens > MOE_MAX_GEMV_TOKENS;
-  if (gemm && (L->fmt != MOE_FMT_BF16 || !gemm_shape_supported(L->H, L->I)))
+  if (gemm && (L->fmt == MOE_FMT_F32 || !gemm_shape_supported(L->H, L->I)))
     return fail(MOE_ERR_INVALID_ARG,
-                "more than 64 tokens per forward needs a bf16 layer with H and I multiples of 128");
+                "more than 64 tokens per forward needs a bf16, FP8, int4 or MXFP4 layer with H and I "
+                "multiples of 128");
   moe_plan* p = new (std::nothrow) moe_plan();
   if (!p) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
   std::memset(p, 0, sizeof(*p));
@@ -401,10 +403,14 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->gemv_pairs = (int)std::min<size_t>(P, (size_t)MOE_MAX_GEMV_TOKENS * L->k);
   const size_t o_h = take(sizeof(float) * (size_t)p->gemv_pairs * L->I);
   size_t o_hb = 0, o_hl = 0, o_y = 0;
+  size_t o_wq = 0;
   if (gemm) {
     o_hb = take(2 * P * L->I);
     o_hl = take(2 * P * L->I);
     o_y = take(4 * P * L->H);
+    // a wave holds at most min(K, E) experts; each expanded to a bf16 record
+    if (L->fmt != MOE_FMT_BF16)
+      o_wq = take((size_t)std::min(L->K, L->E) * rec_layout(MOE_FMT_BF16, L->H, L->I).stride);
   }
   auto cleanup = [&](moe_status s) {
     moe_plan_destroy(p);
@@ -426,6 +432,7 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->hb = gemm ? (uint16_t*)(b + o_hb) : nullptr;
   p->hb_lo = gemm ? (uint16_t*)(b + o_hl) : nullptr;
   p->y = gemm ? (float*)(b + o_y) : nullptr;
+  p->wdq = (gemm && L->fmt != MOE_FMT_BF16) ? b + o_wq : nullptr;
   const size_t hbytes = sizeof(PlanHdr) + sizeof(int32_t) * (3 * E + 1);
   if (hipHostMalloc((void**)&p->hdr, hbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipHostMalloc plan header"));
@@ -640,17 +647,17 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
   moe_status st;
   if (n_res > 0 && copies_pending) {
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_res, pairs_in(o_lo, n_res), T, x, out,
-                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false);
+                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false, nullptr, nullptr, p->wdq);
     if (st) return st;
     HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo + n_res, n_exp - n_res,
                  pairs_in(o_lo + n_res, n_exp - n_res), T, x, out, w > 0 || !gemm, p->dev.pair_pos,
-                 p->dev.wave_of, w, T, /*combine=*/gemm, x_res);
+                 p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
     if (st) return st;
   } else {
     if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, pairs_in(o_lo, n_exp), T, x, out,
-                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res);
+                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
     if (st) return st;
   }
   HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
@@ -989,7 +996,8 @@ namespace {
 moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uint16_t* hb_lo,
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
-                   int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev) {
+                   int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev,
+                   uint8_t* wdq) {
   FfnArgs a{};
   a.n_dev = n_dev;
   a.fmt = L->fmt;
@@ -1038,6 +1046,13 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     timer_push(L, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn);
   } else {
     TimerRec t1{}, t2{}, t3{};
+    if (L->fmt != MOE_FMT_BF16) {  // quantised experts: expand the wave's records to bf16 first
+      if (!wdq) return fail(MOE_ERR_STATE, "plan has no dequantisation scratch");
+      const size_t ws = rec_layout(MOE_FMT_BF16, L->H, L->I).stride;
+      HIP_TRY(launch_dequant_bf16(a, wdq, ws, L->compute));
+      a.wbase = wdq;
+      a.wstride = ws;
+    }
     if ((st = timer_events(L, &t1)) || (st = timer_events(L, &t2))) return st;
     a.ev0 = t1.a;
     a.ev1 = t1.b;

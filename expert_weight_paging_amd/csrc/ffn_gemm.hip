@@ -316,7 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
   if (M <= 0) return;  // uniform over the workgroup
   const int H = a.H, I = a.I;
   const int KD = UP ? H : I;
-  const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
+  // bf16 records: the slot itself, or (quantised formats) the dequantised copy
+  const uint8_t* rec = a.wbase ? a.wbase + (size_t)(o - a.o_lo) * a.wstride
+                               : a.slots + (size_t)a.order_slot[o] * a.stride;
   const uint16_t* W = (const uint16_t*)(rec + (UP ? (size_t)0 : (size_t)2 * I * H * 2));
   const int col0 = tile * (UP ? UP_HCOLS : DN_COLS);
   // weight copy sources: chunk p = i * 512 + tid of the weight tile is tile row

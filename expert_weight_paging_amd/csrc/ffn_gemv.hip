@@ -623,6 +623,67 @@ hipError_t down_dispatch(const FfnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ dequant
+// Prefill with quantised experts: the wave's records are expanded once into
+// bf16 records (the bf16 format's layout) that the grouped MFMA GEMMs read.
+// Each thread writes 8 consecutive bf16 values of one row (16 bytes), the
+// dequantised weight rounded to nearest even; the formats' decodings are
+// those of the GEMV kernels above.
+template <int F>
+__device__ inline void decode8(const uint8_t* rec, const RecLayout& L, bool up, int r, int c, int H, int I,
+                               float* v) {
+  const int cols = up ? H : I;
+  if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+    const uint2 q = *(const uint2*)(rec + (up ? L.w13 : L.wd) + (size_t)r * cols + (size_t)c * 8);
+    const float s = ((const float*)(rec + (up ? L.s13 : L.sd)))[(r / 128) * (cols / 128) + (c * 8) / 128];
+    const f32x2 a = fp8x2<false>(q.x), b = fp8x2<true>(q.x), d = fp8x2<false>(q.y), e = fp8x2<true>(q.y);
+    v[0] = a.x * s; v[1] = a.y * s; v[2] = b.x * s; v[3] = b.y * s;
+    v[4] = d.x * s; v[5] = d.y * s; v[6] = e.x * s; v[7] = e.y * s;
+  } else {
+    const uint32_t w = *(const uint32_t*)(rec + (up ? L.w13 : L.wd) + (size_t)r * (cols / 2) + (size_t)c * 4);
+    if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+      const size_t g = (size_t)r * (cols / 128) + (c * 8) / 128;
+      const float s = half_to_float(((const uint16_t*)(rec + (up ? L.s13 : L.sd)))[g]);
+      const float z = half_to_float(((const uint16_t*)(rec + (up ? L.z13 : L.zd)))[g]);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) v[n] = ((float)((w >> (4 * n)) & 0xFu) - z) * s;
+    } else {  // MXFP4
+      const float s = e8m0_to_float((rec + (up ? L.s13 : L.sd))[(size_t)r * (cols / 32) + (c * 8) / 32]);
+      uint32_t ev, od;
+      e2m1x8_to_e4m3(w, &ev, &od);
+      const f32x2 a = fp8x2<false>(ev), b = fp8x2<true>(ev), d = fp8x2<false>(od), e = fp8x2<true>(od);
+      v[0] = a.x * s; v[1] = d.x * s; v[2] = a.y * s; v[3] = d.y * s;
+      v[4] = b.x * s; v[5] = e.x * s; v[6] = b.y * s; v[7] = e.y * s;
+    }
+  }
+}
+
+constexpr int kDqBlocks = 64;  // workgroups per expert (grid-stride over its rows)
+
+template <int F>
+__global__ __launch_bounds__(256) void dequant_bf16_kernel(FfnArgs a, uint8_t* dst, size_t dst_stride) {
+  const int o = a.o_lo + blockIdx.y;
+  const int H = a.H, I = a.I;
+  const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
+  uint16_t* out = (uint16_t*)(dst + (size_t)blockIdx.y * dst_stride);
+  const RecLayout L = rec_layout(F, H, I);
+  const size_t n13 = (size_t)2 * I * (H / 8), n = n13 + (size_t)H * (I / 8);
+  for (size_t w = (size_t)blockIdx.x * 256 + threadIdx.x; w < n; w += (size_t)gridDim.x * 256) {
+    const bool up = w < n13;
+    const size_t ww = up ? w : w - n13;
+    const int cpr = (up ? H : I) / 8;  // 8-value chunks per row
+    const int r = (int)(ww / cpr), c = (int)(ww % cpr);
+    float v[8];
+    decode8<F>(rec, L, up, r, c, H, I, v);
+    uint4 q;
+    q.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    q.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    q.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+    q.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+    *(uint4*)(out + (up ? (size_t)0 : (size_t)2 * I * H) + (size_t)r * (up ? H : I) + (size_t)c * 8) = q;
+  }
+}
+
 int nj_of(int n) {
   const int nj = (n + kWave - 1) / kWave;
   return (nj == 1 || nj == 2 || nj == 3 || nj == 4 || nj == 6 || nj == 8) ? nj : 0;
@@ -659,6 +720,18 @@ hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s) {
     case MOE_FMT_MXFP4_B32: return up_dispatch<MOE_FMT_MXFP4_B32, uint16_t>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequant_bf16(const FfnArgs& a, uint8_t* dst, size_t dst_stride, hipStream_t s) {
+  if (a.n_exp <= 0) return hipSuccess;
+  const dim3 grid(kDqBlocks, a.n_exp), block(256);
+  switch (a.fmt) {
+    case MOE_FMT_FP8_E4M3_B128: launch_k(dequant_bf16_kernel<MOE_FMT_FP8_E4M3_B128>, grid, block, s, a.ev0, a.ev1, a, dst, dst_stride); break;
+    case MOE_FMT_INT4_ASYM_G128: launch_k(dequant_bf16_kernel<MOE_FMT_INT4_ASYM_G128>, grid, block, s, a.ev0, a.ev1, a, dst, dst_stride); break;
+    case MOE_FMT_MXFP4_B32: launch_k(dequant_bf16_kernel<MOE_FMT_MXFP4_B32>, grid, block, s, a.ev0, a.ev1, a, dst, dst_stride); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s) {

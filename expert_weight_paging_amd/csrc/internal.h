@@ -160,12 +160,20 @@ struct FfnArgs {
                        // read on the device; n_exp is then only an upper bound
   uint16_t* x_res;     // optional: the launch that completes out also applies the
                        // stack residual x_res = bf16_rne(x_res + out), bf16 [T][H]
+  // optional (GEMM path, quantised formats): the wave's records dequantised to
+  // the bf16 record layout, expert o at wbase + (o - o_lo) * wstride
+  const uint8_t* wbase;
+  size_t wstride;
   hipEvent_t ev0, ev1; // optional timing events for the next launch
 };
 
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);
 bool ffn_shape_supported(int fmt, int H, int I);
+
+// Expands the records of wave-order positions [o_lo, o_lo + n_exp) from the
+// layer's format into bf16 records (rec_layout(BF16)) at dst + p * dst_stride.
+hipError_t launch_dequant_bf16(const FfnArgs& a, uint8_t* dst, size_t dst_stride, hipStream_t s);
 
 hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s);

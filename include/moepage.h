@@ -89,7 +89,7 @@ typedef enum moe_format {
 /* Limits of this implementation (checked at init). */
 #define MOE_MAX_EXPERTS 1024        /* E                                      */
 #define MOE_MAX_TOP_K 32            /* top_k                                  */
-#define MOE_MAX_GEMV_TOKENS 64      /* tokens per forward for non-bf16 formats */
+#define MOE_MAX_GEMV_TOKENS 64      /* tokens per forward on the GEMV path (f32: the limit) */
 
 /* Record stride in bytes for a format and shape, or 0 if unsupported. */
 size_t moe_record_bytes(int32_t format, int32_t hidden, int32_t intermediate);
@@ -172,7 +172,11 @@ void moe_layer_destroy(moe_layer* layer);
 
 /* Create a plan for up to max_tokens tokens per route call with this layer.
  * Allocates small device arrays (ids, weights, slot map, grouping), the
- * pinned host-visible plan and the FFN workspace. */
+ * pinned host-visible plan and the FFN workspace; with max_tokens above
+ * MOE_MAX_GEMV_TOKENS the GEMM workspace too (for FP8, int4 and MXFP4 layers
+ * it includes min(K, E) bf16 records, 6 * H * I bytes each). Errors:
+ * MOE_ERR_INVALID_ARG (max_tokens < 1; more than MOE_MAX_GEMV_TOKENS tokens
+ * on an f32 layer or with H or I not a multiple of 128), MOE_ERR_HIP. */
 moe_status moe_plan_create(const moe_layer* layer, int32_t max_tokens, moe_plan** out);
 void moe_plan_destroy(moe_plan* plan);
 
@@ -232,8 +236,10 @@ moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
  *   out: device, float32 [T][H]; wave 0 writes it, later waves add to it
  * out[t] = sum over (t, j) in this wave of w_tj * W_d (SiLU(W_gate x_t) *
  * (W_up x_t)), reading each expert from its slot. For T <= MOE_MAX_GEMV_TOKENS
- * the weights are streamed once per wave (GEMV path); bf16 layers with more
- * tokens use the token-grouped MFMA GEMM. */
+ * the weights are streamed once per wave (GEMV path); with more tokens the
+ * token-grouped bf16 MFMA GEMM runs (H and I multiples of 128): FP8, int4 and
+ * MXFP4 records are first expanded to bf16 in the plan's workspace (each
+ * weight rounded to nearest even), f32 layers are limited to the GEMV path. */
 moe_status moe_forward(moe_layer* layer, const moe_plan* plan, int32_t wave,
                        const void* x, float* out);
 

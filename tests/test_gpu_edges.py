@@ -165,6 +165,9 @@ def test_error_codes():
     assert st == 0
     layer = ewp.Layer.__new__(ewp.Layer)
     layer.handle, layer.top_k, layer.E, layer.K = h, 2, E, K
+    with pytest.raises(ewp.MoeError) as ei:        # f32 layers stay on the GEMV path (<= 64 tokens)
+        ewp.Plan(layer, 65)
+    assert ei.value.name == "MOE_ERR_INVALID_ARG"
     plan = ewp.Plan(layer, 2)
     x = torch.zeros(2, H, device="cuda")
     out = torch.zeros(2, H, device="cuda")

@@ -9,7 +9,7 @@ import workloads as W
 from oracle.layer import PagedLayer, bf16_rne, run_stack
 from workloads import gen
 
-from gpu_harness import PairedLayer, rel_err, say, x_values
+from gpu_harness import TOL, PairedLayer, rel_err, say, x_values
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,42 @@ def test_prefill_qwen_layer_2048_tokens():
     logits, x0 = gen.prefill_inputs(cfg, layers=1)
     info = _prefill_layer_check(p, logits[0], x0)
     assert info["num_waves"] == 2 and info["num_misses"] == 36
+    p.close()
+
+
+@pytest.mark.parametrize("fmt", [gen.FP8, gen.INT4, gen.MXFP4])
+def test_prefill_quantised_formats(fmt):
+    """More than 64 tokens with FP8, int4 and MXFP4 experts: the wave's records
+    are expanded to bf16 and run through the MFMA GEMMs (two waves per step)."""
+    T, E, k, H, I, K = 300, 16, 2, 256, 384, 12
+    say("case: prefill %s T=%d E=%d k=%d H=%d I=%d K=%d" % ({gen.FP8: "fp8", gen.INT4: "int4", gen.MXFP4: "mxfp4"}[fmt], T, E, k, H, I, K))
+    rng = np.random.default_rng(40 + fmt)
+    recs = [gen.encode_record(fmt, (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32),
+                              (rng.standard_normal((H, I)) * 0.02).astype(np.float32)) for _ in range(E)]
+
+    def fill(a):
+        for e in range(E):
+            a[e] = recs[e]
+    p = PairedLayer(E, k, H, I, K, fmt, fill, max_tokens=T)
+    for step in range(2):
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        x = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        info = _prefill_layer_check(p, logits, x, tol=TOL[fmt])
+        assert info["num_waves"] == 2
+    p.close()
+
+
+def test_prefill_mxfp4_qwen_layer_2048_tokens():
+    cfg = W.CONFIGS[6]
+    K = 92
+    say("case: prefill mxfp4 layer E=128 k=8 H=2048 I=768 K=92 warm, 2048 tokens")
+    p = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt,
+                    lambda a: gen.expert_store(cfg, out=a), max_tokens=2048, initial_fill=True)
+    rng = np.random.default_rng(2048)
+    logits = rng.standard_normal((2048, cfg.E)).astype(np.float32)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((2048, cfg.H)).astype(np.float32))
+    info = _prefill_layer_check(p, logits, x, tol=TOL[cfg.fmt])
+    assert info["num_waves"] == 2
     p.close()
 
 
