@@ -331,6 +331,41 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ id
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
+// Grouping of a small step: wavefront w collects the pairs of order positions
+// w, w + NWV, ... by ballots over the step's ids (in LDS), ascending, at the
+// CSR offsets the plan left in sm.cnt (indexed by order position).
+template <int NWV>
+__device__ inline void group_small(const PlanSmem& sm, const int32_t* s_ids, int P, int D, const PlanDev& dev) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int i = wid; i < D; i += NWV) {
+    const int e = sm.order_e[i];
+    const int base = sm.cnt[i];
+    int running = 0;
+    for (int c = 0; c < P; c += kWave) {
+      const int p = c + lane;
+      const bool m = p < P && s_ids[p] == e;
+      const unsigned long long mask = __ballot(m);
+      if (m) {
+        const int q = base + running + __popcll(mask & below);
+        dev.pair_list[q] = p;
+        dev.pair_pos[p] = q;
+      }
+      running += __popcll(mask);
+    }
+  }
+}
+
+// Device-resolved steps: accumulate the step counters (steps, distinct
+// experts, activations, hits, misses, waves) by no-return atomic adds.
+__device__ inline void add_dstats(long long* dstats, int T, int P, int D, int nH, int nw) {
+  if (dstats && threadIdx.x < 6 && T > 0) {
+    const long long v[6] = {1, D, P, nH, D - nH, nw};
+    __hip_atomic_fetch_add(dstats + threadIdx.x, v[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Decode-sized steps (T <= 64, T * k <= kSmallPairs): router, slot plan and
 // grouping in one workgroup, one launch.
 constexpr int kSmallPairs = 2048;
@@ -367,28 +402,313 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
   for (int p = threadIdx.x; p < P; p += NT) dev.ids[p] = s_ids[p];
   int D, nH, nw;
   plan_body<NT>(s_ids, P, T, E, K, state, sl, pre, dev, sm, &D, &nH, &nw);
-  // grouping: wavefront w collects the pairs of order positions w, w+NWV, ...
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int i = wid; i < D; i += NWV) {
-    const int e = sm.order_e[i];
-    const int base = sm.cnt[i];
-    int running = 0;
-    for (int c = 0; c < P; c += kWave) {
-      const int p = c + lane;
-      const bool m = p < P && s_ids[p] == e;
-      const unsigned long long mask = __ballot(m);
-      if (m) {
-        const int q = base + running + __popcll(mask & below);
-        dev.pair_list[q] = p;
-        dev.pair_pos[p] = q;
-      }
-      running += __popcll(mask);
+  group_small<NWV>(sm, s_ids, P, D, dev);
+  add_dstats(dstats, T, P, D, nH, nw);
+  publish(sm, E, T, P, D, nH, nw, hdr, seq);
+}
+
+// ------------------------------------------------------------------ small steps, one planning wavefront
+// The same router, plan and grouping as route_plan_small_kernel, for tables of
+// E <= 64 * NJ experts (so K <= E slots fit 64 * NJ too). The plan is the
+// serial part of a decode step, so it runs in wavefront 0 alone: lane l owns
+// experts l + 64 j and slots l + 64 j, hit and miss ranks come from ballots
+// and population counts, the CSR offsets from a wavefront scan, and the only
+// synchronisation inside the plan is between the lanes of one wavefront.
+// The other wavefronts route tokens before it and group pairs after it.
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// One token routed by all NWV wavefronts (single-token steps): each
+// wavefront ranks the token's packed logits against one NWV-th of them, the
+// partial ranks meet in LDS, and wavefront 0 lists the selection and computes
+// the weights exactly as route_token does.
+template <int NJ, int NWV>
+__device__ inline void route_token_split(const float* __restrict__ z, int E, int k, int lane, int wid,
+                                         unsigned long long* pk, int* rank_part, float* zs,
+                                         int32_t* ids_out, float* w_out) {
+  unsigned long long mine[NJ];
+  float zv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    zv[j] = 0.f;
+    mine[j] = ~0ull;
+    if (e < E) {
+      zv[j] = z[e];
+      mine[j] = pack_logit(zv[j], e);
+      if (wid == 0) pk[e] = mine[j];
     }
   }
-  if (dstats && threadIdx.x < 6 && T > 0) {  // no-return atomic adds: no read round trip
-    const long long v[6] = {1, D, P, nH, D - nH, nw};
-    __hip_atomic_fetch_add(dstats + threadIdx.x, v[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((E & 1) && wid == 0 && lane == 0) pk[E] = 0ull;
+  __syncthreads();
+  const int n2 = (E + 1) >> 1;
+  const int per = (n2 + NWV - 1) / NWV;
+  const int u0 = wid * per, u1 = min(n2, u0 + per);
+  int rank[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rank[j] = 0;
+  const ulonglong2* pk2 = (const ulonglong2*)pk;
+#pragma unroll 4
+  for (int u = u0; u < u1; ++u) {
+    const ulonglong2 v = pk2[u];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) rank[j] += (v.x > mine[j] ? 1 : 0) + (v.y > mine[j] ? 1 : 0);
   }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E) rank_part[wid * (kWave * NJ) + e] = rank[j];
+  }
+  __syncthreads();
+  if (wid != 0) return;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E) {
+      int r = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) r += rank_part[w * (kWave * NJ) + e];
+      if (r < k) {
+        ids_out[r] = e;
+        zs[r] = zv[j];
+      }
+    }
+  }
+  wave_lds_sync();
+  const float zr = lane < k ? zs[lane] : 0.f;
+  const float zmax = zs[0];
+  const float ex = lane < k ? __expf(zr - zmax) : 0.f;
+  const float sum = wave_sum(ex);
+  if (lane < k) w_out[lane] = ex / sum;
+  wave_lds_sync();
+}
+
+// The table state a planning lane owns, loaded at kernel start.
+template <int NJ>
+struct LaneState {
+  int expert_slot[NJ], slot_expert[NJ];
+  long long stamp[NJ], clock;
+};
+
+template <int NJ>
+__device__ inline LaneState<NJ> load_lane_state(const uint8_t* state, const StateLayout& sl, int E, int K) {
+  const int lane = threadIdx.x & (kWave - 1);
+  LaneState<NJ> r;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    r.expert_slot[j] = i < E ? ((const int32_t*)(state + sl.expert_slot))[i] : -1;
+    r.slot_expert[j] = i < K ? ((const int32_t*)(state + sl.slot_expert))[i] : -1;
+    r.stamp[j] = i < K ? ((const long long*)(state + sl.stamp))[i] : 0;
+  }
+  r.clock = *(const long long*)(state + sl.clock);
+  return r;
+}
+
+// The slot plan of plan_body, run by one wavefront (wavefront 0). ids: the
+// step's P routed ids in LDS. Leaves in LDS what the grouping and the publish
+// read: order_e / order_s by wave-order position, pos by expert, cnt by
+// position (CSR offsets), and D, nH, n_waves in warp[0..2].
+template <int NJ>
+__device__ void plan_wave(const int32_t* ids, int P, int T, int E, int K, uint8_t* state,
+                          const StateLayout& sl, const LaneState<NJ>& pre, const PlanDev& dev,
+                          PlanSmem& sm) {
+  int32_t* g_slot_expert = (int32_t*)(state + sl.slot_expert);
+  int32_t* g_expert_slot = (int32_t*)(state + sl.expert_slot);
+  long long* g_stamp = (long long*)(state + sl.stamp);
+  long long* g_clock = (long long*)(state + sl.clock);
+  const int lane = threadIdx.x & (kWave - 1);
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    if (i < E) {
+      sm.cnt[i] = 0;
+      sm.expert_slot[i] = pre.expert_slot[j];
+    }
+    if (i < K) {
+      sm.slot_expert[i] = pre.slot_expert[j];
+      sm.stamp[i] = pre.stamp[j];
+    }
+  }
+  wave_lds_sync();
+  for (int p = lane; p < P; p += kWave) atomicAdd(&sm.cnt[ids[p]], 1);
+  wave_lds_sync();
+
+  // referenced experts: residents (hits) first, then missing ones, each ascending
+  unsigned long long hm[NJ], mm[NJ];
+  int nH = 0, nM = 0, hb[NJ], mb[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    const bool ref = e < E && sm.cnt[e] > 0;
+    const bool hit = ref && pre.expert_slot[j] >= 0;
+    hm[j] = __ballot(hit);
+    mm[j] = __ballot(ref && !hit);
+    hb[j] = nH;
+    mb[j] = nM;
+    nH += __popcll(hm[j]);
+    nM += __popcll(mm[j]);
+  }
+  const int D = nH + nM;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + kWave * j;
+    const bool hit = (hm[j] >> lane) & 1, miss = (mm[j] >> lane) & 1;
+    const int pos = hit ? hb[j] + __popcll(hm[j] & below)
+                        : (miss ? nH + mb[j] + __popcll(mm[j] & below) : -1);
+    if (e < E) sm.pos[e] = pos;
+    if (pos >= 0) sm.order_e[pos] = e;
+  }
+  const int n_waves = (D + K - 1) / K;
+  long long clock = pre.clock;
+  wave_lds_sync();
+
+  for (int w = 0; w < n_waves; ++w) {
+    clock += 1;
+    const int lo = w * K;
+    const int hi = min(lo + K, D);
+    const int m_lo = max(lo, nH);
+    const int nm = hi - m_lo;
+    unsigned long long key[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int s = lane + kWave * j;
+      key[j] = ~0ull;
+      if (s < K) {
+        const int e = sm.slot_expert[s];
+        const bool prot = e >= 0 && sm.pos[e] >= lo && sm.pos[e] < hi;
+        key[j] = victim_key(sm.stamp[s], s, prot);
+        sm.vkey[s] = key[j];
+      }
+    }
+    if ((K & 1) && lane == 0) sm.vkey[K] = ~0ull;  // pads the pairwise reads; never below a key
+    wave_lds_sync();
+    if (nm > 0) {
+      int rank[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) rank[j] = 0;
+      const ulonglong2* v2 = (const ulonglong2*)sm.vkey;
+      const int n2 = (K + 1) >> 1;
+#pragma unroll 4
+      for (int u = 0; u < n2; ++u) {
+        const ulonglong2 v = v2[u];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) rank[j] += (v.x < key[j] ? 1 : 0) + (v.y < key[j] ? 1 : 0);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int s = lane + kWave * j;
+        if (s < K && key[j] != ~0ull && rank[j] < nm) {
+          const int e_new = sm.order_e[m_lo + rank[j]];
+          const int old = sm.slot_expert[s];
+          if (old >= 0) sm.expert_slot[old] = -1;
+          sm.slot_expert[s] = e_new;
+          sm.expert_slot[e_new] = s;
+          sm.order_s[m_lo + rank[j]] = s;
+        }
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = lane + kWave * j;
+      if (i >= lo && i < min(hi, nH)) sm.order_s[i] = sm.expert_slot[sm.order_e[i]];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = lane + kWave * j;
+      if (i >= lo && i < hi) sm.stamp[sm.order_s[i]] = clock;
+    }
+    wave_lds_sync();
+  }
+
+  // table state back to HBM; wave order, CSR offsets over it, counters
+  int carry = 0, off[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    if (i < E) g_expert_slot[i] = sm.expert_slot[i];
+    if (i < K) {
+      g_slot_expert[i] = sm.slot_expert[i];
+      g_stamp[i] = sm.stamp[i];
+    }
+    const int c = i < D ? sm.cnt[sm.order_e[i]] : 0;
+    const int inc = wave_incl_scan(c);
+    off[j] = carry + inc - c;
+    carry += __shfl(inc, kWave - 1, kWave);
+    if (i < E) dev.pair_off[i] = i < D ? off[j] : P;
+    if (i < D) {
+      dev.order_expert[i] = sm.order_e[i];
+      dev.order_slot[i] = sm.order_s[i];
+    }
+  }
+  if (lane == 0) {
+    *g_clock = clock;
+    dev.pair_off[E] = P;
+    dev.counts[0] = D;
+    dev.counts[1] = nH;
+    dev.counts[2] = n_waves;
+    dev.counts[3] = T;
+    sm.warp[0] = D;
+    sm.warp[1] = nH;
+    sm.warp[2] = n_waves;
+  }
+  wave_lds_sync();  // every lane has read cnt by expert before it is rewritten by position
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    if (i < D) sm.cnt[i] = off[j];
+  }
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int k, int K, uint8_t* state, StateLayout sl,
+                                                              PlanDev dev, PlanHdr* hdr, int32_t seq,
+                                                              long long* dstats) {
+  constexpr int NT = 256, NWV = NT / kWave;
+  __shared__ PlanSmem sm;
+  __shared__ int32_t s_ids[kSmallPairs];
+  __shared__ float s_z[NWV][MOE_MAX_TOP_K];
+  __shared__ int s_rank[NWV * kWave * NJ];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int P = T * k;
+  LaneState<NJ> pre;
+  if (wid == 0) pre = load_lane_state<NJ>(state, sl, E, K);
+  // the router's per-token LDS borrows the victim-key array (unused until the plan)
+  if (T == 1) {
+    route_token_split<NJ, NWV>(logits, E, k, lane, wid, sm.vkey, s_rank, s_z[0], s_ids, dev.weights);
+  } else {
+    for (int t = wid; t < T; t += NWV)
+      route_token<NJ>(logits + (size_t)t * E, E, k, lane, sm.vkey + wid * (kWave * NJ), s_z[wid],
+                      s_ids + t * k, dev.weights + (size_t)t * k);
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < P; p += NT) dev.ids[p] = s_ids[p];
+  if (wid == 0) plan_wave<NJ>(s_ids, P, T, E, K, state, sl, pre, dev, sm);
+  __syncthreads();
+  const int D = sm.warp[0], nH = sm.warp[1], nw = sm.warp[2];
+  // per-pair slot and wave
+  for (int p = threadIdx.x; p < P; p += NT) {
+    const int pos = sm.pos[s_ids[p]];
+    dev.slot_ids[p] = sm.order_s[pos];
+    dev.wave_of[p] = pos / K;
+  }
+  group_small<NWV>(sm, s_ids, P, D, dev);
+  add_dstats(dstats, T, P, D, nH, nw);
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
@@ -496,12 +816,16 @@ hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int
 #define MOE_SMALL(NT, NJ)                                                                   \
   launch_k(route_plan_small_kernel<NT, NJ>, dim3(1), dim3(NT), s, ev0, ev1, logits, T, E, k, K, st, \
            sl, dev, host_hdr_dev, seq, dstats)
-  if (E <= 64) MOE_SMALL(256, 1);
-  else if (E <= 128) MOE_SMALL(256, 2);
-  else if (E <= 256) MOE_SMALL(256, 4);
+#define MOE_WAVE(NJ)                                                                         \
+  launch_k(route_plan_wave_kernel<NJ>, dim3(1), dim3(256), s, ev0, ev1, logits, T, E, k, K, st, sl, dev, \
+           host_hdr_dev, seq, dstats)
+  if (E <= 64) MOE_WAVE(1);
+  else if (E <= 128) MOE_WAVE(2);
+  else if (E <= 256) MOE_WAVE(4);
   else if (E <= 512) MOE_SMALL(1024, 8);
   else MOE_SMALL(1024, 16);
 #undef MOE_SMALL
+#undef MOE_WAVE
   return hipGetLastError();
 }
 
