@@ -34,6 +34,14 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS only: this wavefront's LDS accesses are
+// complete, then every wavefront has arrived. Unlike __syncthreads it does not
+// wait for outstanding global stores, which no wavefront of the workgroup
+// reads back.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
 // ------------------------------------------------------------------ router
 // One wavefront per token ([PE] "What does Paged Experts actually do?": each
 // token goes to top_k of E experts). Every logit's rank is the number of
@@ -49,15 +57,19 @@ __device__ inline void route_token(const float* __restrict__ z, int E, int k, in
                                    float* w_out) {
   unsigned long long mine[NJ];
   float zv[NJ];
+  // every load issued before any is used (indices clamped in range, the
+  // lanes past E discard theirs)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) zv[j] = z[min(lane + kWave * j, E - 1)];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + kWave * j;
-    zv[j] = 0.f;
     mine[j] = ~0ull;
     if (e < E) {
-      zv[j] = z[e];
       mine[j] = pack_logit(zv[j], e);
       pk[e] = mine[j];
+    } else {
+      zv[j] = 0.f;
     }
   }
   // a zero entry is below every packed logit, so it pads E to even harmlessly
@@ -158,6 +170,7 @@ struct PlanSmem {
   int expert_slot[MOE_MAX_EXPERTS];
   long long stamp[MOE_MAX_EXPERTS];
   __attribute__((aligned(16))) unsigned long long vkey[MOE_MAX_EXPERTS];
+  int cpos[MOE_MAX_EXPERTS];  // routed pairs of each wave-order position (one-wavefront plan)
   int warp[MOE_MAX_EXPERTS / kWave + 1];
 };
 
@@ -331,15 +344,17 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ id
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
-// Grouping of a small step: wavefront w collects the pairs of order positions
-// w, w + NWV, ... by ballots over the step's ids (in LDS), ascending, at the
+// Grouping of a small step: wavefronts W0 .. NWV-1 take the order positions
+// round robin (wavefront W0 + r takes r, r + NWV - W0, ...) and collect each
+// position's pairs by ballots over the step's ids (in LDS), ascending, at the
 // CSR offsets the plan left in sm.cnt (indexed by order position).
-template <int NWV>
+template <int NWV, int W0>
 __device__ inline void group_small(const PlanSmem& sm, const int32_t* s_ids, int P, int D, const PlanDev& dev) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int i = wid; i < D; i += NWV) {
+  if (wid < W0) return;
+  for (int i = wid - W0; i < D; i += NWV - W0) {
     const int e = sm.order_e[i];
     const int base = sm.cnt[i];
     int running = 0;
@@ -359,10 +374,12 @@ __device__ inline void group_small(const PlanSmem& sm, const int32_t* s_ids, int
 
 // Device-resolved steps: accumulate the step counters (steps, distinct
 // experts, activations, hits, misses, waves) by no-return atomic adds.
-__device__ inline void add_dstats(long long* dstats, int T, int P, int D, int nH, int nw) {
-  if (dstats && threadIdx.x < 6 && T > 0) {
+// Threads t0 .. t0 + 5 issue the six adds.
+__device__ inline void add_dstats(long long* dstats, int T, int P, int D, int nH, int nw, int t0) {
+  const int t = (int)threadIdx.x - t0;
+  if (dstats && t >= 0 && t < 6 && T > 0) {
     const long long v[6] = {1, D, P, nH, D - nH, nw};
-    __hip_atomic_fetch_add(dstats + threadIdx.x, v[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(dstats + t, v[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -402,8 +419,8 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
   for (int p = threadIdx.x; p < P; p += NT) dev.ids[p] = s_ids[p];
   int D, nH, nw;
   plan_body<NT>(s_ids, P, T, E, K, state, sl, pre, dev, sm, &D, &nH, &nw);
-  group_small<NWV>(sm, s_ids, P, D, dev);
-  add_dstats(dstats, T, P, D, nH, nw);
+  group_small<NWV, 0>(sm, s_ids, P, D, dev);
+  add_dstats(dstats, T, P, D, nH, nw, 0);
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
@@ -438,18 +455,20 @@ __device__ inline void route_token_split(const float* __restrict__ z, int E, int
   unsigned long long mine[NJ];
   float zv[NJ];
 #pragma unroll
+  for (int j = 0; j < NJ; ++j) zv[j] = z[min(lane + kWave * j, E - 1)];
+#pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + kWave * j;
-    zv[j] = 0.f;
     mine[j] = ~0ull;
     if (e < E) {
-      zv[j] = z[e];
       mine[j] = pack_logit(zv[j], e);
       if (wid == 0) pk[e] = mine[j];
+    } else {
+      zv[j] = 0.f;
     }
   }
   if ((E & 1) && wid == 0 && lane == 0) pk[E] = 0ull;
-  __syncthreads();
+  lds_barrier();
   const int n2 = (E + 1) >> 1;
   const int per = (n2 + NWV - 1) / NWV;
   const int u0 = wid * per, u1 = min(n2, u0 + per);
@@ -468,7 +487,7 @@ __device__ inline void route_token_split(const float* __restrict__ z, int E, int
     const int e = lane + kWave * j;
     if (e < E) rank_part[wid * (kWave * NJ) + e] = rank[j];
   }
-  __syncthreads();
+  lds_barrier();
   if (wid != 0) return;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -517,44 +536,59 @@ __device__ inline LaneState<NJ> load_lane_state(const uint8_t* state, const Stat
 // The slot plan of plan_body, run by one wavefront (wavefront 0). ids: the
 // step's P routed ids in LDS. Leaves in LDS what the grouping and the publish
 // read: order_e / order_s by wave-order position, pos by expert, cnt by
-// position (CSR offsets), and D, nH, n_waves in warp[0..2].
+// position (CSR offsets), and D, nH, n_waves in warp[0..2]; the table state
+// and offsets for the stores in `out`. It issues no global memory access.
+// Each lane keeps its slots' expert and stamp in registers. Two facts of the
+// plan keep the LDS traffic small: the slots a wave protects are, in wave 0,
+// exactly the slots of the hits (every hit is in wave 0 and no miss is resident
+// when its wave starts) and, in later waves, none; and a hit keeps the slot it
+// had at the start of the step during wave 0.
+// What plan_wave leaves in registers for plan_wave_store.
 template <int NJ>
-__device__ void plan_wave(const int32_t* ids, int P, int T, int E, int K, uint8_t* state,
-                          const StateLayout& sl, const LaneState<NJ>& pre, const PlanDev& dev,
-                          PlanSmem& sm) {
-  int32_t* g_slot_expert = (int32_t*)(state + sl.slot_expert);
-  int32_t* g_expert_slot = (int32_t*)(state + sl.expert_slot);
-  long long* g_stamp = (long long*)(state + sl.stamp);
-  long long* g_clock = (long long*)(state + sl.clock);
+struct PlanOut {
+  int se[NJ], off[NJ];
+  long long st[NJ], clock;
+};
+
+template <int NJ>
+__device__ void plan_wave(const int32_t* ids, int P, int E, int K, const LaneState<NJ>& pre,
+                          PlanSmem& sm, PlanOut<NJ>& out) {
   const int lane = threadIdx.x & (kWave - 1);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-
+  int se[NJ];
+  long long st[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int i = lane + kWave * j;
+    se[j] = pre.slot_expert[j];
+    st[j] = pre.stamp[j];
     if (i < E) {
       sm.cnt[i] = 0;
       sm.expert_slot[i] = pre.expert_slot[j];
-    }
-    if (i < K) {
-      sm.slot_expert[i] = pre.slot_expert[j];
-      sm.stamp[i] = pre.stamp[j];
     }
   }
   wave_lds_sync();
   for (int p = lane; p < P; p += kWave) atomicAdd(&sm.cnt[ids[p]], 1);
   wave_lds_sync();
 
+  // routed count of each owned expert; whether each owned slot holds a routed
+  // (hence hit) expert
+  int c[NJ];
+  bool hit_slot[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    c[j] = i < E ? sm.cnt[i] : 0;
+    hit_slot[j] = i < K && se[j] >= 0 && sm.cnt[se[j]] > 0;
+  }
   // referenced experts: residents (hits) first, then missing ones, each ascending
   unsigned long long hm[NJ], mm[NJ];
   int nH = 0, nM = 0, hb[NJ], mb[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int e = lane + kWave * j;
-    const bool ref = e < E && sm.cnt[e] > 0;
-    const bool hit = ref && pre.expert_slot[j] >= 0;
+    const bool hit = c[j] > 0 && pre.expert_slot[j] >= 0;
     hm[j] = __ballot(hit);
-    mm[j] = __ballot(ref && !hit);
+    mm[j] = __ballot(c[j] > 0 && !hit);
     hb[j] = nH;
     mb[j] = nM;
     nH += __popcll(hm[j]);
@@ -568,7 +602,11 @@ __device__ void plan_wave(const int32_t* ids, int P, int T, int E, int K, uint8_
     const int pos = hit ? hb[j] + __popcll(hm[j] & below)
                         : (miss ? nH + mb[j] + __popcll(mm[j] & below) : -1);
     if (e < E) sm.pos[e] = pos;
-    if (pos >= 0) sm.order_e[pos] = e;
+    if (pos >= 0) {
+      sm.order_e[pos] = e;
+      sm.cpos[pos] = c[j];
+      if (hit) sm.order_s[pos] = pre.expert_slot[j];
+    }
   }
   const int n_waves = (D + K - 1) / K;
   long long clock = pre.clock;
@@ -586,9 +624,8 @@ __device__ void plan_wave(const int32_t* ids, int P, int T, int E, int K, uint8_
       const int s = lane + kWave * j;
       key[j] = ~0ull;
       if (s < K) {
-        const int e = sm.slot_expert[s];
-        const bool prot = e >= 0 && sm.pos[e] >= lo && sm.pos[e] < hi;
-        key[j] = victim_key(sm.stamp[s], s, prot);
+        if (w == 0 && hit_slot[j]) st[j] = clock;  // protected: a hit of this wave
+        else key[j] = victim_key(st[j], s, false);
         sm.vkey[s] = key[j];
       }
     }
@@ -610,66 +647,81 @@ __device__ void plan_wave(const int32_t* ids, int P, int T, int E, int K, uint8_
       for (int j = 0; j < NJ; ++j) {
         const int s = lane + kWave * j;
         if (s < K && key[j] != ~0ull && rank[j] < nm) {
-          const int e_new = sm.order_e[m_lo + rank[j]];
-          const int old = sm.slot_expert[s];
-          if (old >= 0) sm.expert_slot[old] = -1;
-          sm.slot_expert[s] = e_new;
+          const int q = m_lo + rank[j];
+          const int e_new = sm.order_e[q];
+          if (se[j] >= 0) sm.expert_slot[se[j]] = -1;
           sm.expert_slot[e_new] = s;
-          sm.order_s[m_lo + rank[j]] = s;
+          se[j] = e_new;
+          st[j] = clock;
+          sm.order_s[q] = s;
         }
       }
     }
-    wave_lds_sync();
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int i = lane + kWave * j;
-      if (i >= lo && i < min(hi, nH)) sm.order_s[i] = sm.expert_slot[sm.order_e[i]];
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int i = lane + kWave * j;
-      if (i >= lo && i < hi) sm.stamp[sm.order_s[i]] = clock;
-    }
-    wave_lds_sync();
+    wave_lds_sync();  // the next wave rewrites vkey; the write-back reads expert_slot
   }
 
-  // table state back to HBM; wave order, CSR offsets over it, counters
-  int carry = 0, off[NJ];
+  // CSR offsets over the wave order (the stores wait for plan_wave_store)
+  int carry = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    out.off[j] = P;
+    if (kWave * j < D) {  // uniform: positions past D need no scan
+      const int cj = i < D ? sm.cpos[i] : 0;
+      const int inc = wave_incl_scan(cj);
+      out.off[j] = carry + inc - cj;
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+    out.se[j] = se[j];
+    out.st[j] = st[j];
+  }
+  out.clock = clock;
+  if (lane == 0) {
+    sm.warp[0] = D;
+    sm.warp[1] = nH;
+    sm.warp[2] = n_waves;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = lane + kWave * j;
+    if (i < D) sm.cnt[i] = out.off[j];  // from here on: CSR offset of order position i
+  }
+}
+
+// The global stores of plan_wave (same wavefront, after the workgroup has
+// passed the barrier that follows the plan): the table state, the wave order
+// with its slots, the CSR offsets and the counters. Issued together with the
+// per-pair stores of the other wavefronts, so their latencies overlap.
+template <int NJ>
+__device__ void plan_wave_store(const PlanOut<NJ>& out, int P, int T, int E, int K, uint8_t* state,
+                                const StateLayout& sl, const PlanDev& dev, const PlanSmem& sm, int D,
+                                int nH, int n_waves) {
+  int32_t* g_slot_expert = (int32_t*)(state + sl.slot_expert);
+  int32_t* g_expert_slot = (int32_t*)(state + sl.expert_slot);
+  long long* g_stamp = (long long*)(state + sl.stamp);
+  long long* g_clock = (long long*)(state + sl.clock);
+  const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int i = lane + kWave * j;
     if (i < E) g_expert_slot[i] = sm.expert_slot[i];
     if (i < K) {
-      g_slot_expert[i] = sm.slot_expert[i];
-      g_stamp[i] = sm.stamp[i];
+      g_slot_expert[i] = out.se[j];
+      g_stamp[i] = out.st[j];
     }
-    const int c = i < D ? sm.cnt[sm.order_e[i]] : 0;
-    const int inc = wave_incl_scan(c);
-    off[j] = carry + inc - c;
-    carry += __shfl(inc, kWave - 1, kWave);
-    if (i < E) dev.pair_off[i] = i < D ? off[j] : P;
+    if (i < E) dev.pair_off[i] = i < D ? out.off[j] : P;
     if (i < D) {
       dev.order_expert[i] = sm.order_e[i];
       dev.order_slot[i] = sm.order_s[i];
     }
   }
   if (lane == 0) {
-    *g_clock = clock;
+    *g_clock = out.clock;
     dev.pair_off[E] = P;
     dev.counts[0] = D;
     dev.counts[1] = nH;
     dev.counts[2] = n_waves;
     dev.counts[3] = T;
-    sm.warp[0] = D;
-    sm.warp[1] = nH;
-    sm.warp[2] = n_waves;
-  }
-  wave_lds_sync();  // every lane has read cnt by expert before it is rewritten by position
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int i = lane + kWave * j;
-    if (i < D) sm.cnt[i] = off[j];
   }
 }
 
@@ -683,32 +735,43 @@ __global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __res
   __shared__ int32_t s_ids[kSmallPairs];
   __shared__ float s_z[NWV][MOE_MAX_TOP_K];
   __shared__ int s_rank[NWV * kWave * NJ];
+  __shared__ float s_w[kSmallPairs];
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int P = T * k;
   LaneState<NJ> pre;
   if (wid == 0) pre = load_lane_state<NJ>(state, sl, E, K);
-  // the router's per-token LDS borrows the victim-key array (unused until the plan)
+  // Ids and weights stay in LDS until the plan is done: a global store issued
+  // before it would make the plan's first use of the table state wait for the
+  // store as well (loads and stores share one counter). The router's per-token
+  // LDS borrows the victim-key array (unused until the plan).
   if (T == 1) {
-    route_token_split<NJ, NWV>(logits, E, k, lane, wid, sm.vkey, s_rank, s_z[0], s_ids, dev.weights);
+    route_token_split<NJ, NWV>(logits, E, k, lane, wid, sm.vkey, s_rank, s_z[0], s_ids, s_w);
   } else {
     for (int t = wid; t < T; t += NWV)
       route_token<NJ>(logits + (size_t)t * E, E, k, lane, sm.vkey + wid * (kWave * NJ), s_z[wid],
-                      s_ids + t * k, dev.weights + (size_t)t * k);
+                      s_ids + t * k, s_w + t * k);
   }
-  __syncthreads();
-  for (int p = threadIdx.x; p < P; p += NT) dev.ids[p] = s_ids[p];
-  if (wid == 0) plan_wave<NJ>(s_ids, P, T, E, K, state, sl, pre, dev, sm);
-  __syncthreads();
+  lds_barrier();
+  PlanOut<NJ> out;
+  if (wid == 0) plan_wave<NJ>(s_ids, P, E, K, pre, sm, out);
+  lds_barrier();
   const int D = sm.warp[0], nH = sm.warp[1], nw = sm.warp[2];
-  // per-pair slot and wave
-  for (int p = threadIdx.x; p < P; p += NT) {
-    const int pos = sm.pos[s_ids[p]];
-    dev.slot_ids[p] = sm.order_s[pos];
-    dev.wave_of[p] = pos / K;
+  // wavefront 0 stores the plan while wavefronts 1 .. NWV-1 store the pairs
+  if (wid == 0) plan_wave_store<NJ>(out, P, T, E, K, state, sl, dev, sm, D, nH, nw);
+  // per-pair id, weight, slot and wave
+  if (wid > 0) {
+    for (int p = (int)threadIdx.x - kWave; p < P; p += NT - kWave) {
+      const int e = s_ids[p];
+      const int pos = sm.pos[e];
+      dev.ids[p] = e;
+      dev.weights[p] = s_w[p];
+      dev.slot_ids[p] = sm.order_s[pos];
+      dev.wave_of[p] = pos / K;
+    }
   }
-  group_small<NWV>(sm, s_ids, P, D, dev);
-  add_dstats(dstats, T, P, D, nH, nw);
+  group_small<NWV, 1>(sm, s_ids, P, D, dev);
+  add_dstats(dstats, T, P, D, nH, nw, kWave);
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
 
