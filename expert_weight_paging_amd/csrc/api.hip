@@ -57,6 +57,8 @@ struct moe_layer {
   uint8_t* state;
   hipStream_t compute, copy, route;
   hipEvent_t ev_fwd_done, ev_copied, ev_routed;
+  hipEvent_t ev_victims_free;     // recorded by forward(w) once the slots page_in(w + 1) overwrites are read
+  int victims_free_wave;          // the w of that forward in the current step, or -1
   bool fwd_recorded, copy_recorded;
   int initial_fill;
   moe_stats stats;
@@ -167,6 +169,7 @@ moe_status restore_initial(moe_layer* L) {
     HIP_TRY(hipMemcpy(L->slots, L->host_store, (size_t)L->K * L->stride, hipMemcpyHostToDevice));
   L->cur_plan = nullptr;
   L->next_page = L->next_fwd = L->n_waves = 0;
+  L->victims_free_wave = -1;
   return MOE_OK;
 }
 
@@ -330,7 +333,8 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
   };
   if (hipEventCreateWithFlags(&L->ev_fwd_done, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&L->ev_copied, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&L->ev_routed, hipEventDisableTiming) != hipSuccess)
+      hipEventCreateWithFlags(&L->ev_routed, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&L->ev_victims_free, hipEventDisableTiming) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "hipEventCreate failed"));
   // device alias of the host store, for device-resolved steps (none if unmapped)
   void* hs_dev = nullptr;
@@ -357,6 +361,7 @@ void moe_layer_destroy(moe_layer* L) {
   if (L->ev_fwd_done) (void)hipEventDestroy(L->ev_fwd_done);
   if (L->ev_copied) (void)hipEventDestroy(L->ev_copied);
   if (L->ev_routed) (void)hipEventDestroy(L->ev_routed);
+  if (L->ev_victims_free) (void)hipEventDestroy(L->ev_victims_free);
   if (L->dstats) (void)hipFree(L->dstats);
 
   for (auto& t : L->pending) {
@@ -534,6 +539,7 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
   }
   L->n_waves = h.num_waves;
   L->next_page = L->next_fwd = 0;
+  L->victims_free_wave = -1;
   L->cur_plan = h.num_waves > 0 ? p : nullptr;
   return MOE_OK;
 }
@@ -588,7 +594,10 @@ moe_status moe_page_in(moe_layer* L, const moe_plan* p, int32_t w) {
   moe_status st = moe_plan_get_wave(p, w, &wi);
   if (st) return st;
   // a victim slot may still be read by the previous forward of this layer
-  if (L->fwd_recorded) HIP_TRY(hipStreamWaitEvent(L->copy, L->ev_fwd_done, 0));
+  // (when that forward computed the experts in this wave's victim slots first,
+  // only that part is waited for)
+  if (w > 0 && L->victims_free_wave == w - 1) HIP_TRY(hipStreamWaitEvent(L->copy, L->ev_victims_free, 0));
+  else if (L->fwd_recorded) HIP_TRY(hipStreamWaitEvent(L->copy, L->ev_fwd_done, 0));
   TimerRec tr{};
   st = timer_begin(L, L->copy, &tr);
   if (st) return st;
@@ -596,8 +605,17 @@ moe_status moe_page_in(moe_layer* L, const moe_plan* p, int32_t w) {
     const int e = wi.miss_experts[i], s = wi.miss_slots[i];
     if (e < 0 || e >= L->E || s < 0 || s >= L->K)
       return fail(MOE_ERR_STATE, "corrupt miss list");
+  }
+  // One DMA copy per run of misses that is contiguous in both stores (expert
+  // e + 1 into slot s + 1 after e into s): the same bytes in fewer, larger
+  // copies, which keep the link busier than one copy per record.
+  for (int i = 0; i < wi.num_misses;) {
+    const int e = wi.miss_experts[i], s = wi.miss_slots[i];
+    int n = 1;
+    while (i + n < wi.num_misses && wi.miss_experts[i + n] == e + n && wi.miss_slots[i + n] == s + n) ++n;
     HIP_TRY(hipMemcpyAsync(L->slots + (size_t)s * L->stride, L->host_store + (size_t)e * L->stride,
-                           L->stride, hipMemcpyHostToDevice, L->copy));
+                           (size_t)n * L->stride, hipMemcpyHostToDevice, L->copy));
+    i += n;
   }
   st = timer_end(L, L->copy, &tr, MOE_T_PAGE_IN, (double)wi.num_misses * L->stride, 0.0);
   if (st) return st;
@@ -617,6 +635,40 @@ moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x
 }
 
 namespace {
+// The part of wave w's positions [o_lo, o_lo + n_exp) that reads the slots
+// wave w + 1 pages into: the shortest prefix or suffix of the range that holds
+// all of them, as [*v_lo, *v_lo + *v_n); *v_n = 0 if there are none, n_exp if
+// they span the range.
+void victims_first(const moe_layer* L, const moe_plan* p, int w, int o_lo, int n_exp, int* v_lo, int* v_n) {
+  const int K = L->K, D = p->info.num_distinct, nH = p->info.num_hits;
+  const int32_t* os = (const int32_t*)(p->hdr + 1) + L->E;  // slot of each wave-order position
+  const int lo1 = (w + 1) * K, hi1 = std::min(lo1 + K, D), m1 = std::max(lo1, nH);
+  std::vector<char> victim((size_t)K, 0);
+  for (int i = m1; i < hi1; ++i)
+    if (os[i] >= 0 && os[i] < K) victim[(size_t)os[i]] = 1;
+  int first = -1, last = -1;
+  for (int o = o_lo; o < o_lo + n_exp; ++o) {
+    const int sl = os[o];
+    if (sl >= 0 && sl < K && victim[(size_t)sl]) {
+      if (first < 0) first = o;
+      last = o;
+    }
+  }
+  *v_lo = o_lo;
+  *v_n = n_exp;
+  if (first < 0) {
+    *v_n = 0;
+    return;
+  }
+  const int pre = last - o_lo + 1, suf = o_lo + n_exp - first;
+  if (pre <= suf) {
+    *v_n = pre;
+  } else {
+    *v_lo = first;
+    *v_n = suf;
+  }
+}
+
 // x_res, if given, receives the stack residual bf16_rne(x_res + out) from the
 // kernel that completes out (only on a step's last wave).
 moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out,
@@ -656,8 +708,30 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
     if (st) return st;
   } else {
     if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
-    st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, pairs_in(o_lo, n_exp), T, x, out,
-                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
+    // Victims first (GEMM path): when the next wave pages experts into slots
+    // this wave reads, the experts in those slots are computed first, and the
+    // next wave's copies start while the rest of this wave computes. The
+    // combine after both parts sums in the same fixed order, so the result is
+    // bitwise the same as one launch.
+    int v_lo = o_lo, v_n = n_exp;
+    if (gemm && w + 1 < p->info.num_waves) victims_first(L, p, w, o_lo, n_exp, &v_lo, &v_n);
+    if (v_n == 0) {  // the next wave's copies touch none of this wave's slots
+      HIP_TRY(hipEventRecord(L->ev_victims_free, L->compute));
+      L->victims_free_wave = w;
+    }
+    if (v_n > 0 && v_n < n_exp) {
+      const int r_lo = v_lo == o_lo ? o_lo + v_n : o_lo, r_n = n_exp - v_n;
+      st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, v_lo, v_n, pairs_in(v_lo, v_n), T, x, out, w > 0,
+                   p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false, nullptr, nullptr, p->wdq);
+      if (st) return st;
+      HIP_TRY(hipEventRecord(L->ev_victims_free, L->compute));
+      L->victims_free_wave = w;
+      st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, r_lo, r_n, pairs_in(r_lo, r_n), T, x, out, w > 0,
+                   p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
+    } else {
+      st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, pairs_in(o_lo, n_exp), T, x, out,
+                   w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
+    }
     if (st) return st;
   }
   HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));

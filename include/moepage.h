@@ -225,8 +225,10 @@ moe_status moe_plan_get_wave(const moe_plan* plan, int32_t wave, moe_wave_info* 
 moe_status moe_plan_read(const moe_plan* plan, int32_t* ids, float* weights,
                          int32_t* slot_ids, int32_t* wave_of);
 
-/* Page in the misses of one wave: one hipMemcpyAsync per miss, host record ->
- * its slot, on copy_stream, after the layer's previous forward has finished
+/* Page in the misses of one wave: each miss's whole host record -> its slot by
+ * hipMemcpyAsync (misses that are consecutive in both stores, expert e + 1 into
+ * slot s + 1 after e into s, share one copy), on copy_stream, after the
+ * layer's previous forward has finished
  * (a victim slot may still be read by it). Waves are paged in and computed in
  * order: page_in(w) requires forward(w-1) to have been issued. */
 moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
