@@ -529,6 +529,8 @@ def roofline(res, workload, variant):
         flops = tm[dom]["flops"] / sec / 1e12
         gbps = tm[dom]["bytes"] / sec / 1e9
         kname = "grouped_gemm_kernel<%s>" % ("true" if dom == "gemm_up" else "false")
+        # both GEMMs of the expert FFN together (the down GEMM's flops count h once)
+        both = sum(tm[k]["flops"] for k in kinds) / (sum(tm[k]["ms"] for k in kinds) * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": kname, "achieved": round(flops, 1),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(flops / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -536,6 +538,8 @@ def roofline(res, workload, variant):
                 "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
                 "algorithmic_flops_per_launch": tm[dom]["flops"] / tm[dom]["count"],
                 "weight_GBps": round(gbps, 1), "weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "gemm_up_plus_down_TFLOPs": round(both, 1),
+                "gemm_up_plus_down_frac": round(both / BF16_MFMA_PEAK_TFLOPS, 4),
                 "launch_floor_us": round(res["floor_us"], 3)}
     kinds = [k for k in ("ffn_up", "ffn_down") if tm[k]["count"]]
     dom = max(kinds, key=lambda k: tm[k]["ms"])

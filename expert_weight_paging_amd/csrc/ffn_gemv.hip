@@ -221,7 +221,10 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
   const int wid = threadIdx.x / kWave;
   const int H = a.H, I = a.I;
   const int i0 = (blockIdx.x * 4 + wid) * RPW;
-  if (i0 >= I) return;
+  // bf16: every wavefront takes part in the workgroup barriers below (a
+  // wavefront past the last row loads row I - 1 again and stores nothing)
+  constexpr bool kStageX = F == MOE_FMT_BF16 && sizeof(XT) == 2;
+  if (!kStageX && i0 >= I) return;
   if (a.n_dev && (int)blockIdx.y >= *a.n_dev) return;  // device-resolved count: uniform per block
   const int o = a.o_lo + blockIdx.y;
   const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
@@ -293,17 +296,23 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
 
   const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
   const XT* xbase = (const XT*)a.x;
-  if constexpr (F == MOE_FMT_BF16 && sizeof(XT) == 2) {
+  if constexpr (kStageX) {
     // bf16 weights and activations: dot the packed pairs directly (8 values
-    // per 16-byte chunk in 4 words), activations never widened to fp32
+    // per 16-byte chunk in 4 words), activations never widened to fp32. The
+    // pair's activation row is read from memory once per workgroup into LDS
+    // and shared by its four wavefronts.
+    __shared__ uint4 xs[kWave * NJ];
     for (int q = p0; q < p1; ++q) {
       const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
+      if (q > p0) __syncthreads();  // the previous pair's reads of xs are done
+      for (int c = threadIdx.x; c < nch; c += 4 * kWave)
+        xs[c] = *(const uint4*)((const uint16_t*)xbase + (size_t)t * H + c * CV1);
+      __syncthreads();
       uint4 xw[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int c = lane + kWave * j;
-        xw[j] = c < nch ? *(const uint4*)((const uint16_t*)xbase + (size_t)t * H + c * CV1)
-                        : make_uint4(0, 0, 0, 0);
+        xw[j] = c < nch ? xs[c] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {

@@ -41,6 +41,19 @@ def test_bf16_layer_256_steps():
     p.close()
 
 
+@pytest.mark.parametrize("B", [3, 8])
+def test_bf16_layer_batches(B):
+    """Several tokens per expert (the bf16 up kernel shares each pair's
+    activation row through LDS, pair after pair); B=8 gives multi-wave steps."""
+    cfg = W.CONFIGS[2]
+    say("case: bf16 layer K=40, 24 steps at batch %d" % B)
+    p = _layer(cfg, B)
+    logits, x = gen.decode_inputs(cfg, B, steps=24)
+    worst = p.run(logits, x, sample=lambda t: t % 4 == 3)
+    say("bf16 B=%d worst rel err" % B, worst)
+    p.close()
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 5, 6, 8])
 def test_fp8_layer_batches(B):
     cfg = W.CONFIGS[3]
