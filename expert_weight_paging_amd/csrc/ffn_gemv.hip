@@ -221,10 +221,12 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
   const int wid = threadIdx.x / kWave;
   const int H = a.H, I = a.I;
   const int i0 = (blockIdx.x * 4 + wid) * RPW;
-  // bf16: every wavefront takes part in the workgroup barriers below (a
-  // wavefront past the last row loads row I - 1 again and stores nothing)
-  constexpr bool kStageX = F == MOE_FMT_BF16 && sizeof(XT) == 2;
-  if (!kStageX && i0 >= I) return;
+  // Every wavefront takes part in the workgroup barriers below (one past the
+  // last row loads row I - 1 again and stores nothing): each pair's
+  // activation row is read from memory once per workgroup into LDS and
+  // shared by its four wavefronts.
+  __shared__ uint4 xs[kWave * NJ * CV1 * sizeof(XT) / 16];
+  const int nx16 = H * (int)sizeof(XT) / 16;  // 16-byte chunks of one activation row
   if (a.n_dev && (int)blockIdx.y >= *a.n_dev) return;  // device-resolved count: uniform per block
   const int o = a.o_lo + blockIdx.y;
   const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
@@ -296,17 +298,14 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
 
   const int p0 = a.pair_off[o], p1 = a.pair_off[o + 1];
   const XT* xbase = (const XT*)a.x;
-  if constexpr (kStageX) {
+  if constexpr (F == MOE_FMT_BF16 && sizeof(XT) == 2) {
     // bf16 weights and activations: dot the packed pairs directly (8 values
-    // per 16-byte chunk in 4 words), activations never widened to fp32. The
-    // pair's activation row is read from memory once per workgroup into LDS
-    // and shared by its four wavefronts.
-    __shared__ uint4 xs[kWave * NJ];
+    // per 16-byte chunk in 4 words), activations never widened to fp32
     for (int q = p0; q < p1; ++q) {
       const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
       if (q > p0) __syncthreads();  // the previous pair's reads of xs are done
-      for (int c = threadIdx.x; c < nch; c += 4 * kWave)
-        xs[c] = *(const uint4*)((const uint16_t*)xbase + (size_t)t * H + c * CV1);
+      for (int c = threadIdx.x; c < nx16; c += 4 * kWave)
+        xs[c] = ((const uint4*)(xbase + (size_t)t * H))[c];
       __syncthreads();
       uint4 xw[NJ];
 #pragma unroll
@@ -338,11 +337,15 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
   for (int q = p0; q < p1; ++q) {
     // with one token every pair is token 0: no dependent pair-list load
     const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
+    if (q > p0) __syncthreads();  // the previous pair's reads of xs are done
+    for (int c = threadIdx.x; c < nx16; c += 4 * kWave) xs[c] = ((const uint4*)(xbase + (size_t)t * H))[c];
+    __syncthreads();
+    const XT* xrow = (const XT*)xs;
     float xv[NJ][CV1];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = lane + kWave * j;
-      if (c < nch) load_x<F, XT>(xbase + (size_t)t * H, c * CV1, xv[j]);
+      if (c < nch) load_x<F, XT>(xrow, c * CV1, xv[j]);
       else {
 #pragma unroll
         for (int v = 0; v < CV1; ++v) xv[j][v] = 0.f;
