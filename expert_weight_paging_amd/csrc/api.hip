@@ -50,7 +50,8 @@ struct moe_layer {
   const uint8_t* host_store;
   const uint8_t* host_store_dev;  // device alias of the host store (null if not mapped)
   long long* dstats;              // device-resolved steps' counters (steps, refs, activations,
-                                  // hits, misses, waves), device memory
+                                  // hits, misses, waves; [6]: the route-and-page-in launch's
+                                  // ticket counter), device memory
   bool dev_steps;                 // a device-resolved step has been enqueued
   bool dev_pending;               // ... and no host-mode route has waited for it yet
   uint8_t* slots;
@@ -851,20 +852,33 @@ moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int3
   moe_status st = MOE_OK;
   do {
     TimerRec tr{}, tc{};
-    if ((st = timer_events(L, &tr)) || (st = timer_events(L, &tc))) break;
-    if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, nullptr, 0, ps, tr.a, tr.b,
-                                L->dstats) != hipSuccess) {
-      st = fail(MOE_ERR_HIP, "route launch failed");
-      break;
+    if (ps == cs && route_page_in_ok(L->E)) {
+      // one launch routes, plans and pages in (timed as the page-in; its ticket
+      // counter is the layer's device counter 6)
+      if ((st = timer_events(L, &tc))) break;
+      if (launch_route_plan_page_in(logits, T, L->E, L->k, L->K, L->state, p->dev, L->dstats,
+                                    (unsigned long long*)(L->dstats + 6), L->host_store_dev, L->slots,
+                                    L->stride, ps, tc.a, tc.b) != hipSuccess) {
+        st = fail(MOE_ERR_HIP, "route and page-in launch failed");
+        break;
+      }
+      timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
+    } else {
+      if ((st = timer_events(L, &tr)) || (st = timer_events(L, &tc))) break;
+      if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, nullptr, 0, ps, tr.a, tr.b,
+                                  L->dstats) != hipSuccess) {
+        st = fail(MOE_ERR_HIP, "route launch failed");
+        break;
+      }
+      timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
+      if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, p->dev, L->E, L->K, ps, tc.a, tc.b) !=
+          hipSuccess) {
+        st = fail(MOE_ERR_HIP, "page-in launch failed");
+        break;
+      }
+      // bytes are not known on the host here; moe_layer_stats has the misses
+      timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
     }
-    timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
-    if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, p->dev, L->E, L->K, ps, tc.a, tc.b) !=
-        hipSuccess) {
-      st = fail(MOE_ERR_HIP, "page-in launch failed");
-      break;
-    }
-    // bytes are not known on the host here; moe_layer_stats has the misses
-    timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
     if (ps != cs && (hipEventRecord(L->ev_copied, ps) != hipSuccess ||
                      hipStreamWaitEvent(cs, L->ev_copied, 0) != hipSuccess)) {
       st = fail(MOE_ERR_HIP, "hand-over from the copy stream failed");

@@ -131,6 +131,15 @@ bool route_small_ok(int T, int k);
 hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int K, void* state,
                                    PlanDev dev, PlanHdr* host_hdr_dev, int32_t seq, hipStream_t s,
                                    hipEvent_t ev0, hipEvent_t ev1, long long* dstats = nullptr);
+// Device-resolved single-wave step, route and page-in in one launch (E <= 256):
+// every workgroup plans the step, workgroup 0 stores the plan and counters,
+// the last to finish planning (by the ticket counter, a multiple of the grid
+// size between launches) stores the table state, and all copy their share of
+// the missed records from the device-mapped host store into the slots.
+bool route_page_in_ok(int E);
+hipError_t launch_route_plan_page_in(const float* logits, int T, int E, int k, int K, void* state, PlanDev dev,
+                                     long long* dstats, unsigned long long* ticket, const uint8_t* host_store_dev,
+                                     uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 // Device-resolved page-in of a single-wave plan: copies the records of wave
 // order positions [counts[1], counts[0]) (the misses) from the device-mapped
 // host store into their slots.

@@ -689,13 +689,14 @@ __device__ void plan_wave(const int32_t* ids, int P, int E, int K, const LaneSta
 }
 
 // The global stores of plan_wave (same wavefront, after the workgroup has
-// passed the barrier that follows the plan): the table state, the wave order
-// with its slots, the CSR offsets and the counters. Issued together with the
-// per-pair stores of the other wavefronts, so their latencies overlap.
+// passed the barrier that follows the plan): the table state (with_state),
+// the wave order with its slots, the CSR offsets and the counters
+// (with_order). Issued together with the per-pair stores of the other
+// wavefronts, so their latencies overlap.
 template <int NJ>
 __device__ void plan_wave_store(const PlanOut<NJ>& out, int P, int T, int E, int K, uint8_t* state,
                                 const StateLayout& sl, const PlanDev& dev, const PlanSmem& sm, int D,
-                                int nH, int n_waves) {
+                                int nH, int n_waves, bool with_state = true, bool with_order = true) {
   int32_t* g_slot_expert = (int32_t*)(state + sl.slot_expert);
   int32_t* g_expert_slot = (int32_t*)(state + sl.expert_slot);
   long long* g_stamp = (long long*)(state + sl.stamp);
@@ -704,24 +705,30 @@ __device__ void plan_wave_store(const PlanOut<NJ>& out, int P, int T, int E, int
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int i = lane + kWave * j;
-    if (i < E) g_expert_slot[i] = sm.expert_slot[i];
-    if (i < K) {
-      g_slot_expert[i] = out.se[j];
-      g_stamp[i] = out.st[j];
+    if (with_state) {
+      if (i < E) g_expert_slot[i] = sm.expert_slot[i];
+      if (i < K) {
+        g_slot_expert[i] = out.se[j];
+        g_stamp[i] = out.st[j];
+      }
     }
-    if (i < E) dev.pair_off[i] = i < D ? out.off[j] : P;
-    if (i < D) {
-      dev.order_expert[i] = sm.order_e[i];
-      dev.order_slot[i] = sm.order_s[i];
+    if (with_order) {
+      if (i < E) dev.pair_off[i] = i < D ? out.off[j] : P;
+      if (i < D) {
+        dev.order_expert[i] = sm.order_e[i];
+        dev.order_slot[i] = sm.order_s[i];
+      }
     }
   }
   if (lane == 0) {
-    *g_clock = out.clock;
-    dev.pair_off[E] = P;
-    dev.counts[0] = D;
-    dev.counts[1] = nH;
-    dev.counts[2] = n_waves;
-    dev.counts[3] = T;
+    if (with_state) *g_clock = out.clock;
+    if (with_order) {
+      dev.pair_off[E] = P;
+      dev.counts[0] = D;
+      dev.counts[1] = nH;
+      dev.counts[2] = n_waves;
+      dev.counts[3] = T;
+    }
   }
 }
 
@@ -773,6 +780,101 @@ __global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __res
   group_small<NWV, 1>(sm, s_ids, P, D, dev);
   add_dstats(dstats, T, P, D, nH, nw, kWave);
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
+}
+
+// ------------------------------------------------------------------ route + page-in, one launch
+// Device-resolved single-wave steps ([PE] "What happens with more than one
+// request?": the single wave is the step a graph can capture; "TL;DR": only the
+// routed experts that are not resident are copied in). kPageInBlocks
+// workgroups each run the router and the one-wavefront plan on the same inputs,
+// so each holds the same plan in its LDS, and each then copies its share of the
+// missed records from the device-mapped host store into their slots: no second
+// launch and no exchange between workgroups. Workgroup 0 stores the plan, the
+// pairs and the counters. The table state may be rewritten only once every
+// workgroup has read it: each takes a ticket from a counter after its plan
+// (which has consumed the state), and the workgroup holding the last ticket of
+// the launch stores the new state. The counter grows by the grid size per
+// launch, so "last" is a ticket that is one below a multiple of it.
+constexpr int kPageInBlocks = 64;
+constexpr int kCopyUnroll = 4;
+
+template <int NJ>
+__global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __restrict__ logits, int T,
+                                                                 int E, int k, int K, uint8_t* state,
+                                                                 StateLayout sl, PlanDev dev, long long* dstats,
+                                                                 unsigned long long* ticket,
+                                                                 const uint8_t* __restrict__ host,
+                                                                 uint8_t* __restrict__ slots, size_t stride) {
+  constexpr int NT = 256, NWV = NT / kWave;
+  __shared__ PlanSmem sm;
+  __shared__ int32_t s_ids[kSmallPairs];
+  __shared__ float s_z[NWV][MOE_MAX_TOP_K];
+  __shared__ int s_rank[NWV * kWave * NJ];
+  __shared__ float s_w[kSmallPairs];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const bool lead = blockIdx.x == 0;
+  const int P = T * k;
+  LaneState<NJ> pre;
+  if (wid == 0) pre = load_lane_state<NJ>(state, sl, E, K);
+  if (T == 1) {
+    route_token_split<NJ, NWV>(logits, E, k, lane, wid, sm.vkey, s_rank, s_z[0], s_ids, s_w);
+  } else {
+    for (int t = wid; t < T; t += NWV)
+      route_token<NJ>(logits + (size_t)t * E, E, k, lane, sm.vkey + wid * (kWave * NJ), s_z[wid],
+                      s_ids + t * k, s_w + t * k);
+  }
+  lds_barrier();
+  PlanOut<NJ> out;
+  if (wid == 0) {
+    plan_wave<NJ>(s_ids, P, E, K, pre, sm, out);
+    if (lane == 0) {
+      const unsigned long long tk =
+          __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (tk + 1) % gridDim.x == 0;
+    }
+  }
+  lds_barrier();
+  const int D = sm.warp[0], nH = sm.warp[1], nw = sm.warp[2];
+  if (wid == 0 && (lead || s_last))
+    plan_wave_store<NJ>(out, P, T, E, K, state, sl, dev, sm, D, nH, nw, s_last != 0, lead);
+  if (lead) {
+    if (wid > 0) {
+      for (int p = (int)threadIdx.x - kWave; p < P; p += NT - kWave) {
+        const int e = s_ids[p];
+        const int pos = sm.pos[e];
+        dev.ids[p] = e;
+        dev.weights[p] = s_w[p];
+        dev.slot_ids[p] = sm.order_s[pos];
+        dev.wave_of[p] = pos / K;
+      }
+    }
+    group_small<NWV, 1>(sm, s_ids, P, D, dev);
+    add_dstats(dstats, T, P, D, nH, nw, kWave);
+  }
+  // this workgroup's share of every missed record (the single wave's order
+  // positions nH .. D-1), 16-byte chunks, kCopyUnroll loads in flight per thread
+  const size_t n16 = stride / 16;  // records are 256-byte multiples
+  const size_t step = (size_t)gridDim.x * NT * kCopyUnroll;
+  for (int m = nH; m < D; ++m) {
+    const int e = sm.order_e[m], sl_ = sm.order_s[m];
+    const uint4* src = (const uint4*)(host + (size_t)e * stride);
+    uint4* dst = (uint4*)(slots + (size_t)sl_ * stride);
+    for (size_t i = (size_t)blockIdx.x * NT * kCopyUnroll + threadIdx.x; i < n16; i += step) {
+      uint4 v[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const size_t j = i + (size_t)u * NT;
+        if (j < n16) v[u] = src[j];
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const size_t j = i + (size_t)u * NT;
+        if (j < n16) dst[j] = v[u];
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ grouping
@@ -889,6 +991,24 @@ hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int
   else MOE_SMALL(1024, 16);
 #undef MOE_SMALL
 #undef MOE_WAVE
+  return hipGetLastError();
+}
+
+bool route_page_in_ok(int E) { return E <= 256; }
+
+hipError_t launch_route_plan_page_in(const float* logits, int T, int E, int k, int K, void* state, PlanDev dev,
+                                     long long* dstats, unsigned long long* ticket, const uint8_t* host_store_dev,
+                                     uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const StateLayout sl = state_layout(E, K);
+  uint8_t* st = (uint8_t*)state;
+#define MOE_FUSED(NJ)                                                                                    \
+  launch_k(route_plan_page_in_kernel<NJ>, dim3(kPageInBlocks), dim3(256), s, ev0, ev1, logits, T, E, k, K, st, \
+           sl, dev, dstats, ticket, host_store_dev, slots, stride)
+  if (E <= 64) MOE_FUSED(1);
+  else if (E <= 128) MOE_FUSED(2);
+  else if (E <= 256) MOE_FUSED(4);
+  else return hipErrorInvalidValue;
+#undef MOE_FUSED
   return hipGetLastError();
 }
 
