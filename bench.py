@@ -62,6 +62,7 @@ def log(*a):
 KERNEL_SOURCE = {"ffn_up_kernel": "ffn_gemv.hip", "ffn_down_kernel": "ffn_gemv.hip",
                  "grouped_gemm_kernel<true>": "ffn_gemm.hip", "grouped_gemm_kernel<false>": "ffn_gemm.hip",
                  "combine_kernel": "ffn_gemm.hip", "route_plan_small_kernel": "plan.hip",
+                 "route_plan_wave_kernel": "plan.hip", "route_plan_page_in_kernel": "plan.hip",
                  "page_in_kernel": "page_in.hip"}
 
 
@@ -116,8 +117,8 @@ def ingest_pmc(fetch_csv, write_csv, workload):
                 if "copyBuffer" in name and v > 256 * 1024:  # the 1 GiB copy (>= 256 MiB read)
                     calib.append(v)
                     continue
-                for pat, key in KERNEL_KEYS:
-                    if pat in name.replace(" ", ""):
+                for pat, key in KERNEL_KEYS:  # the kernel's own name, not a longer one ending in it
+                    if "::" + pat in name.replace(" ", ""):
                         per.setdefault(key, []).append(v)
         if not calib:
             raise SystemExit("no 1 GiB copy in %s: run the bench without --no-peaks" % path)
