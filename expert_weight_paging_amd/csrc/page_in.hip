@@ -16,6 +16,7 @@
 // 16-byte loads in flight per thread keep the link as busy as the DMA engines
 // (measured on MI355X: 50 to 57 GB/s for 2.5 to 75 MB), while leaving the
 // other CUs free.
+#include "copy.h"
 #include "internal.h"
 
 namespace moepage {
@@ -34,26 +35,11 @@ __global__ __launch_bounds__(kCopyThreads) void page_in_kernel(const uint8_t* __
                                                                const int32_t* __restrict__ counts, int E,
                                                                int K) {
   const int D = counts[0], nH = counts[1];
-  const size_t n16 = stride / 16;  // records are 256-byte multiples
-  const size_t step = (size_t)gridDim.x * kCopyThreads * kCopyUnroll;
   for (int m = nH; m < D; ++m) {  // the misses of the single wave, in wave order
     const int e = order_expert[m], s = order_slot[m];
     if (e < 0 || e >= E || s < 0 || s >= K) continue;  // never produced by the plan
-    const uint4* src = (const uint4*)(host + (size_t)e * stride);
-    uint4* dst = (uint4*)(slots + (size_t)s * stride);
-    for (size_t i = (size_t)blockIdx.x * kCopyThreads * kCopyUnroll + threadIdx.x; i < n16; i += step) {
-      uint4 v[kCopyUnroll];
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const size_t j = i + (size_t)u * kCopyThreads;
-        if (j < n16) v[u] = src[j];
-      }
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const size_t j = i + (size_t)u * kCopyThreads;
-        if (j < n16) dst[j] = v[u];
-      }
-    }
+    copy_record_share<kCopyThreads, kCopyUnroll>(host + (size_t)e * stride, slots + (size_t)s * stride, stride,
+                                                 blockIdx.x, gridDim.x);
   }
 }
 

@@ -3,6 +3,7 @@
 // [PE] = "Running an MoE Model Larger Than Your VRAM: SGLang Paged Experts, the
 // PCIe Math, and the 4-Request Cliff". [LRU] = "Locality of reference helped
 // 94GB Qwen3.8-Flash-Next runs at 68 tok/s on one RTX 5090".
+#include "copy.h"
 #include "internal.h"
 #include "wave.h"
 
@@ -732,17 +733,39 @@ __device__ void plan_wave_store(const PlanOut<NJ>& out, int P, int T, int E, int
   }
 }
 
-template <int NJ>
-__global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __restrict__ logits, int T, int E,
-                                                              int k, int K, uint8_t* state, StateLayout sl,
-                                                              PlanDev dev, PlanHdr* hdr, int32_t seq,
-                                                              long long* dstats) {
+// ------------------------------------------------------------------ small steps, one launch
+// Router, one-wavefront plan and grouping of a decode-sized step (E <= 256).
+//
+// route_plan_wave_kernel (PAGE_IN = false): one workgroup; the plan is stored
+// and, for host-driven steps, published to the host.
+//
+// route_plan_page_in_kernel (PAGE_IN = true; device-resolved single-wave steps, [PE] "What happens with
+// more than one request?": the single wave is the step a graph can capture;
+// "TL;DR": only the routed experts that are not resident are copied in):
+// kPageInBlocks workgroups each route and plan the step from the same inputs,
+// so each holds the same plan in its LDS, and each then copies its share of
+// the missed records from the device-mapped host store into their slots: no
+// second launch and no exchange between workgroups. Workgroup 0 stores the
+// plan, the pairs and the counters. The table state may be rewritten only once
+// every workgroup has read it: each takes a ticket from a counter after its
+// plan (which has consumed the state), and the workgroup holding the last
+// ticket of the launch stores the new state. The counter grows by the grid
+// size per launch, so "last" is a ticket that is one below a multiple of it.
+constexpr int kPageInBlocks = 64;
+constexpr int kCopyUnroll = 4;
+
+template <int NJ, bool PAGE_IN>
+__device__ void route_plan_body(const float* __restrict__ logits, int T, int E, int k, int K, uint8_t* state,
+                                const StateLayout& sl, const PlanDev& dev, PlanHdr* hdr, int32_t seq,
+                                long long* dstats, unsigned long long* ticket, const uint8_t* __restrict__ host,
+                                uint8_t* __restrict__ slots, size_t stride) {
   constexpr int NT = 256, NWV = NT / kWave;
   __shared__ PlanSmem sm;
   __shared__ int32_t s_ids[kSmallPairs];
   __shared__ float s_z[NWV][MOE_MAX_TOP_K];
   __shared__ int s_rank[NWV * kWave * NJ];
   __shared__ float s_w[kSmallPairs];
+  __shared__ int s_last;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int P = T * k;
@@ -761,75 +784,9 @@ __global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __res
   }
   lds_barrier();
   PlanOut<NJ> out;
-  if (wid == 0) plan_wave<NJ>(s_ids, P, E, K, pre, sm, out);
-  lds_barrier();
-  const int D = sm.warp[0], nH = sm.warp[1], nw = sm.warp[2];
-  // wavefront 0 stores the plan while wavefronts 1 .. NWV-1 store the pairs
-  if (wid == 0) plan_wave_store<NJ>(out, P, T, E, K, state, sl, dev, sm, D, nH, nw);
-  // per-pair id, weight, slot and wave
-  if (wid > 0) {
-    for (int p = (int)threadIdx.x - kWave; p < P; p += NT - kWave) {
-      const int e = s_ids[p];
-      const int pos = sm.pos[e];
-      dev.ids[p] = e;
-      dev.weights[p] = s_w[p];
-      dev.slot_ids[p] = sm.order_s[pos];
-      dev.wave_of[p] = pos / K;
-    }
-  }
-  group_small<NWV, 1>(sm, s_ids, P, D, dev);
-  add_dstats(dstats, T, P, D, nH, nw, kWave);
-  publish(sm, E, T, P, D, nH, nw, hdr, seq);
-}
-
-// ------------------------------------------------------------------ route + page-in, one launch
-// Device-resolved single-wave steps ([PE] "What happens with more than one
-// request?": the single wave is the step a graph can capture; "TL;DR": only the
-// routed experts that are not resident are copied in). kPageInBlocks
-// workgroups each run the router and the one-wavefront plan on the same inputs,
-// so each holds the same plan in its LDS, and each then copies its share of the
-// missed records from the device-mapped host store into their slots: no second
-// launch and no exchange between workgroups. Workgroup 0 stores the plan, the
-// pairs and the counters. The table state may be rewritten only once every
-// workgroup has read it: each takes a ticket from a counter after its plan
-// (which has consumed the state), and the workgroup holding the last ticket of
-// the launch stores the new state. The counter grows by the grid size per
-// launch, so "last" is a ticket that is one below a multiple of it.
-constexpr int kPageInBlocks = 64;
-constexpr int kCopyUnroll = 4;
-
-template <int NJ>
-__global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __restrict__ logits, int T,
-                                                                 int E, int k, int K, uint8_t* state,
-                                                                 StateLayout sl, PlanDev dev, long long* dstats,
-                                                                 unsigned long long* ticket,
-                                                                 const uint8_t* __restrict__ host,
-                                                                 uint8_t* __restrict__ slots, size_t stride) {
-  constexpr int NT = 256, NWV = NT / kWave;
-  __shared__ PlanSmem sm;
-  __shared__ int32_t s_ids[kSmallPairs];
-  __shared__ float s_z[NWV][MOE_MAX_TOP_K];
-  __shared__ int s_rank[NWV * kWave * NJ];
-  __shared__ float s_w[kSmallPairs];
-  __shared__ int s_last;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  const bool lead = blockIdx.x == 0;
-  const int P = T * k;
-  LaneState<NJ> pre;
-  if (wid == 0) pre = load_lane_state<NJ>(state, sl, E, K);
-  if (T == 1) {
-    route_token_split<NJ, NWV>(logits, E, k, lane, wid, sm.vkey, s_rank, s_z[0], s_ids, s_w);
-  } else {
-    for (int t = wid; t < T; t += NWV)
-      route_token<NJ>(logits + (size_t)t * E, E, k, lane, sm.vkey + wid * (kWave * NJ), s_z[wid],
-                      s_ids + t * k, s_w + t * k);
-  }
-  lds_barrier();
-  PlanOut<NJ> out;
   if (wid == 0) {
     plan_wave<NJ>(s_ids, P, E, K, pre, sm, out);
-    if (lane == 0) {
+    if (PAGE_IN && lane == 0) {
       const unsigned long long tk =
           __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (tk + 1) % gridDim.x == 0;
@@ -837,10 +794,12 @@ __global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __
   }
   lds_barrier();
   const int D = sm.warp[0], nH = sm.warp[1], nw = sm.warp[2];
-  if (wid == 0 && (lead || s_last))
-    plan_wave_store<NJ>(out, P, T, E, K, state, sl, dev, sm, D, nH, nw, s_last != 0, lead);
+  const bool lead = !PAGE_IN || blockIdx.x == 0;  // stores the plan, pairs and counters
+  const bool last = !PAGE_IN || s_last != 0;      // stores the table state
+  // wavefront 0 stores the plan while wavefronts 1 .. NWV-1 store the pairs
+  if (wid == 0 && (lead || last)) plan_wave_store<NJ>(out, P, T, E, K, state, sl, dev, sm, D, nH, nw, last, lead);
   if (lead) {
-    if (wid > 0) {
+    if (wid > 0) {  // per-pair id, weight, slot and wave
       for (int p = (int)threadIdx.x - kWave; p < P; p += NT - kWave) {
         const int e = s_ids[p];
         const int pos = sm.pos[e];
@@ -853,28 +812,33 @@ __global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __
     group_small<NWV, 1>(sm, s_ids, P, D, dev);
     add_dstats(dstats, T, P, D, nH, nw, kWave);
   }
-  // this workgroup's share of every missed record (the single wave's order
-  // positions nH .. D-1), 16-byte chunks, kCopyUnroll loads in flight per thread
-  const size_t n16 = stride / 16;  // records are 256-byte multiples
-  const size_t step = (size_t)gridDim.x * NT * kCopyUnroll;
-  for (int m = nH; m < D; ++m) {
-    const int e = sm.order_e[m], sl_ = sm.order_s[m];
-    const uint4* src = (const uint4*)(host + (size_t)e * stride);
-    uint4* dst = (uint4*)(slots + (size_t)sl_ * stride);
-    for (size_t i = (size_t)blockIdx.x * NT * kCopyUnroll + threadIdx.x; i < n16; i += step) {
-      uint4 v[kCopyUnroll];
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const size_t j = i + (size_t)u * NT;
-        if (j < n16) v[u] = src[j];
-      }
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const size_t j = i + (size_t)u * NT;
-        if (j < n16) dst[j] = v[u];
-      }
-    }
+  if constexpr (PAGE_IN) {
+    // this workgroup's share of every missed record (the single wave's order
+    // positions nH .. D-1)
+    for (int m = nH; m < D; ++m)
+      copy_record_share<NT, kCopyUnroll>(host + (size_t)sm.order_e[m] * stride, slots + (size_t)sm.order_s[m] * stride,
+                                         stride, blockIdx.x, gridDim.x);
+  } else {
+    publish(sm, E, T, P, D, nH, nw, hdr, seq);
   }
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int k, int K, uint8_t* state, StateLayout sl,
+                                                              PlanDev dev, PlanHdr* hdr, int32_t seq,
+                                                              long long* dstats) {
+  route_plan_body<NJ, false>(logits, T, E, k, K, state, sl, dev, hdr, seq, dstats, nullptr, nullptr, nullptr, 0);
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __restrict__ logits, int T,
+                                                                 int E, int k, int K, uint8_t* state,
+                                                                 StateLayout sl, PlanDev dev, long long* dstats,
+                                                                 unsigned long long* ticket,
+                                                                 const uint8_t* __restrict__ host,
+                                                                 uint8_t* __restrict__ slots, size_t stride) {
+  route_plan_body<NJ, true>(logits, T, E, k, K, state, sl, dev, nullptr, 0, dstats, ticket, host, slots, stride);
 }
 
 // ------------------------------------------------------------------ grouping
