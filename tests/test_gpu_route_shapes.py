@@ -53,7 +53,8 @@ def test_host_steps_across_table_shapes(E, k, K, B):
     p.close()
 
 
-@pytest.mark.parametrize("E,k,K,B", [(256, 8, 77, 1), (255, 6, 101, 3), (65, 4, 13, 3)])
+@pytest.mark.parametrize("E,k,K,B", [(256, 8, 77, 1), (255, 6, 101, 3), (65, 4, 13, 3), (64, 8, 64, 8),
+                                     (256, 8, 256, 4)])
 def test_device_steps_across_table_shapes(E, k, K, B):
     say("case: device-resolved route, E=%d k=%d K=%d B=%d, 16 steps" % (E, k, K, B))
     assert B * k <= K
