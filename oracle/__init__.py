@@ -27,7 +27,9 @@ What the method computes (and so what the oracle computes):
     MoE layer; paging does not change its result ([PE] "Can paging change the
     model's outputs?").
 
-All floating point is float64 (numpy). Integer results (top-k ids, slot
+All floating point is float64 (numpy) for parity; ``PagedLayer(dtype=float32)``
+takes the same steps in single precision and is the variant timed as the
+CPU baseline. Integer results (top-k ids, slot
 assignments, miss lists, wave counts, table state) are unique under the tie
 rules stated in ``router`` and ``lru``.
 
@@ -45,6 +47,12 @@ Pins (tests/test_oracle_*.py, all ``-m "not gpu"``):
   expert  -- SwiGLU against torch.nn.functional.silu / F.linear in float64;
   layer   -- paged output == unpaged output bitwise;
   stack   -- bf16 round-to-nearest-even against torch.bfloat16 conversion;
+             run_stack against an independent chain of unpaged layers and
+             torch's bf16 rounding (bitwise, over warm tables), and against a
+             torch-built MoE per layer; x0-fed, residual-free and
+             last-output-only compositions shown to differ;
+  float32 -- the single-precision variant against float64: same plans, outputs
+             within the float32 tolerance on every format;
   sizing  -- the worked example the [PE] preflight section prints, reproduced;
              slots for a memory budget against a brute-force search.
 No oracle function is "parity unpinned".

@@ -12,15 +12,16 @@ y = W_down h, SiLU(a) = a * sigmoid(a); no shared expert.
 import numpy as np
 
 
-def silu(a):
-    a = np.asarray(a, dtype=np.float64)
-    return a / (1.0 + np.exp(-a))
+def silu(a, dtype=np.float64):
+    a = np.asarray(a, dtype=dtype)
+    return a / (a.dtype.type(1.0) + np.exp(-a))
 
 
-def swiglu_expert(w_gate, w_up, w_down, x):
-    """x float64 [H] or [n, H] -> y [H] or [n, H]."""
-    x = np.asarray(x, dtype=np.float64)
+def swiglu_expert(w_gate, w_up, w_down, x, dtype=np.float64):
+    """x [H] or [n, H] -> y [H] or [n, H], computed in `dtype` (float64 for
+    parity; float32 is the variant timed as the CPU baseline)."""
+    x = np.asarray(x, dtype=dtype)
     g = x @ w_gate.T
     u = x @ w_up.T
-    h = silu(g) * u
+    h = silu(g, dtype) * u
     return h @ w_down.T

@@ -40,9 +40,15 @@ def bf16_bits(v):
 
 
 class PagedLayer:
-    """host_store: uint8 [E][stride]. Keeps its own CPU slot store [K][stride]."""
+    """host_store: uint8 [E][stride]. Keeps its own CPU slot store [K][stride].
 
-    def __init__(self, host_store, fmt, E, top_k, H, I, K, initial_fill=False, max_cached=48):
+    dtype: float64 (parity) or float32 (the same steps in single precision,
+    the variant timed as the CPU baseline; routing and the plan are the same).
+    """
+
+    def __init__(self, host_store, fmt, E, top_k, H, I, K, initial_fill=False, max_cached=48,
+                 dtype=np.float64):
+        self.dtype = dtype
         self.store = np.asarray(host_store, dtype=np.uint8)
         self.max_cached = max_cached
         self.fmt, self.E, self.top_k, self.H, self.I, self.K = fmt, E, top_k, H, I, K
@@ -69,7 +75,8 @@ class PagedLayer:
         if s not in self._cache:
             if len(self._cache) >= self.max_cached:
                 self._cache.pop(next(iter(self._cache)))
-            self._cache[s] = formats.decode_record(self.slots[s], self.fmt, self.H, self.I)
+            self._cache[s] = tuple(np.asarray(m, dtype=self.dtype) for m in
+                                   formats.decode_record(self.slots[s], self.fmt, self.H, self.I))
         return self._cache[s]
 
     def step(self, logits, x, compute=True):
@@ -85,8 +92,8 @@ class PagedLayer:
         plan = self.table.plan(ids, on_page_in=None)
         # replay the page-ins in wave order: a later wave may reuse a slot that
         # an earlier wave of the same step computed from
-        x = np.asarray(x, dtype=np.float64)
-        out = np.zeros((x.shape[0], self.H), dtype=np.float64) if compute else None
+        x = np.asarray(x, dtype=self.dtype)
+        out = np.zeros((x.shape[0], self.H), dtype=self.dtype) if compute else None
         for wave in plan.waves:
             for e, s in wave.misses:
                 self._page_in(e, s)
@@ -123,8 +130,8 @@ class PagedLayer:
         if rows.size == 0:
             return
         wg, wu, wd = weights
-        y = swiglu_expert(wg, wu, wd, x[rows])
-        out[rows] += w[rows, cols][:, None] * y
+        y = swiglu_expert(wg, wu, wd, x[rows], dtype=out.dtype)
+        out[rows] += w[rows, cols][:, None].astype(out.dtype) * y
 
     def unpaged_forward(self, logits, x):
         """The same layer computed straight from the host store (no slots),

@@ -98,16 +98,82 @@ def test_bf16_rne_vs_torch():
     assert np.array_equal(bf16_rne(v), ref)
 
 
-def test_stack_residual():
+def _torch_bf16(v):
+    """float64 -> bfloat16 -> float64 through torch's own conversion."""
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _tiny_stack_layers(cfg, n):
+    """n layers of the tiny workload whose stores differ (layer l: pool record
+    perm_l[e] for expert e), each with a cold table."""
+    stores = [gen.expert_store(cfg)[np.random.default_rng(70 + l).permutation(cfg.E)] for l in range(n)]
+    return stores, [PagedLayer(s, cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K) for s in stores]
+
+
+def test_stack_against_independent_chain():
+    """run_stack pinned against a chain built without it: fresh layers'
+    unpaged_forward (itself pinned to a torch-built MoE above) composed with
+    torch's bfloat16 rounding of x + out, layer by layer and over two tokens
+    (the second through warm tables). Bitwise: both sum each layer in the same
+    wave/expert order. A stack that fed x0 to every layer, skipped the
+    residual or reused one layer's output is shown to give a different answer,
+    so the comparison can fail for those mistakes."""
     cfg = W.CONFIGS[1]
-    store = gen.expert_store(cfg)
-    layers = [PagedLayer(store, cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K) for _ in range(3)]
+    n = 3
+    _, layers = _tiny_stack_layers(cfg, n)
+    stores, chain = _tiny_stack_layers(cfg, n)
+    assert not all(np.array_equal(stores[0], s) for s in stores[1:])
     rng = np.random.default_rng(2)
-    logits = [rng.standard_normal((1, cfg.E)).astype(np.float32) for _ in range(3)]
-    x0 = bf16_rne(rng.standard_normal((1, cfg.H)))
-    xf, outs, plans = run_stack(layers, logits, x0)
-    x = x0
-    for o in outs:
-        x = bf16_rne(x + o)
-    assert np.array_equal(x, xf)
-    assert len(plans) == 3
+    for tok in range(2):
+        logits = [rng.standard_normal((1, cfg.E)).astype(np.float32) for _ in range(n)]
+        x0 = _torch_bf16(rng.standard_normal((1, cfg.H)))
+        xf, outs, plans = run_stack(layers, logits, x0)
+        assert len(outs) == n and len(plans) == n
+        # independent chain: unpaged math of each layer, then advance the
+        # chain layer's table exactly as a step does (its output is not used)
+        x, ref_outs = x0, []
+        for l in range(n):
+            o = chain[l].unpaged_forward(logits[l], x)
+            _, _, _, p = chain[l].step(logits[l], x, compute=False)
+            assert p.n_waves == plans[l].n_waves and p.waves[0].misses == plans[l].waves[0].misses
+            ref_outs.append(o)
+            x = _torch_bf16(x + o)
+        for l in range(n):
+            assert np.array_equal(outs[l], ref_outs[l]), (tok, l)
+        assert np.array_equal(xf, x), tok
+        # also against the torch-built MoE on the same hidden states (tie-free logits)
+        xl = x0
+        for l in range(n):
+            t = _torch_moe(stores[l], cfg.fmt, cfg.top_k, cfg.H, cfg.I, logits[l], xl)
+            assert np.allclose(outs[l], t, rtol=1e-12, atol=1e-15)
+            xl = _torch_bf16(xl + t)
+        # negative controls: plausible composition mistakes change the result
+        fresh = _tiny_stack_layers(cfg, n)[1]
+        wrong_x0 = _torch_bf16(x0 + sum(fresh[l].unpaged_forward(logits[l], x0) for l in range(n)))
+        assert not np.array_equal(wrong_x0, xf)
+        no_residual = x0
+        for l in range(n):
+            no_residual = _torch_bf16(fresh[l].unpaged_forward(logits[l], no_residual))
+        assert not np.array_equal(no_residual, xf)
+        assert not np.array_equal(_torch_bf16(x0 + outs[-1]), xf)
+
+
+def test_float32_variant_matches_float64():
+    """The float32 oracle (timed as the CPU baseline) takes the same steps:
+    identical ids and plans, outputs within the float32 tolerance of the
+    float64 oracle, on every format and multi-wave steps."""
+    for fmt in (formats.F32, formats.BF16, formats.FP8, formats.INT4, formats.MXFP4):
+        lay64, rng = _multiwave_layer(fmt)
+        lay32 = PagedLayer(lay64.store, fmt, lay64.E, lay64.top_k, lay64.H, lay64.I, lay64.K,
+                           dtype=np.float32)
+        for _ in range(8):
+            B = int(rng.integers(1, 4))
+            logits = rng.standard_normal((B, lay64.E)).astype(np.float32)
+            x = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((B, lay64.H)).astype(np.float32)))
+            o64, i64, w64, p64 = lay64.step(logits, x)
+            o32, i32, w32, p32 = lay32.step(logits, x)
+            assert o32.dtype == np.float32
+            assert np.array_equal(i64, i32) and np.array_equal(p64.slot_ids, p32.slot_ids)
+            assert [w.misses for w in p64.waves] == [w.misses for w in p32.waves]
+            rms = np.sqrt(np.mean(o64 ** 2))
+            assert np.abs(o32 - o64).max() <= 1e-5 * rms, fmt
