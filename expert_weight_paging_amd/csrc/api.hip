@@ -45,6 +45,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct moe_layer {
   int E, k, H, I, K, fmt;
+  int device;                     // HIP device current at init (where the buffers live)
   RecLayout rl;
   size_t stride;
   const uint8_t* host_store;
@@ -185,6 +186,33 @@ bool is_pinned(const void* p) {
   return attr.type == hipMemoryTypeHost;
 }
 
+// Every byte of [p, p + n) lies in page-locked host memory: walks the range
+// allocation by allocation (each allocation's extent from the runtime), so a
+// range whose ends are pinned but whose middle is not (two allocations with a
+// gap between them) is refused. Where the runtime gives no extent, every
+// 4 KiB page is checked.
+bool range_pinned(const uint8_t* p, size_t n) {
+  const uintptr_t end = (uintptr_t)p + n;
+  uintptr_t cur = (uintptr_t)p;
+  while (cur < end) {
+    if (!is_pinned((const void*)cur)) return false;
+    void* base = nullptr;
+    size_t size = 0;
+    uintptr_t next = 0;
+    if (hipPointerGetAttribute(&base, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, (hipDeviceptr_t)cur) ==
+            hipSuccess &&
+        hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, (hipDeviceptr_t)cur) == hipSuccess &&
+        (uintptr_t)base <= cur && (uintptr_t)base + size > cur) {
+      next = (uintptr_t)base + size;
+    } else {
+      (void)hipGetLastError();
+      next = (cur | 4095) + 1;  // next 4 KiB page
+    }
+    cur = next;
+  }
+  return is_pinned(p + n - 1);
+}
+
 // Weight bytes of the gate/up and the down part of one record.
 double up_weight_bytes(const moe_layer* L) {
   const RecLayout& r = L->rl;
@@ -303,8 +331,10 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
   if (((uintptr_t)d->slot_store & 255) || ((uintptr_t)d->state & 7))
     return fail(MOE_ERR_INVALID_ARG, "slot_store must be 256-byte and state 8-byte aligned");
   const uint8_t* hs = (const uint8_t*)d->host_store;
-  if (!is_pinned(hs) || !is_pinned(hs + (size_t)d->num_experts * rl.stride - 1))
+  if (!range_pinned(hs, (size_t)d->num_experts * rl.stride))
     return fail(MOE_ERR_NOT_PINNED, "host_store is not page-locked host memory over its whole range");
+  if (d->self_check && d->num_slots < 2)
+    return fail(MOE_ERR_INVALID_ARG, "self_check places each expert in two different slots: needs K >= 2");
 
   moe_layer* L = new (std::nothrow) moe_layer();
   if (!L) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
@@ -323,6 +353,7 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
   L->copy = (hipStream_t)copy_stream;
   L->route = (hipStream_t)route_stream;
   L->initial_fill = d->initial_fill ? 1 : 0;
+  L->device = -1;
   L->fwd_recorded = L->copy_recorded = false;
   std::memset(&L->stats, 0, sizeof(L->stats));
   std::memset(&L->acc, 0, sizeof(L->acc));
@@ -341,6 +372,7 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
   void* hs_dev = nullptr;
   if (hipHostGetDevicePointer(&hs_dev, (void*)hs, 0) == hipSuccess) L->host_store_dev = (const uint8_t*)hs_dev;
   else (void)hipGetLastError();
+  if (hipGetDevice(&L->device) != hipSuccess) return bail(fail(MOE_ERR_HIP, "hipGetDevice failed"));
   if (hipMalloc((void**)&L->dstats, 8 * sizeof(long long)) != hipSuccess ||
       hipMemset(L->dstats, 0, 8 * sizeof(long long)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "device counters allocation failed"));
@@ -474,8 +506,8 @@ namespace {
 // `on`, if given, replaces the layer's route stream for this step.
 moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p, hipEvent_t after,
                       hipStream_t on) {
-  const hipStream_t rs = on ? on : L->route;
   if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
+  const hipStream_t rs = on ? on : L->route;
   if (p->layer != L) return fail(MOE_ERR_INVALID_ARG, "plan was created for another layer");
   if (T < 0 || T > p->max_tokens) return fail(MOE_ERR_INVALID_ARG, "num_tokens out of 0..max_tokens");
   if (T > 0 && !logits) return fail(MOE_ERR_INVALID_ARG, "null logits");
@@ -483,8 +515,15 @@ moe_status route_impl(moe_layer* L, const float* logits, int32_t T, moe_plan* p,
     return fail(MOE_ERR_STATE, "previous step of this layer has waves not yet forwarded");
 
   if (p->consumed_recorded && rs != L->compute) HIP_TRY(hipStreamWaitEvent(rs, p->ev_consumed, 0));
-  // a device-resolved step of this layer (compute stream) may still update the table state
-  if (L->dev_pending && rs != L->compute) HIP_TRY(hipStreamWaitEvent(rs, L->ev_fwd_done, 0));
+  // A device-resolved step of this layer may still update the table state on
+  // the compute stream, also one replayed from a captured graph (whose
+  // launches the library does not see): once this layer has had device steps,
+  // the route waits for everything enqueued on the compute stream so far.
+  if (L->dev_steps && rs != L->compute) {
+    HIP_TRY(hipEventRecord(L->ev_fwd_done, L->compute));
+    L->fwd_recorded = true;
+    HIP_TRY(hipStreamWaitEvent(rs, L->ev_fwd_done, 0));
+  }
   L->dev_pending = false;
   if (after) HIP_TRY(hipStreamWaitEvent(rs, after, 0));
   TimerRec tr{};
@@ -693,10 +732,16 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
   const int32_t* hoff = (const int32_t*)(p->hdr + 1) + 2 * L->E;  // CSR offsets, host copy
   auto pairs_in = [&](int lo, int n) { return hoff[lo + n] - hoff[lo]; };
   const bool gemm = T > MOE_MAX_GEMV_TOKENS;
-  // Splitting costs extra launches; it only pays while this wave's copies are
-  // still in flight.
-  const bool copies_pending = n_res < n_exp && L->copy_recorded &&
-                              hipEventQuery(L->ev_copied) == hipErrorNotReady;
+  // Whether to split is decided from the plan alone on the GEMV path, where the
+  // two launches add into out in a different order than one launch does: a
+  // wave with both resident and missed experts is always split, so a step's
+  // bits never depend on how far its copies had got. On the GEMM path the
+  // split only changes which launch fills an expert's rows of y, and the
+  // combine sums them in a fixed order, so there the split is taken only while
+  // the copies are still in flight (it costs extra launches).
+  const bool copies_pending =
+      n_res < n_exp && L->copy_recorded &&
+      (!gemm || hipEventQuery(L->ev_copied) == hipErrorNotReady);
   moe_status st;
   if (n_res > 0 && copies_pending) {
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_res, pairs_in(o_lo, n_res), T, x, out,
@@ -844,11 +889,12 @@ moe_status step_device_check(const moe_layer* L, const moe_plan* p, int32_t T) {
 // residual on the compute stream. With ps != compute the host records
 // L->ev_copied on ps and the compute stream waits for it (under capture the
 // pair becomes a graph dependency).
-moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
-                            float* out, uint16_t* x_res, hipStream_t ps, bool cap) {
+moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const float* logits, int32_t T,
+                            const void* x, float* out, uint16_t* x_res, hipStream_t ps, bool cap,
+                            bool no_timers) {
   const hipStream_t cs = L->compute;
   const bool timing = L->timing;
-  if (cap) L->timing = false;  // dispatch-stamped events are not captured
+  if (cap || no_timers) L->timing = false;  // dispatch-stamped events are not captured
   moe_status st = MOE_OK;
   do {
     TimerRec tr{}, tc{};
@@ -856,7 +902,7 @@ moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int3
       // one launch routes, plans and pages in (timed as the page-in; its ticket
       // counter is the layer's device counter 6)
       if ((st = timer_events(L, &tc))) break;
-      if (launch_route_plan_page_in(logits, T, L->E, L->k, L->K, L->state, p->dev, L->dstats,
+      if (launch_route_plan_page_in(logits, T, L->E, L->k, L->K, L->state, dev, L->dstats,
                                     (unsigned long long*)(L->dstats + 6), L->host_store_dev, L->slots,
                                     L->stride, ps, tc.a, tc.b) != hipSuccess) {
         st = fail(MOE_ERR_HIP, "route and page-in launch failed");
@@ -865,13 +911,13 @@ moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int3
       timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
     } else {
       if ((st = timer_events(L, &tr)) || (st = timer_events(L, &tc))) break;
-      if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, p->dev, nullptr, 0, ps, tr.a, tr.b,
+      if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, dev, nullptr, 0, ps, tr.a, tr.b,
                                   L->dstats) != hipSuccess) {
         st = fail(MOE_ERR_HIP, "route launch failed");
         break;
       }
       timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
-      if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, p->dev, L->E, L->K, ps, tc.a, tc.b) !=
+      if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, dev, L->E, L->K, ps, tc.a, tc.b) !=
           hipSuccess) {
         st = fail(MOE_ERR_HIP, "page-in launch failed");
         break;
@@ -886,19 +932,34 @@ moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int3
     }
     // at most min(T * top_k, E) experts; exactly top_k for one token
     const int n_max = std::min(T * L->k, L->E);
-    st = run_ffn(L, p->dev, p->h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr,
-                 nullptr, 0, T, false, x_res, p->dev.counts);
+    st = run_ffn(L, dev, h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr,
+                 nullptr, 0, T, false, x_res, dev.counts);
   } while (0);
   L->timing = timing;
   if (st) return st;
   if (!cap) {  // ordering for later host-driven calls on other streams
     HIP_TRY(hipEventRecord(L->ev_fwd_done, cs));
     L->fwd_recorded = true;
-    HIP_TRY(hipEventRecord(p->ev_consumed, cs));
-    p->consumed_recorded = true;
   }
   L->dev_steps = true;
   L->dev_pending = true;
+  return MOE_OK;
+}
+
+// Device-resolved single-wave step: route + plan (kept on the device,
+// counters in dstats) and the kernel page-in of the misses on stream `ps`,
+// then the expert FFN (expert count read on the device) and the optional stack
+// residual on the compute stream. With ps != compute the host records
+// L->ev_copied on ps and the compute stream waits for it (under capture the
+// pair becomes a graph dependency).
+moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
+                            float* out, uint16_t* x_res, hipStream_t ps, bool cap) {
+  moe_status st = step_device_core(L, p->dev, p->h, logits, T, x, out, x_res, ps, cap, false);
+  if (st) return st;
+  if (!cap) {
+    HIP_TRY(hipEventRecord(p->ev_consumed, L->compute));
+    p->consumed_recorded = true;
+  }
   p->valid = false;
   p->dev_routed = true;
   p->dev_tokens = T;
@@ -1215,7 +1276,9 @@ moe_status self_check(moe_layer* L) {
     L->timing = false;
     for (int perm = 0; perm < 2 && !result; ++perm) {
       for (int i = 0; i < n && !result; ++i) {
-        const int slot = perm == 0 ? i : (L->K - 1 - i);
+        // second placement: every expert shifted by ceil(K / 2) slots (mod K),
+        // a different slot for each expert whenever K >= 2 (checked at init)
+        const int slot = perm == 0 ? i : (i + (L->K + 1) / 2) % L->K;
         if (hipMemcpy(L->slots + (size_t)slot * L->stride, L->host_store + (size_t)i * L->stride,
                       L->stride, hipMemcpyHostToDevice) != hipSuccess ||
             hipMemcpy(b + o_os, &slot, 4, hipMemcpyHostToDevice) != hipSuccess) {

@@ -145,7 +145,7 @@ typedef struct moe_layer_desc {
   void* state;           /* device, moe_state_bytes(E, K); caller-owned          */
   int32_t initial_fill;  /* 0: empty table; 1: experts 0..K-1 copied into slots
                             0..K-1 (stamp 0) at init and at reset                */
-  int32_t self_check;    /* 1: run the slot-independence check at init           */
+  int32_t self_check;    /* 1: run the slot-independence check at init (K >= 2)  */
 } moe_layer_desc;
 
 typedef struct moe_layer moe_layer;
@@ -166,7 +166,11 @@ moe_status moe_layer_init(const moe_layer_desc* desc, void* compute_stream,
                           void* copy_stream, void* route_stream, moe_layer** out);
 
 /* Restore the initial table (empty, or experts 0..K-1 when initial_fill),
- * synchronously. Statistics are kept. */
+ * synchronously, after the layer's streams have drained ([PE] "What does
+ * Paged Experts actually do?": the K resident slots start empty or hold the
+ * first K experts; this returns a layer to that state between runs).
+ * Statistics are kept. MOE_ERR_INVALID_ARG for a null layer, MOE_ERR_HIP if a
+ * synchronisation or copy fails. */
 moe_status moe_layer_reset(moe_layer* layer);
 void moe_layer_destroy(moe_layer* layer);
 
@@ -225,15 +229,26 @@ moe_status moe_plan_get_wave(const moe_plan* plan, int32_t wave, moe_wave_info* 
 moe_status moe_plan_read(const moe_plan* plan, int32_t* ids, float* weights,
                          int32_t* slot_ids, int32_t* wave_of);
 
-/* Page in the misses of one wave: each miss's whole host record -> its slot by
- * hipMemcpyAsync (misses that are consecutive in both stores, expert e + 1 into
+/* Page in the misses of one wave ([PE] "What does Paged Experts actually
+ * do?": only the routed experts that are not resident are copied from the
+ * pinned host store into slots; "What happens with more than one request?":
+ * every wave has its own page-in; "Can paging change the model's outputs?":
+ * the whole record moves, so no per-expert tensor is left behind): each
+ * miss's whole host record -> its slot by hipMemcpyAsync (misses that are consecutive in both stores, expert e + 1 into
  * slot s + 1 after e into s, share one copy), on copy_stream, after the
  * layer's previous forward has finished
  * (a victim slot may still be read by it). Waves are paged in and computed in
- * order: page_in(w) requires forward(w-1) to have been issued. */
+ * order: page_in(w) requires forward(w-1) to have been issued.
+ * Errors: MOE_ERR_INVALID_ARG (null layer or plan), MOE_ERR_STATE (plan not
+ * this layer's current step, wave out of order, corrupt miss list),
+ * MOE_ERR_HIP (a copy could not be enqueued). */
 moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
 
-/* Expert math of one wave on compute_stream, after that wave's page-in:
+/* Expert math of one wave on compute_stream, after that wave's page-in
+ * ([PE] "What does Paged Experts actually do?": once a wave's experts are in
+ * their slots the MoE computation runs over the slots; its output for a token
+ * is the router-weighted sum of its top_k SwiGLU experts, 3 matrices of H x I
+ * each as "Why is it fast when experts keep crossing PCIe?" sizes them):
  *   x:   device, [T][H], float32 for MOE_FMT_F32 else bfloat16
  *   out: device, float32 [T][H]; wave 0 writes it, later waves add to it
  * out[t] = sum over (t, j) in this wave of w_tj * W_d (SiLU(W_gate x_t) *
@@ -241,7 +256,12 @@ moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
  * the weights are streamed once per wave (GEMV path); with more tokens the
  * token-grouped bf16 MFMA GEMM runs (H and I multiples of 128): FP8, int4 and
  * MXFP4 records are first expanded to bf16 in the plan's workspace (each
- * weight rounded to nearest even), f32 layers are limited to the GEMV path. */
+ * weight rounded to nearest even), f32 layers are limited to the GEMV path.
+ * A wave with both resident and missed experts is computed in two launches on
+ * the GEMV path (residents first, while the copies are in flight), decided
+ * from the plan alone, so results are bitwise reproducible.
+ * Errors: MOE_ERR_INVALID_ARG (null or misaligned x/out), MOE_ERR_STATE
+ * (forward without its page-in, out of order), MOE_ERR_HIP. */
 moe_status moe_forward(moe_layer* layer, const moe_plan* plan, int32_t wave,
                        const void* x, float* out);
 
@@ -296,7 +316,10 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
  * steps are kept on the device and added by moe_layer_stats. Errors:
  * MOE_ERR_INVALID_ARG (sizes, pointers, alignment), MOE_ERR_STATE (unmapped
  * store, unfinished host step), MOE_ERR_FORMAT (x_res on an f32 layer),
- * MOE_ERR_HIP. */
+ * MOE_ERR_HIP. A later host-driven moe_route of the layer waits for all work
+ * enqueued on the compute stream by then; replays of a captured graph must
+ * therefore be launched on the compute stream (or be ordered before the
+ * route by the caller). */
 moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits,
                            int32_t num_tokens, const void* x, float* out, void* x_res);
 
@@ -353,7 +376,12 @@ typedef struct moe_stats {
 moe_status moe_layer_stats(const moe_layer* layer, moe_stats* out);
 
 /* Synchronous copy of the table state to host buffers (any may be NULL):
- * slot_expert int32 [K], expert_slot int32 [E], stamp int64 [K], clock. */
+ * slot_expert int32 [K], expert_slot int32 [E], stamp int64 [K], clock
+ * ([PE] "TL;DR" and [LRU] "The fix": which expert each slot holds and when it
+ * was last used decide the least-recently-used victim; exported so that a
+ * caller can check the table against a reference). Waits for the layer's
+ * route and compute streams. MOE_ERR_INVALID_ARG for a null layer,
+ * MOE_ERR_HIP if the copy fails. */
 moe_status moe_layer_get_state(moe_layer* layer, int32_t* slot_expert, int32_t* expert_slot,
                                int64_t* stamp, int64_t* clock);
 

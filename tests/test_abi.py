@@ -110,3 +110,33 @@ def test_preflight_matches_oracle():
         assert got["reuse_implied"] == (ref["verdict"] == "reuse implied")
     with pytest.raises(ewp.MoeError):
         ewp.preflight(48, 128, 8, 2.43, 129, 50.0, 205.6, kv)   # K > E
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_null_handles_are_refused_without_a_gpu():
+    """Every entry point that takes a layer or plan handle returns
+    MOE_ERR_INVALID_ARG (-1) for a null one, before any HIP call (the header
+    promises that nothing aborts across the ABI)."""
+    import expert_weight_paging_amd as ewp
+    L = ewp.lib()
+    assert L.moe_route(None, None, 1, None) == -1
+    assert L.moe_route(None, None, 0, None) == -1
+    assert L.moe_page_in(None, None, 0) == -1
+    assert L.moe_forward(None, None, 0, None, None) == -1
+    assert L.moe_layer_reset(None) == -1
+    assert L.moe_layer_stats(None, None) == -1
+    assert L.moe_layer_get_state(None, None, None, None, None) == -1
+    assert L.moe_plan_get_info(None, None) == -1
+    assert L.moe_plan_get_wave(None, 0, None) == -1
+    assert L.moe_plan_read(None, None, None, None, None) == -1
+    assert L.moe_plan_create(None, 1, None) == -1
+    assert L.moe_step_device(None, None, None, 1, None, None, None) == -1
+    assert L.moe_step_token_waves(None, None, None, 1, None, None, None) == -1
+    assert L.moe_stack_forward(None, None, 0, None, 1, None, None, 0) == -1
+    assert L.moe_stack_forward_device(None, None, 0, None, 1, None, None, 0) == -1
+    assert L.moe_timing_enable(None, 1) == -1
+    assert L.moe_timing_read(None, None) == -1
+    assert L.moe_layer_init(None, None, None, None, None) == -1
+    L.moe_layer_destroy(None)
+    L.moe_plan_destroy(None)
+    assert b"null" in L.moe_last_error()

@@ -190,3 +190,105 @@ def test_error_codes():
     plan.close()
     layer.close()                                  # destroys h exactly once
     host.free()
+
+
+def test_self_check_needs_two_slots_and_odd_k_passes():
+    """The check places each expert in two different slots: K = 1 is refused at
+    init, odd K (where a mirrored placement would keep the middle expert in
+    its slot) passes."""
+    say("case: self-check with K = 1 and K = 3")
+    E, H, I = 8, 64, 32
+    fill = _tiny_fill(E, H, I, seed=3)
+    p = PairedLayer(E, 2, H, I, 3, gen.F32, fill, max_tokens=1, self_check=True)
+    p.close()
+    with pytest.raises(ewp.MoeError) as ei:
+        PairedLayer(E, 1, H, I, 1, gen.F32, fill, max_tokens=1, self_check=True)
+    assert ei.value.name == "MOE_ERR_INVALID_ARG"
+
+
+class _PtrAttr(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int), ("device", ctypes.c_int), ("devicePointer", ctypes.c_void_p),
+                ("hostPointer", ctypes.c_void_p), ("isManaged", ctypes.c_int),
+                ("allocationFlags", ctypes.c_uint)]
+
+
+def _is_host_pinned(hip, addr):
+    a = _PtrAttr()
+    if hip.hipPointerGetAttributes(ctypes.byref(a), ctypes.c_void_p(addr)) != 0:
+        hip.hipGetLastError()
+        return False
+    return a.type == 1
+
+
+def test_store_with_unpinned_middle_is_refused():
+    """A store whose first and last bytes are page-locked but whose middle is
+    not (two pinned allocations with a gap between them) is refused with
+    MOE_ERR_NOT_PINNED ([PE] "A rollout checklist": the whole store must be
+    pinned, refused at startup); a store inside one allocation is accepted."""
+    say("case: host store spanning two pinned allocations with an unpinned gap")
+    H, I, K = 64, 32, 4
+    rb = ewp.record_bytes(0, H, I)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    L = ewp.lib()
+    bufs = [L.moe_host_alloc(1 << 20) for _ in range(6)]
+    assert all(bufs)
+    try:
+        def extent(ptr):               # [base, base + size) of the allocation holding ptr
+            base, size = ctypes.c_void_p(), ctypes.c_size_t()
+            assert hip.hipPointerGetAttribute(ctypes.byref(base), 11, ctypes.c_void_p(ptr)) == 0
+            assert hip.hipPointerGetAttribute(ctypes.byref(size), 12, ctypes.c_void_p(ptr)) == 0
+            return base.value, base.value + size.value
+        order = sorted(bufs)
+        pick = None
+        for a, c in zip(order, order[1:]):
+            a_end = extent(a)[1]
+            c_end = extent(c)[1]
+            E = -(-(c - a + 1) // rb)
+            if (c > a_end and E <= 1024 and a + E * rb <= c_end and
+                    not _is_host_pinned(hip, a_end) and not _is_host_pinned(hip, c - 1)):
+                pick = (a, E)
+                break
+        if pick is None:
+            pytest.skip("no two pinned allocations with an unpinned gap within 1024 records")
+        a, E = pick
+        slots, state = ewp.alloc_layer_buffers(E, K, rb, "cuda")
+        assert _is_host_pinned(hip, a) and _is_host_pinned(hip, a + E * rb - 1)
+        st, h = _init(_desc(E=E, K=K, host=a, slots=slots.data_ptr(), state=state.data_ptr()))
+        assert st == -2, (st, L.moe_last_error())
+        # the same layer over one allocation is fine
+        st, h = _init(_desc(E=8, K=K, host=a, slots=slots.data_ptr(), state=state.data_ptr()))
+        assert st == 0, L.moe_last_error()
+        L.moe_layer_destroy(h)
+    finally:
+        for b in bufs:
+            L.moe_host_free(b)
+
+
+def test_host_step_bits_do_not_depend_on_copy_progress():
+    """A host-driven decode step gives the same bits whether its copies are
+    still in flight when the forward is enqueued or already complete: the
+    resident-first split is decided from the plan, not from timing."""
+    cfg = W.CONFIGS[2]
+    say("case: bf16 layer, 16 host-driven steps, copies complete vs in flight")
+    logits, x = gen.decode_inputs(cfg, 1, steps=16)
+    outs = []
+    for sync_copies in (False, True):
+        s = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+        p = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt,
+                        lambda a: gen.expert_store(cfg, out=a), max_tokens=1, streams=s)
+        lg = torch.from_numpy(logits).cuda()
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        out = torch.empty(1, cfg.H, dtype=torch.float32, device="cuda")
+        res = []
+        for t in range(16):
+            info = p.gpu.route(p.plan, lg[t])
+            for w in range(info["num_waves"]):
+                p.gpu.page_in(p.plan, w)
+                if sync_copies:
+                    torch.cuda.synchronize()
+                p.gpu.forward(p.plan, w, xd[t], out)
+            torch.cuda.synchronize()
+            res.append(out.cpu().numpy().copy())
+        outs.append(np.stack(res))
+        p.close()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
