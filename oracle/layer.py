@@ -11,9 +11,15 @@ into it exactly as the planner says, and computes every expert FROM ITS SLOT,
 so that a planner or copy mistake shows up in the output. ``unpaged_forward``
 computes from the store directly; the two agree bitwise.
 
-Stack reading (no attention, no norm): x_next = bf16_rne(x + moe(x)).
+Stack reading (attention omitted): every layer reads the residual stream
+through a unit-gain RMSNorm, as the MoE block of the model the pages run
+(Qwen3-30B-A3B, [PE] "What does Paged Experts actually do?") does, and adds
+its output back: a = bf16_rne(rms_norm(x)), x_next = bf16_rne(x + moe(a)).
+Without the norm the SwiGLU experts make the hidden state grow about
+quadratically per layer, past every 16- and 32-bit range within 48 layers.
 """
 import numpy as np
+import xxhash
 
 from . import formats
 from .expert import swiglu_expert
@@ -33,6 +39,15 @@ def bf16_rne(v):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
+RMS_EPS = 1e-6
+
+
+def rms_norm(x, eps=RMS_EPS):
+    """Unit-gain RMSNorm over the last axis, float64: x / sqrt(mean(x^2) + eps)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
 def bf16_bits(v):
     """float64 values that are exact bf16 -> uint16 bit patterns."""
     f = np.asarray(v, dtype=np.float64).astype(np.float32)
@@ -47,8 +62,12 @@ class PagedLayer:
     """
 
     def __init__(self, host_store, fmt, E, top_k, H, I, K, initial_fill=False, max_cached=48,
-                 dtype=np.float64):
+                 dtype=np.float64, decode_cache=None):
         self.dtype = dtype
+        # optional dict shared by several layers: decoded weights keyed by a
+        # 128-bit hash of the record bytes (decoding is a function of those
+        # bytes alone), so a record that several layers hold is decoded once
+        self.decode_cache = decode_cache
         self.store = np.asarray(host_store, dtype=np.uint8)
         self.max_cached = max_cached
         self.fmt, self.E, self.top_k, self.H, self.I, self.K = fmt, E, top_k, H, I, K
@@ -70,13 +89,25 @@ class PagedLayer:
         self.slots[s] = self.store[e]
         self._cache.pop(s, None)
 
+    def _decode(self, rec):
+        """Weights (gate, up, down) of one record's bytes, in the layer's dtype;
+        through the shared memo when there is one."""
+        key = None
+        if self.decode_cache is not None:
+            key = (xxhash.xxh3_128_digest(rec), np.dtype(self.dtype).str, self.fmt, self.H, self.I)
+            if key in self.decode_cache:
+                return self.decode_cache[key]
+        w = tuple(np.asarray(m, dtype=self.dtype) for m in formats.decode_record(rec, self.fmt, self.H, self.I))
+        if key is not None:
+            self.decode_cache[key] = w
+        return w
+
     def _slot_weights(self, s):
         # decoded from the slot's bytes; invalidated on every page-in into s
         if s not in self._cache:
             if len(self._cache) >= self.max_cached:
                 self._cache.pop(next(iter(self._cache)))
-            self._cache[s] = tuple(np.asarray(m, dtype=self.dtype) for m in
-                                   formats.decode_record(self.slots[s], self.fmt, self.H, self.I))
+            self._cache[s] = self._decode(self.slots[s])
         return self._cache[s]
 
     def step(self, logits, x, compute=True):
@@ -146,13 +177,13 @@ class PagedLayer:
         plan = dry.plan(ids)
         for wave in plan.waves:
             for e in wave.experts:
-                self._apply(formats.decode_record(self.store[e], self.fmt, self.H, self.I),
-                            e, ids, w, x, out)
+                self._apply(self._decode(self.store[e]), e, ids, w, x, out)
         return out
 
 
 def run_stack(layers, logits_per_layer, x0):
-    """Stack of paged layers: x_{l+1} = bf16_rne(x_l + out_l).
+    """Stack of paged layers: a_l = bf16_rne(rms_norm(x_l)),
+    x_{l+1} = bf16_rne(x_l + out_l) with out_l the layer's MoE output on a_l.
 
     logits_per_layer: list of float32 [B,E]; x0: values [B,H] (bf16-exact).
     Returns (x_final, per-layer outputs, per-layer plans).
@@ -160,7 +191,7 @@ def run_stack(layers, logits_per_layer, x0):
     x = np.asarray(x0, dtype=np.float64)
     outs, plans = [], []
     for layer, logits in zip(layers, logits_per_layer):
-        out, _, _, plan = layer.step(logits, x)
+        out, _, _, plan = layer.step(logits, bf16_rne(rms_norm(x)))
         outs.append(out)
         plans.append(plan)
         x = bf16_rne(x + out)

@@ -7,7 +7,7 @@ import torch.nn.functional as F
 import workloads as W
 from oracle import formats
 from oracle.expert import silu, swiglu_expert
-from oracle.layer import PagedLayer, bf16_rne, run_stack
+from oracle.layer import RMS_EPS, PagedLayer, bf16_rne, rms_norm, run_stack
 from workloads import gen
 
 
@@ -103,6 +103,24 @@ def _torch_bf16(v):
     return torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
 
 
+def _torch_norm(v):
+    """Unit-gain RMSNorm through torch's own routine, float64."""
+    t = torch.from_numpy(np.asarray(v, np.float64))
+    return F.rms_norm(t, (t.shape[-1],), eps=RMS_EPS).numpy()
+
+
+def test_rms_norm_vs_torch_and_closed_forms():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((7, 96)) * np.exp2(rng.integers(-8, 8, (7, 1)))
+    assert np.allclose(rms_norm(x), _torch_norm(x), rtol=1e-14, atol=0)
+    c = 3.0                                            # a constant row c: c / sqrt(c^2 + eps)
+    assert np.allclose(rms_norm(np.full((1, 64), c)), c / np.sqrt(c * c + RMS_EPS), rtol=1e-15)
+    big = x * 1e3                                      # norm(c x, c^2 eps) = norm(x, eps)
+    assert np.allclose(rms_norm(big, eps=1e6 * RMS_EPS), rms_norm(x), rtol=1e-13)
+    assert np.allclose(np.mean(rms_norm(x, eps=0.0) ** 2, axis=-1), 1.0, rtol=1e-13)
+    assert np.array_equal(rms_norm(np.zeros((1, 8))), np.zeros((1, 8)))
+
+
 def _tiny_stack_layers(cfg, n):
     """n layers of the tiny workload whose stores differ (layer l: pool record
     perm_l[e] for expert e), each with a cold table."""
@@ -111,13 +129,14 @@ def _tiny_stack_layers(cfg, n):
 
 
 def test_stack_against_independent_chain():
-    """run_stack pinned against a chain built without it: fresh layers'
-    unpaged_forward (itself pinned to a torch-built MoE above) composed with
-    torch's bfloat16 rounding of x + out, layer by layer and over two tokens
-    (the second through warm tables). Bitwise: both sum each layer in the same
-    wave/expert order. A stack that fed x0 to every layer, skipped the
-    residual or reused one layer's output is shown to give a different answer,
-    so the comparison can fail for those mistakes."""
+    """run_stack pinned against a chain built without it: torch's RMSNorm and
+    bfloat16 rounding of the layer input, fresh layers' unpaged_forward
+    (itself pinned to a torch-built MoE above), torch's bfloat16 rounding of
+    x + out, layer by layer and over two tokens (the second through warm
+    tables). Bitwise: both sum each layer in the same wave/expert order. A
+    stack that fed x0 to every layer, skipped the residual or the norm, or
+    reused one layer's output is shown to give a different answer, so the
+    comparison can fail for those mistakes."""
     cfg = W.CONFIGS[1]
     n = 3
     _, layers = _tiny_stack_layers(cfg, n)
@@ -133,8 +152,9 @@ def test_stack_against_independent_chain():
         # chain layer's table exactly as a step does (its output is not used)
         x, ref_outs = x0, []
         for l in range(n):
-            o = chain[l].unpaged_forward(logits[l], x)
-            _, _, _, p = chain[l].step(logits[l], x, compute=False)
+            a = _torch_bf16(_torch_norm(x))
+            o = chain[l].unpaged_forward(logits[l], a)
+            _, _, _, p = chain[l].step(logits[l], a, compute=False)
             assert p.n_waves == plans[l].n_waves and p.waves[0].misses == plans[l].waves[0].misses
             ref_outs.append(o)
             x = _torch_bf16(x + o)
@@ -144,17 +164,22 @@ def test_stack_against_independent_chain():
         # also against the torch-built MoE on the same hidden states (tie-free logits)
         xl = x0
         for l in range(n):
-            t = _torch_moe(stores[l], cfg.fmt, cfg.top_k, cfg.H, cfg.I, logits[l], xl)
+            t = _torch_moe(stores[l], cfg.fmt, cfg.top_k, cfg.H, cfg.I, logits[l], _torch_bf16(_torch_norm(xl)))
             assert np.allclose(outs[l], t, rtol=1e-12, atol=1e-15)
             xl = _torch_bf16(xl + t)
         # negative controls: plausible composition mistakes change the result
         fresh = _tiny_stack_layers(cfg, n)[1]
-        wrong_x0 = _torch_bf16(x0 + sum(fresh[l].unpaged_forward(logits[l], x0) for l in range(n)))
+        a0 = _torch_bf16(_torch_norm(x0))
+        wrong_x0 = _torch_bf16(x0 + sum(fresh[l].unpaged_forward(logits[l], a0) for l in range(n)))
         assert not np.array_equal(wrong_x0, xf)
         no_residual = x0
         for l in range(n):
-            no_residual = _torch_bf16(fresh[l].unpaged_forward(logits[l], no_residual))
+            no_residual = _torch_bf16(fresh[l].unpaged_forward(logits[l], _torch_bf16(_torch_norm(no_residual))))
         assert not np.array_equal(no_residual, xf)
+        no_norm = x0
+        for l in range(n):
+            no_norm = _torch_bf16(no_norm + fresh[l].unpaged_forward(logits[l], no_norm))
+        assert not np.array_equal(no_norm, xf)
         assert not np.array_equal(_torch_bf16(x0 + outs[-1]), xf)
 
 
@@ -177,3 +202,30 @@ def test_float32_variant_matches_float64():
             assert [w.misses for w in p64.waves] == [w.misses for w in p32.waves]
             rms = np.sqrt(np.mean(o64 ** 2))
             assert np.abs(o32 - o64).max() <= 1e-5 * rms, fmt
+
+
+def test_shared_decode_cache_changes_nothing():
+    """Layers sharing a decode memo (records keyed by a hash of their bytes)
+    give bitwise the outputs of layers that decode every slot themselves, and
+    a planted copy of the wrong record is still visible through the memo."""
+    cfg = W.CONFIGS[1]
+    stores, plain = _tiny_stack_layers(cfg, 3)
+    memo = {}
+    cached = [PagedLayer(s, cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, decode_cache=memo)
+              for s in stores]
+    rng = np.random.default_rng(9)
+    for _ in range(6):
+        logits = [rng.standard_normal((2, cfg.E)).astype(np.float32) for _ in range(3)]
+        x0 = bf16_rne(rng.standard_normal((2, cfg.H)))
+        a = run_stack(plain, logits, x0)
+        b = run_stack(cached, logits, x0)
+        assert np.array_equal(a[0], b[0]) and all(np.array_equal(u, v) for u, v in zip(a[1], b[1]))
+    assert 0 < len(memo) <= cfg.E                  # the three layers hold permutations of one pool
+    lay = PagedLayer(stores[0], cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, decode_cache=memo)
+    logits = rng.standard_normal((1, cfg.E)).astype(np.float32)
+    x = rng.standard_normal((1, cfg.H))
+    ref = lay.unpaged_forward(logits, x)
+    orig = lay._page_in
+    lay._page_in = lambda e, s: orig((e + 1) % lay.E, s)        # planted mistake
+    out, *_ = lay.step(logits, x)
+    assert not np.allclose(out, ref)
