@@ -79,6 +79,8 @@ EXPORTS = {
     "moe_page_in": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
     "moe_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "moe_rmsnorm_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p]),
     "moe_residual_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int64, ctypes.c_void_p]),
     "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
@@ -357,6 +359,13 @@ def timing_floor(stream=None, reps=100):
     us = ctypes.c_double()
     _check(lib().moe_timing_floor(_stream(stream), int(reps), ctypes.byref(us)))
     return us.value
+
+
+def rmsnorm_bf16(x, a, stream=None):
+    """a = bf16_rne(x / sqrt(mean(x^2) + 1e-6)) per row (x, a bf16 [T][H], may alias): the
+    input of every layer of a stack."""
+    T, H = x.shape
+    _check(lib().moe_rmsnorm_bf16(_ptr(x), _ptr(a), int(T), int(H), _stream(stream)))
 
 
 def residual_bf16(x_in, out, x_out, stream=None):

@@ -87,6 +87,7 @@ struct moe_plan {
   uint16_t* hb_lo;    // GEMM scratch (h low part)
   float* y;           // GEMM scratch
   uint8_t* wdq;       // GEMM scratch, quantised formats: the wave's records as bf16
+  uint16_t* xn;       // GEMM scratch: the normalised activations of a stack layer [T][H] bf16
   int gemv_pairs;     // capacity of h in pairs
   hipEvent_t ev_consumed;
   bool consumed_recorded;
@@ -235,7 +236,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res = nullptr,
-                   const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr);
+                   const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr, int norm = 0);
 
 moe_status self_check(moe_layer* L);
 
@@ -440,12 +441,13 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
                o_pl = take(4 * P), o_pp = take(4 * P), o_cnt = take(16);
   p->gemv_pairs = (int)std::min<size_t>(P, (size_t)MOE_MAX_GEMV_TOKENS * L->k);
   const size_t o_h = take(sizeof(float) * (size_t)p->gemv_pairs * L->I);
-  size_t o_hb = 0, o_hl = 0, o_y = 0;
+  size_t o_hb = 0, o_hl = 0, o_y = 0, o_xn = 0;
   size_t o_wq = 0;
   if (gemm) {
     o_hb = take(2 * P * L->I);
     o_hl = take(2 * P * L->I);
     o_y = take(4 * P * L->H);
+    o_xn = take(2 * (size_t)max_tokens * L->H);
     // a wave holds at most min(K, E) experts; each expanded to a bf16 record
     if (L->fmt != MOE_FMT_BF16)
       o_wq = take((size_t)std::min(L->K, L->E) * rec_layout(MOE_FMT_BF16, L->H, L->I).stride);
@@ -470,6 +472,7 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->hb = gemm ? (uint16_t*)(b + o_hb) : nullptr;
   p->hb_lo = gemm ? (uint16_t*)(b + o_hl) : nullptr;
   p->y = gemm ? (float*)(b + o_y) : nullptr;
+  p->xn = gemm ? (uint16_t*)(b + o_xn) : nullptr;
   p->wdq = (gemm && L->fmt != MOE_FMT_BF16) ? b + o_wq : nullptr;
   const size_t hbytes = sizeof(PlanHdr) + sizeof(int32_t) * (3 * E + 1);
   if (hipHostMalloc((void**)&p->hdr, hbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
@@ -667,7 +670,7 @@ moe_status moe_page_in(moe_layer* L, const moe_plan* p, int32_t w) {
 
 namespace {
 moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out,
-                        uint16_t* x_res);
+                        uint16_t* x_res, int norm = 0);
 }
 
 moe_status moe_forward(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out) {
@@ -710,9 +713,12 @@ void victims_first(const moe_layer* L, const moe_plan* p, int w, int o_lo, int n
 }
 
 // x_res, if given, receives the stack residual bf16_rne(x_res + out) from the
-// kernel that completes out (only on a step's last wave).
+// kernel that completes out (only on a step's last wave). norm: x is a stack
+// layer's residual stream and the experts read its unit-gain RMSNorm (GEMV
+// path: computed by the up kernels; GEMM path: by a norm kernel into the
+// plan's workspace before wave 0).
 moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* x, float* out,
-                        uint16_t* x_res) {
+                        uint16_t* x_res, int norm) {
   if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
   if (L->cur_plan != p) return fail(MOE_ERR_STATE, "plan is not this layer's current step");
   if (w != L->next_fwd || L->next_page != w + 1)
@@ -722,6 +728,12 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
   if (((uintptr_t)x & 15) || ((uintptr_t)out & 15))
     return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_routed, 0));
+  if (norm && T > MOE_MAX_GEMV_TOKENS) {
+    if (!p->xn) return fail(MOE_ERR_STATE, "plan has no normalisation workspace");
+    if (w == 0) HIP_TRY(launch_rmsnorm((const uint16_t*)x, p->xn, T, L->H, L->compute));
+    x = p->xn;
+    norm = 0;
+  }
   const int K = L->K, D = p->info.num_distinct, nH = p->info.num_hits;
   const int o_lo = w * K, n_exp = std::min(K, D - o_lo);
   // The wave order lists the experts that were resident first: they can be
@@ -745,12 +757,12 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
   moe_status st;
   if (n_res > 0 && copies_pending) {
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_res, pairs_in(o_lo, n_res), T, x, out,
-                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false, nullptr, nullptr, p->wdq);
+                 w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false, nullptr, nullptr, p->wdq, norm);
     if (st) return st;
     HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
     st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo + n_res, n_exp - n_res,
                  pairs_in(o_lo + n_res, n_exp - n_res), T, x, out, w > 0 || !gemm, p->dev.pair_pos,
-                 p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
+                 p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq, norm);
     if (st) return st;
   } else {
     if (L->copy_recorded) HIP_TRY(hipStreamWaitEvent(L->compute, L->ev_copied, 0));
@@ -768,15 +780,15 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
     if (v_n > 0 && v_n < n_exp) {
       const int r_lo = v_lo == o_lo ? o_lo + v_n : o_lo, r_n = n_exp - v_n;
       st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, v_lo, v_n, pairs_in(v_lo, v_n), T, x, out, w > 0,
-                   p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false, nullptr, nullptr, p->wdq);
+                   p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/false, nullptr, nullptr, p->wdq, norm);
       if (st) return st;
       HIP_TRY(hipEventRecord(L->ev_victims_free, L->compute));
       L->victims_free_wave = w;
       st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, r_lo, r_n, pairs_in(r_lo, r_n), T, x, out, w > 0,
-                   p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
+                   p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq, norm);
     } else {
       st = run_ffn(L, p->dev, p->h, p->hb, p->hb_lo, p->y, o_lo, n_exp, pairs_in(o_lo, n_exp), T, x, out,
-                   w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq);
+                   w > 0, p->dev.pair_pos, p->dev.wave_of, w, T, /*combine=*/gemm, x_res, nullptr, p->wdq, norm);
     }
     if (st) return st;
   }
@@ -789,6 +801,16 @@ moe_status forward_impl(moe_layer* L, const moe_plan* p, int32_t w, const void* 
   return MOE_OK;
 }
 }  // namespace
+
+moe_status moe_rmsnorm_bf16(const void* x, void* a, int32_t T, int32_t H, void* stream) {
+  if (T < 0 || H < 8 || (H & 7) || (T > 0 && (!x || !a)))
+    return fail(MOE_ERR_INVALID_ARG, "bad norm arguments (H must be a positive multiple of 8)");
+  if (((uintptr_t)x & 15) || ((uintptr_t)a & 15))
+    return fail(MOE_ERR_INVALID_ARG, "x and a must be 16-byte aligned");
+  if ((size_t)H * 2 > 64 * 1024) return fail(MOE_ERR_INVALID_ARG, "H above 32768");
+  HIP_TRY(launch_rmsnorm((const uint16_t*)x, (uint16_t*)a, T, H, (hipStream_t)stream));
+  return MOE_OK;
+}
 
 moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out, int64_t n,
                              void* stream) {
@@ -843,7 +865,7 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
           if (r) return r;
         }
         // the kernel that completes the last wave's out also applies the residual
-        r = forward_impl(L, P, w, x, out, w == nw - 1 ? (uint16_t*)x : nullptr);
+        r = forward_impl(L, P, w, x, out, w == nw - 1 ? (uint16_t*)x : nullptr, /*norm=*/1);
         if (r) return r;
       }
       if (!lookahead && l + 1 < n) {
@@ -891,7 +913,7 @@ moe_status step_device_check(const moe_layer* L, const moe_plan* p, int32_t T) {
 // pair becomes a graph dependency).
 moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const float* logits, int32_t T,
                             const void* x, float* out, uint16_t* x_res, hipStream_t ps, bool cap,
-                            bool no_timers) {
+                            bool no_timers, int norm = 0) {
   const hipStream_t cs = L->compute;
   const bool timing = L->timing;
   if (cap || no_timers) L->timing = false;  // dispatch-stamped events are not captured
@@ -933,7 +955,7 @@ moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const fl
     // at most min(T * top_k, E) experts; exactly top_k for one token
     const int n_max = std::min(T * L->k, L->E);
     st = run_ffn(L, dev, h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr,
-                 nullptr, 0, T, false, x_res, dev.counts);
+                 nullptr, 0, T, false, x_res, dev.counts, nullptr, norm);
   } while (0);
   L->timing = timing;
   if (st) return st;
@@ -953,8 +975,8 @@ moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const fl
 // L->ev_copied on ps and the compute stream waits for it (under capture the
 // pair becomes a graph dependency).
 moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
-                            float* out, uint16_t* x_res, hipStream_t ps, bool cap) {
-  moe_status st = step_device_core(L, p->dev, p->h, logits, T, x, out, x_res, ps, cap, false);
+                            float* out, uint16_t* x_res, hipStream_t ps, bool cap, int norm = 0) {
+  moe_status st = step_device_core(L, p->dev, p->h, logits, T, x, out, x_res, ps, cap, false, norm);
   if (st) return st;
   if (!cap) {
     HIP_TRY(hipEventRecord(p->ev_consumed, L->compute));
@@ -1045,7 +1067,7 @@ moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* p
   }
   for (int l = 0; l < n; ++l) {
     moe_status st = step_device_impl(layers[l], plans[l], logits + l * lstride, T, x, out, (uint16_t*)x, ps,
-                                     cap);
+                                     cap, /*norm=*/1);
     if (st) return st;
   }
   return MOE_OK;
@@ -1146,8 +1168,9 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev,
-                   uint8_t* wdq) {
+                   uint8_t* wdq, int norm) {
   FfnArgs a{};
+  a.norm = norm;
   a.n_dev = n_dev;
   a.fmt = L->fmt;
   a.E = L->E;

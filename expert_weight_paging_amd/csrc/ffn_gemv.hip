@@ -20,6 +20,7 @@
 // Every weight byte of the wave is read from HBM exactly once; the summation
 // order is fixed, so results are bitwise reproducible.
 #include "internal.h"
+#include "norm.h"
 #include "wave.h"
 
 namespace moepage {
@@ -226,6 +227,7 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
   // activation row is read from memory once per workgroup into LDS and
   // shared by its four wavefronts.
   __shared__ uint4 xs[kWave * NJ * CV1 * sizeof(XT) / 16];
+  __shared__ float red[4];
   const int nx16 = H * (int)sizeof(XT) / 16;  // 16-byte chunks of one activation row
   if (a.n_dev && (int)blockIdx.y >= *a.n_dev) return;  // device-resolved count: uniform per block
   const int o = a.o_lo + blockIdx.y;
@@ -307,6 +309,7 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
       for (int c = threadIdx.x; c < nx16; c += 4 * kWave)
         xs[c] = ((const uint4*)(xbase + (size_t)t * H))[c];
       __syncthreads();
+      if (a.norm) rmsnorm_row_lds(xs, nx16, H, red);
       uint4 xw[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -340,6 +343,9 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
     if (q > p0) __syncthreads();  // the previous pair's reads of xs are done
     for (int c = threadIdx.x; c < nx16; c += 4 * kWave) xs[c] = ((const uint4*)(xbase + (size_t)t * H))[c];
     __syncthreads();
+    if constexpr (sizeof(XT) == 2) {
+      if (a.norm) rmsnorm_row_lds(xs, nx16, H, red);
+    }
     const XT* xrow = (const XT*)xs;
     float xv[NJ][CV1];
 #pragma unroll

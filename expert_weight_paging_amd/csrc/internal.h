@@ -169,6 +169,8 @@ struct FfnArgs {
                        // read on the device; n_exp is then only an upper bound
   uint16_t* x_res;     // optional: the launch that completes out also applies the
                        // stack residual x_res = bf16_rne(x_res + out), bf16 [T][H]
+  int norm;            // GEMV path, bf16 activations: the up kernel applies the unit-gain
+                       // RMSNorm to each staged activation row (a stack layer's input)
   // optional (GEMM path, quantised formats): the wave's records dequantised to
   // the bf16 record layout, expert o at wbase + (o - o_lo) * wstride
   const uint8_t* wbase;
@@ -192,5 +194,8 @@ bool gemm_shape_supported(int H, int I);
 
 hipError_t launch_residual(const uint16_t* x_in, const float* out, uint16_t* x_out, int64_t n,
                            hipStream_t s);
+
+// Unit-gain RMSNorm of T bf16 rows of H values (H a multiple of 8), x -> a.
+hipError_t launch_rmsnorm(const uint16_t* x, uint16_t* a, int T, int H, hipStream_t s);
 
 }  // namespace moepage

@@ -5,6 +5,7 @@
 // 94GB Qwen3.8-Flash-Next runs at 68 tok/s on one RTX 5090".
 #include "copy.h"
 #include "internal.h"
+#include "norm.h"
 #include "wave.h"
 
 namespace moepage {
@@ -910,7 +911,27 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x_in, con
   }
 }
 
+// Unit-gain RMSNorm, one workgroup per token row (staged in LDS, then the
+// shared norm routine, then written out).
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const uint16_t* x, uint16_t* a, int H) {
+  extern __shared__ uint4 row[];
+  __shared__ float red[4];
+  const int nx16 = H / 8;
+  const uint4* src = (const uint4*)(x + (size_t)blockIdx.x * H);
+  for (int c = threadIdx.x; c < nx16; c += kNormThreads) row[c] = src[c];
+  __syncthreads();
+  rmsnorm_row_lds(row, nx16, H, red);
+  uint4* dst = (uint4*)(a + (size_t)blockIdx.x * H);
+  for (int c = threadIdx.x; c < nx16; c += kNormThreads) dst[c] = row[c];
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm(const uint16_t* x, uint16_t* a, int T, int H, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  rmsnorm_kernel<<<T, kNormThreads, (size_t)H * 2, s>>>(x, a, H);
+  return hipGetLastError();
+}
 
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
                          hipStream_t s, hipEvent_t ev0) {

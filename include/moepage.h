@@ -265,14 +265,27 @@ moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
 moe_status moe_forward(moe_layer* layer, const moe_plan* plan, int32_t wave,
                        const void* x, float* out);
 
-/* Residual of a stack of MoE layers (no attention, no norm):
+/* Unit-gain RMSNorm of bf16 hidden states, the input of every layer of a
+ * stack: a[t][i] = bf16_rne(x[t][i] / sqrt(mean_i(x[t][i]^2) + MOE_RMS_EPS))
+ * (float32 arithmetic, fixed summation order). The pages run Qwen3-30B-A3B
+ * ([PE] "What does Paged Experts actually do?"), whose MoE block reads the
+ * residual stream through an RMSNorm; with no trained weights here its gain
+ * is one. x and a: device bf16 [T][H], 16-byte aligned, may alias; H a
+ * multiple of 8. Runs on the given stream. MOE_ERR_INVALID_ARG for bad
+ * sizes, pointers or alignment. */
+#define MOE_RMS_EPS 1e-6f
+moe_status moe_rmsnorm_bf16(const void* x, void* a, int32_t num_tokens, int32_t hidden, void* stream);
+
+/* Residual of a stack of MoE layers (attention omitted):
  * x_out[i] = bf16_rne(float(x_in[i]) + out[i]) for i < n; x_in and x_out are
  * device bf16 (may alias), out device float32. Runs on the given stream. */
 moe_status moe_residual_bf16(const void* x_in, const float* out, void* x_out,
                              int64_t n, void* stream);
 
 /* A batch through a stack of paged MoE layers, attention omitted: for each
- * layer l, out = MoE_l(x) and then x = bf16_rne(x + out), in place.
+ * layer l, a = moe_rmsnorm_bf16(x), out = MoE_l(a) and then
+ * x = bf16_rne(x + out), in place (on the GEMV path the norm is computed
+ * inside the first expert kernel, with the same bits as moe_rmsnorm_bf16).
  *   layers, plans: n_layers handles (plan l created for layer l with
  *                  max_tokens >= T); all layers share E, top_k, H, format and
  *                  the compute stream
@@ -344,8 +357,9 @@ moe_status moe_step_token_waves(moe_layer* layer, moe_plan* plan, const float* l
                                 int32_t num_tokens, const void* x, float* out, void* x_res);
 
 /* moe_stack_forward through device-resolved steps: for each layer l,
- * moe_step_device(layer l, plan l, logits[l], T, x, out, x_res = x), with no
- * host synchronisation (capturable). Same requirements per layer as
+ * moe_rmsnorm_bf16(x -> a) and moe_step_device(layer l, plan l, logits[l], T,
+ * a, out, x_res = x), with the norm computed inside the up kernel (no extra
+ * launch, the same bits) and no host synchronisation (capturable). Same requirements per layer as
  * moe_step_device; logits device float32 [n_layers][T][E]; x bf16 [T][H]
  * updated in place; out float32 [T][H] holds the last layer's MoE output.
  *   lookahead: 0 = everything on the shared compute stream, layer after

@@ -137,6 +137,9 @@ def test_null_handles_are_refused_without_a_gpu():
     assert L.moe_timing_enable(None, 1) == -1
     assert L.moe_timing_read(None, None) == -1
     assert L.moe_layer_init(None, None, None, None, None) == -1
+
     L.moe_layer_destroy(None)
     L.moe_plan_destroy(None)
     assert b"null" in L.moe_last_error()
+    assert L.moe_rmsnorm_bf16(None, None, 1, 2048, None) == -1        # null rows
+    assert L.moe_rmsnorm_bf16(None, None, 0, 2044, None) == -1        # H not a multiple of 8

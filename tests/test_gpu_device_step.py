@@ -11,6 +11,7 @@ import workloads as W
 from oracle.layer import PagedLayer, bf16_rne
 from workloads import gen
 
+from stack_check import StackPair
 from gpu_harness import TOL, PairedLayer, rel_err, say, x_values
 
 pytestmark = pytest.mark.gpu
@@ -219,13 +220,18 @@ def _close_stack(hosts, layers, plans):
 
 @pytest.mark.parametrize("lookahead", [False, True])
 def test_int4_stack_device(lookahead):
+    """moe_stack_forward_device against a twin stack stepped layer by layer
+    with every layer checked against the oracle (tests/stack_check.py): the
+    hidden state, output, plans and table state must be bitwise equal."""
     cfg = W.CONFIGS[4]
     n_layers, steps = 4, 12
     say("case: int4 stack %d layers x %d tokens, device-resolved, lookahead=%s" % (n_layers, steps, lookahead))
     s, c = torch.cuda.Stream(), torch.cuda.Stream()
-    hosts, layers, plans, refs = _int4_stack(cfg, n_layers, s, c)
+    A = StackPair(cfg, n_layers, 1, False, (s, c, s), keep_refs=False)
+    sb = torch.cuda.Stream()
+    B = StackPair(cfg, n_layers, 1, False, (sb, torch.cuda.Stream(), sb))
     rng = np.random.default_rng(5)
-    worst_hidden = 0.0
+    worst = {}
     for step in range(steps):
         sets = np.stack([np.sort(rng.choice(cfg.E, cfg.top_k, replace=False))[None] for _ in range(n_layers)])
         logits = gen.logits_from_sets(rng, sets, cfg.E)                      # [L][1][E]
@@ -234,26 +240,20 @@ def test_int4_stack_device(lookahead):
         out = torch.empty(1, cfg.H, dtype=torch.float32, device="cuda")
         lg = _dev(logits)
         torch.cuda.synchronize()  # inputs are in place before the stack's stream reads them
-        ewp.stack_forward_device(layers, plans, lg, x, out, lookahead=lookahead)
+        ewp.stack_forward_device(A.layers, A.plans, lg, x, out, lookahead=lookahead)
         torch.cuda.synchronize()
-        xv = x_values(x0, cfg.fmt)
+        xb, ob, summ = B.run_token(logits, x0, "device", chain=slice(None))
+        assert torch.equal(x, xb) and torch.equal(out, ob), step
         for l in range(n_layers):
-            o, ids_ref, w_ref, p_ref = refs[l].step(logits[l], xv)
-            ids, _, sid, _ = plans[l].read()
-            assert np.array_equal(ids, ids_ref) and np.array_equal(sid, p_ref.slot_ids)
-            se, _, st, clk = layers[l].get_state()
-            rse, _, rst, rclk = refs[l].table.state()
-            assert np.array_equal(se, rse) and np.array_equal(st, rst) and clk == rclk
-            if l == n_layers - 1:
-                assert rel_err(out.cpu().numpy(), o) <= TOL[cfg.fmt]
-            xv = bf16_rne(xv + o)
-        got = gen.bf16_bits_to_f32(x.cpu().numpy().view(np.uint16)).astype(np.float64)
-        bound = TOL[cfg.fmt] * np.sqrt(np.mean(o ** 2)) + n_layers * np.exp2(
-            np.floor(np.log2(np.maximum(np.abs(xv), 2.0 ** -126))) - 7)
-        worst_hidden = max(worst_hidden, float((np.abs(got - xv) / bound).max()))
-        assert np.all(np.abs(got - xv) <= bound)
-    say("worst hidden/bound %.3g" % worst_hidden)
-    _close_stack(hosts, layers, plans)
+            for u, v in zip(A.plans[l].read(), B.plans[l].read()):
+                assert np.array_equal(u, v), (step, l)
+            for u, v in zip(A.layers[l].get_state(), B.layers[l].get_state()):
+                assert np.array_equal(np.asarray(u), np.asarray(v)), (step, l)
+        for k, v in summ.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    say("worst: %s" % worst)
+    A.close()
+    B.close()
 
 
 def test_int4_stack_device_lookahead_graph_replays_match_eager():

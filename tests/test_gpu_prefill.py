@@ -101,8 +101,9 @@ def test_prefill_ragged(T, E, k, H, I, K):
 
 
 def test_prefill_stack_residual():
-    """Three bf16 layers at full shape with the device residual, against the
-    oracle's stack run from the same x0. Each layer's MoE output must meet the
+    """Three bf16 layers at full shape with the device norm and residual,
+    against the oracle's stack run from the same x0 (each layer reads the
+    unit-gain RMSNorm of the residual stream). Each layer's MoE output must meet the
     bf16 output tolerance. The hidden state is bf16, so where the two sides'
     sums straddle a rounding boundary they differ by one bf16 ulp; element-wise
     the final hidden state may differ by the last layer's output tolerance plus
@@ -125,11 +126,13 @@ def test_prefill_stack_residual():
     out = torch.empty(T, cfg.H, dtype=torch.float32, device=dev)
     lg = torch.from_numpy(logits).to(dev)
     outs = []
+    a = torch.empty_like(x)
     for l, p in enumerate(layers):
+        ewp.rmsnorm_bf16(x, a)
         info = p.gpu.route(p.plan, lg[l])
         for w in range(info["num_waves"]):
             p.gpu.page_in(p.plan, w)
-            p.gpu.forward(p.plan, w, x, out)
+            p.gpu.forward(p.plan, w, a, out)
         outs.append(out.cpu().numpy().copy())
         ewp.residual_bf16(x, out, x)
     torch.cuda.synchronize()
@@ -172,3 +175,31 @@ def test_residual_kernel_exact():
     ref = bf16_rne(gen.bf16_bits_to_f32(xb).astype(np.float64) + o.astype(np.float64))
     got = gen.bf16_bits_to_f32(yd.cpu().numpy().view(np.uint16)).astype(np.float64)
     assert np.array_equal(got, ref)
+
+
+def test_rmsnorm_kernel():
+    """The unit-gain RMSNorm of a stack layer's input against the oracle's
+    float64 norm, rounded to bf16: equal up to one bf16 ulp where float32 and
+    float64 straddle a rounding boundary (rare); rows of very different
+    scales, a zero row, H not a multiple of the workgroup's 2048 values, and
+    in place."""
+    rng = np.random.default_rng(12)
+    from oracle.layer import rms_norm
+    for T, H in ((7, 2048), (3, 520), (65, 8)):
+        v = rng.standard_normal((T, H)) * np.exp2(rng.integers(-30, 30, (T, 1)))
+        v[0] = 0.0
+        xb = gen.f32_to_bf16_bits(v.astype(np.float32))
+        xd = torch.from_numpy(xb.view(np.int16)).cuda()
+        ad = torch.empty_like(xd)
+        ewp.rmsnorm_bf16(xd, ad)
+        torch.cuda.synchronize()
+        got = gen.bf16_bits_to_f32(ad.cpu().numpy().view(np.uint16)).astype(np.float64)
+        ref = bf16_rne(rms_norm(gen.bf16_bits_to_f32(xb).astype(np.float64)))
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+        d = np.abs(got - ref)
+        say("norm T=%d H=%d: %d of %d values one ulp apart" % (T, H, int((d > 0).sum()), d.size))
+        assert np.all(d <= ulp) and (d > 0).mean() < 1e-2
+        assert np.all(got[0] == 0.0)
+        ewp.rmsnorm_bf16(xd, xd)                        # in place
+        torch.cuda.synchronize()
+        assert torch.equal(xd, ad)

@@ -348,3 +348,22 @@ def prefill_inputs(cfg, layers=None, tokens=None, salt=0):
     logits = logits_from_sets(st["routing"], sets, cfg.E)
     x0 = hidden_states(st["hidden"], (T, cfg.H), cfg.fmt)
     return logits, x0
+
+
+def cold_cycle_inputs(cfg, n_layers, batch, steps):
+    """Decode inputs for n_layers independent layers of a one-layer workload's
+    shape, taken in turn at every step (so a layer's experts leave the chip's
+    caches before that layer runs again): logits float32
+    [steps][n_layers][B][E], one routing chain of the workload's kind per layer
+    and sequence, and x [steps][B][H]."""
+    st = streams(cfg.cid, 300 + batch)
+    sets = np.zeros((steps, n_layers, batch, cfg.top_k), dtype=np.int32)
+    for l in range(n_layers):
+        for b in range(batch):
+            if cfg.routing == "correlated":
+                sets[:, l, b] = correlated_sets(st["routing"], steps, cfg.E, cfg.top_k, cfg.p_keep)
+            else:
+                sets[:, l, b] = uniform_sets(st["routing"], steps, cfg.E, cfg.top_k)
+    logits = logits_from_sets(st["routing"], sets, cfg.E)
+    x = hidden_states(st["hidden"], (steps, batch, cfg.H), cfg.fmt)
+    return logits, x
