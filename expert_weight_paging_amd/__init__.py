@@ -99,6 +99,8 @@ EXPORTS = {
                                      ctypes.c_void_p]),
     "moe_step_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "moe_step_device_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "moe_step_token_waves": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "moe_stack_forward_device": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
@@ -282,6 +284,14 @@ class Layer:
         _check(lib().moe_step_device(self.handle, plan.handle, _ptr(logits), int(T), _ptr(x), _ptr(out),
                                      _ptr(x_res)))
         plan.dev_tokens = int(T)
+
+    def step_device_static(self, logits, x, out, x_res=None, num_tokens=None):
+        """moe_step_device without a plan: the step's workspace is the
+        library's fixed device array (allocates nothing; calls that overlap
+        on one GPU race)."""
+        T = logits.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moe_step_device_static(self.handle, _ptr(logits), int(T), _ptr(x), _ptr(out),
+                                            _ptr(x_res)))
 
     def group_tokens(self, plan):
         """Tokens per group of step_token_waves: min(K // top_k, max_tokens, 64)."""

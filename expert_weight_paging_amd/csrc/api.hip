@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <thread>
@@ -40,6 +41,60 @@ struct TimerRec {
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace of moe_step_device_static: the plan arrays and the GEMV scratch of
+// one device-resolved step, in a fixed device array instead of memory the
+// library allocates. Each GPU holds its own copy until the process ends. In
+// host code `scratch` only names the symbol; its device address on each GPU
+// is taken once (hipGetSymbolAddress, at the first moe_layer_init on that
+// device, with the device current) and only that address is handed to
+// kernels.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_WORKSPACE_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Resolves the scratch array's address on the current device (once per device).
+moe_status resolve_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return MOE_OK;  // the static entry point refuses such a layer
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[device]) return MOE_OK;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(MOE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  g_scratch_ptr[device] = (uint8_t*)ptr;
+  return MOE_OK;
+}
+
+// Offsets of a device-resolved step's arrays in one workspace (the same
+// arrays moe_plan_create allocates, sized for P = T * top_k pairs).
+struct StepWs {
+  size_t ids, w, sid, wo, oe, os, po, pl, pp, cnt, h, total;
+};
+StepWs step_workspace(int E, int P, int I) {
+  StepWs o{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = off;
+    off = align_up(off + bytes, 256);
+    return r;
+  };
+  o.ids = take(4 * (size_t)P);
+  o.w = take(4 * (size_t)P);
+  o.sid = take(4 * (size_t)P);
+  o.wo = take(4 * (size_t)P);
+  o.oe = take(4 * (size_t)E);
+  o.os = take(4 * (size_t)E);
+  o.po = take(4 * ((size_t)E + 1));
+  o.pl = take(4 * (size_t)P);
+  o.pp = take(4 * (size_t)P);
+  o.cnt = take(16);
+  o.h = take(sizeof(float) * (size_t)P * I);
+  o.total = off;
+  return o;
+}
 
 }  // namespace
 
@@ -374,6 +429,7 @@ moe_status moe_layer_init(const moe_layer_desc* d, void* compute_stream, void* c
   if (hipHostGetDevicePointer(&hs_dev, (void*)hs, 0) == hipSuccess) L->host_store_dev = (const uint8_t*)hs_dev;
   else (void)hipGetLastError();
   if (hipGetDevice(&L->device) != hipSuccess) return bail(fail(MOE_ERR_HIP, "hipGetDevice failed"));
+  if ((st = resolve_scratch(L->device))) return bail(st);
   if (hipMalloc((void**)&L->dstats, 8 * sizeof(long long)) != hipSuccess ||
       hipMemset(L->dstats, 0, 8 * sizeof(long long)) != hipSuccess)
     return bail(fail(MOE_ERR_HIP, "device counters allocation failed"));
@@ -1000,6 +1056,43 @@ moe_status moe_step_device(moe_layer* L, moe_plan* p, const float* logits, int32
   if (x_res && L->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
   return step_device_impl(L, p, logits, T, x, out, (uint16_t*)x_res, L->compute,
                           stream_capturing(L->compute));
+}
+
+moe_status moe_step_device_static(moe_layer* L, const float* logits, int32_t T, const void* x, float* out,
+                                  void* x_res) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer");
+  if (T < 1 || T > MOE_MAX_GEMV_TOKENS) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in 1..64");
+  if ((int64_t)T * L->k > L->K)
+    return fail(MOE_ERR_INVALID_ARG, "T * top_k exceeds K: the step may need more than one wave");
+  if (!route_small_ok(T, L->k)) return fail(MOE_ERR_INVALID_ARG, "too many pairs for one route launch");
+  if (!L->host_store_dev) return fail(MOE_ERR_STATE, "host store is not mapped into the device");
+  if (L->cur_plan) return fail(MOE_ERR_STATE, "a host-driven step of this layer is unfinished");
+  if (!logits || !x || !out) return fail(MOE_ERR_INVALID_ARG, "null logits, x or out");
+  if (((uintptr_t)x & 15) || ((uintptr_t)out & 15) || ((uintptr_t)x_res & 7))
+    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned, x_res 8-byte aligned");
+  if (x_res && L->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
+  const StepWs ws = step_workspace(L->E, T * L->k, L->I);
+  if (ws.total > kStaticScratchBytes)
+    return fail(MOE_ERR_INVALID_ARG, "step needs " + std::to_string(ws.total) +
+                                         " bytes of workspace, more than the fixed " +
+                                         std::to_string(kStaticScratchBytes));
+  uint8_t* b = (L->device >= 0 && L->device < kMaxDevices) ? g_scratch_ptr[L->device] : nullptr;
+  if (!b) return fail(MOE_ERR_STATE, "no workspace address for the layer's device");
+  // Every array below is written by the route kernel before it is read in
+  // the same step, so nothing needs clearing between calls.
+  PlanDev dev{};
+  dev.ids = (int32_t*)(b + ws.ids);
+  dev.weights = (float*)(b + ws.w);
+  dev.slot_ids = (int32_t*)(b + ws.sid);
+  dev.wave_of = (int32_t*)(b + ws.wo);
+  dev.order_expert = (int32_t*)(b + ws.oe);
+  dev.order_slot = (int32_t*)(b + ws.os);
+  dev.pair_off = (int32_t*)(b + ws.po);
+  dev.pair_list = (int32_t*)(b + ws.pl);
+  dev.pair_pos = (int32_t*)(b + ws.pp);
+  dev.counts = (int32_t*)(b + ws.cnt);
+  return step_device_core(L, dev, (float*)(b + ws.h), logits, T, x, out, (uint16_t*)x_res, L->compute,
+                          stream_capturing(L->compute), /*no_timers=*/true);
 }
 
 moe_status moe_step_token_waves(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,

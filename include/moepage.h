@@ -336,6 +336,28 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
 moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits,
                            int32_t num_tokens, const void* x, float* out, void* x_res);
 
+/* moe_step_device without a plan, for callers that cannot allocate device
+ * memory while they run (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the step's plan arrays and FFN scratch
+ * (ids, weights, slot map, grouping, h) live in one fixed device array of
+ * MOE_STATIC_WORKSPACE_BYTES per GPU, compiled into the library and held
+ * until the process ends, instead of in a moe_plan. The call allocates
+ * nothing (no hipMalloc, no event creation; timers are skipped) and enqueues
+ * the same kernels as moe_step_device, so out, the table state and the
+ * counters are the same.
+ *   logits, x, out, x_res: as moe_step_device
+ * Requirements: as moe_step_device, and a workspace of
+ * 10 arrays (4 * T * top_k or 4 * E bytes each, 256-byte aligned) plus
+ * 4 * T * top_k * I bytes of h within MOE_STATIC_WORKSPACE_BYTES
+ * (MOE_ERR_INVALID_ARG beyond it). Every call on one GPU shares that GPU's
+ * array and leaves its contents behind: calls that overlap on one GPU (two
+ * streams, two threads, two layers in flight at once) race and give wrong
+ * results; successive calls on one stream are fine. Nothing in the array
+ * needs to start at zero. */
+#define MOE_STATIC_WORKSPACE_BYTES (4u << 20)
+moe_status moe_step_device_static(moe_layer* layer, const float* logits, int32_t num_tokens,
+                                  const void* x, float* out, void* x_res);
+
 /* Token-partitioned waves: a batch larger than one wave allows, served as
  * consecutive groups of G = min(K / top_k, max_tokens, MOE_MAX_GEMV_TOKENS)
  * tokens, each group one device-resolved single-wave step (moe_step_device on
