@@ -163,52 +163,47 @@ __device__ inline float dot1(const uint4 w, const float* x, float* xsum) {
   return acc;
 }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ inline f16x2 as_h2(uint32_t v) {
-  f16x2 r;
-  __builtin_memcpy(&r, &v, 4);
-  return r;
-}
-
-// Activations of one int4 chunk (32 values) as fp16 pairs in the order the
-// code pairs come out of a word: word i, step n pairs values 8i+n and 8i+n+4.
-// bf16 -> fp16 is exact for normal-range values (8 significant bits fit 11).
+// int4 codes against bf16 activations with the two-element bf16 dot: a code
+// pair (q_a, q_b) becomes the bf16 pair (128 + q_a, 128 + q_b) exactly by
+// setting the exponent of 128 (0x4300) under the nibbles (the ulp of bf16 at
+// 128 is 1), so dot2 sums (128 + q) * x, and the 128 is folded into the zero
+// point: sum (q - z) x = sum (128 + q) x - (128 + z) * sum x. Activations stay
+// bf16 (any finite bf16 value); products are exact in fp32.
+//
+// Activations of one int4 chunk (32 values, 4 words of 8 codes) as bf16 pairs
+// in the order the code pairs come out of a word: word i, step n pairs values
+// 8i + n and 8i + n + 4. Built once per token from the packed bf16 row.
 struct XPairs {
   uint32_t p[16];
   float sum;  // sum of the 32 activations (for the zero point)
 };
 
-__device__ inline void make_xpairs(const float* x, XPairs& xp) {
+// xw: the chunk's 32 bf16 activations as 16 packed words (2 per word, in order)
+__device__ inline void make_xpairs(const uint32_t* xw, XPairs& xp) {
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a0 = xw[4 * i], a1 = xw[4 * i + 1], a2 = xw[4 * i + 2], a3 = xw[4 * i + 3];
+    xp.p[4 * i + 0] = __builtin_amdgcn_perm(a2, a0, 0x05040100u);  // (x0, x4)
+    xp.p[4 * i + 1] = __builtin_amdgcn_perm(a2, a0, 0x07060302u);  // (x1, x5)
+    xp.p[4 * i + 2] = __builtin_amdgcn_perm(a3, a1, 0x05040100u);  // (x2, x6)
+    xp.p[4 * i + 3] = __builtin_amdgcn_perm(a3, a1, 0x07060302u);  // (x3, x7)
+  }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const auto h = __builtin_amdgcn_cvt_pkrtz(x[8 * i + n], x[8 * i + n + 4]);
-      uint32_t u;
-      __builtin_memcpy(&u, &h, 4);
-      xp.p[4 * i + n] = u;
-    }
-#pragma unroll
-  for (int v = 0; v < 32; ++v) s += x[v];
+  for (int v = 0; v < 16; ++v) s += bf16lo(xw[v]) + bf16hi(xw[v]);
   xp.sum = s;
 }
 
-// Raw sum of q * x over one 16-byte int4 chunk (32 codes): each code pair
-// becomes the fp16 pair (1024 + q) exactly via the 0x6400 exponent pattern,
-// 1024 is subtracted in fp16 (exact), and v_dot2_f32_f16 accumulates in fp32.
+// Raw sum of (128 + q) * x over one 16-byte int4 chunk (32 codes).
 __device__ inline float dot1_int4(const uint4 w, const XPairs& xp) {
   const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-  const f16x2 k1024 = as_h2(0x64006400u);
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const uint32_t q = ((wv[i] >> (4 * n)) & 0x000F000Fu) | 0x64006400u;
-      const f16x2 qf = as_h2(q) - k1024;
-      acc = __builtin_amdgcn_fdot2(qf, as_h2(xp.p[4 * i + n]), acc, false);
+      const uint32_t q = ((wv[i] >> (4 * n)) & 0x000F000Fu) | 0x43004300u;
+      acc = dot2_bf16(q, xp.p[4 * i + n], acc);
     }
   }
   return acc;
@@ -358,9 +353,23 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
       }
     }
     XPairs xp[F == MOE_FMT_INT4_ASYM_G128 ? NJ : 1];
-    if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+    if constexpr (F == MOE_FMT_INT4_ASYM_G128 && sizeof(XT) == 2) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) make_xpairs(xv[j], xp[j]);
+      for (int j = 0; j < NJ; ++j) {
+        const int c = lane + kWave * j;
+        uint32_t xw[16];
+        if (c < nch) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint4 q = xs[c * 4 + u];
+            xw[4 * u] = q.x; xw[4 * u + 1] = q.y; xw[4 * u + 2] = q.z; xw[4 * u + 3] = q.w;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 16; ++u) xw[u] = 0u;
+        }
+        make_xpairs(xw, xp[j]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -380,8 +389,8 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
         if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
           const float dg = dot1_int4(wg[r][j], xp[j]);
           const float du = dot1_int4(wu[r][j], xp[j]);
-          g = fmaf(sg[r][j], dg - zg[r][j] * xp[j].sum, g);
-          u = fmaf(su[r][j], du - zu[r][j] * xp[j].sum, u);
+          g = fmaf(sg[r][j], dg - (zg[r][j] + 128.f) * xp[j].sum, g);
+          u = fmaf(su[r][j], du - (zu[r][j] + 128.f) * xp[j].sum, u);
         } else {
           float xs = 0.f;
           const float dg = dot1<F>(wg[r][j], xv[j], &xs);

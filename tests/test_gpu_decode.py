@@ -110,3 +110,33 @@ def test_mxfp4_small_ragged_shape():
     worst = p.run(logits, x, check_state_every=1)
     say("mxfp4 small worst rel err %.3g" % worst)
     p.close()
+
+
+@pytest.mark.parametrize("fmt", [gen.INT4, gen.FP8, gen.MXFP4, gen.BF16])
+def test_activation_range_extremes(fmt):
+    """Activations over the whole bf16 range the layers accept: magnitudes
+    near 7e4 (beyond fp16's largest finite value) mixed with values near 1e-6
+    (below fp16's normal range) and ordinary ones, at batch 1 and 3, against
+    the oracle. The expert kernels keep activations in bf16 or fp32, so
+    nothing is clamped or flushed."""
+    E, k, H, I, K = 16, 2, 256, 256, 8
+    say("case: fmt %d activations near 7e4 and 1e-6" % fmt)
+    rng = np.random.default_rng(90 + fmt)
+    recs = [gen.encode_record(fmt, (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32),
+                              (rng.standard_normal((H, I)) * 0.02).astype(np.float32)) for _ in range(E)]
+
+    def fill(a):
+        for e in range(E):
+            a[e] = recs[e]
+    for B in (1, 3):
+        p = PairedLayer(E, k, H, I, K, fmt, fill, max_tokens=B)
+        steps = 6
+        logits = rng.standard_normal((steps, B, E)).astype(np.float32)
+        v = rng.standard_normal((steps, B, H))
+        pick = rng.integers(0, 3, (steps, B, H))
+        v = np.where(pick == 0, np.sign(v) * rng.uniform(6e4, 7.5e4, v.shape),
+                     np.where(pick == 1, v * 1e-6, v))
+        x = gen.f32_to_bf16_bits(v.astype(np.float32))
+        worst = p.run(logits, x, check_state_every=1)
+        say("fmt %d B=%d worst rel err %.3g" % (fmt, B, worst))
+        p.close()

@@ -292,3 +292,43 @@ def test_host_step_bits_do_not_depend_on_copy_progress():
         outs.append(np.stack(res))
         p.close()
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [gen.FP8, gen.INT4])
+def test_zeroed_scale_block_is_flagged(fmt):
+    """[PE] "Can paging change the model's outputs?": an expert that runs with
+    the wrong scale tensor gives wrong outputs silently. Plant that failure in
+    the GPU's host store (one 128x128 FP8 scale block, or the int4 gate/up
+    scale table, of an expert the first step routes, set to zero) and check that
+    parity against the oracle of the clean store flags it, while the plans
+    stay exact (paging itself is not what is wrong)."""
+    from oracle.layer import PagedLayer
+    from oracle.router import route
+    say("case: zeroed %s must fail parity" % {gen.FP8: "FP8 128x128 scale block", gen.INT4: "int4 W13 scales"}[fmt])
+    E, k, H, I, K = 16, 2, 256, 256, 8
+    rng = np.random.default_rng(77)
+    recs = [gen.encode_record(fmt, (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32),
+                              (rng.standard_normal((H, I)) * 0.02).astype(np.float32)) for _ in range(E)]
+    clean = np.stack(recs)
+    logits = rng.standard_normal((6, 1, E)).astype(np.float32)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((6, 1, H)).astype(np.float32))
+    victim = int(route(logits[0], k)[0][0, 0])                 # the first step's top expert
+    if fmt == gen.FP8:
+        s13 = 2 * I * H + H * I                                # after both code matrices
+        bad = slice(s13, s13 + 4)                              # W13 scale block (0, 0), float32
+    else:
+        s13 = (2 * I * H + H * I) // 2                         # after both packed code matrices
+        bad = slice(s13, s13 + 2 * (2 * I) * (H // 128))       # every W13 group scale, float16
+
+    def fill(a):
+        a[:] = clean
+        a[victim, bad] = 0
+    p = PairedLayer(E, k, H, I, K, fmt, fill, max_tokens=1)
+    assert p.host.array[victim, bad].max() == 0 and clean[victim, bad].max() > 0
+    p.ref = PagedLayer(clean, fmt, E, k, H, I, K)              # the oracle reads the clean bytes
+    with pytest.raises(AssertionError) as ei:
+        p.run(logits, x, check_state_every=1)
+    step, err, tol = ei.value.args[0]                          # the output check, not a plan check
+    say("flagged at step %d: rel err %.3g > %.3g" % (step, err, tol))
+    assert err > tol
+    p.close()
