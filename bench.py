@@ -12,7 +12,8 @@ hidden 2048, MoE intermediate 768):
   decode-mxfp4 the same layer with MXFP4 experts (E2M1 weights, one E8M0
                scale per 32), --batch B
   stack-int4   48 int4 layers, K=92 each, batch-1 decode; a step is one token
-               through all 48 layers with the bf16 residual; --routing
+               through all 48 layers, each reading the unit-gain RMSNorm of
+               the residual stream and adding its output back (bf16); --routing
                uniform for the control run; --lookahead to route/page-in
                layer l+1 while layer l computes
   prefill-bf16 one 2048-token chunk through 48 bf16 layers, K=92, warm
@@ -33,7 +34,13 @@ region; expert stores live in pinned host memory by design of the method.
 Prints ONE JSON line: `value` is tokens/s of the workload; `roofline` is the
 dominant kernel's achieved rate over the timed region, from HIP events
 recorded on the stream the kernel runs on, against the MI355X peak;
-`cpu_baseline` is the float64 CPU oracle timed on a bounded sample.
+`cpu_baseline` is the float32 CPU oracle timed on a bounded sample, with the
+host's core count, CPU model and BLAS library.
+For the decode workloads the headline `roofline` is the expert FFN (up and
+down kernels together) measured with the caches cold: --cold-layers
+independent layers of the same shape taken in turn, so that a layer's experts
+have left the 256 MB last-level cache before it runs again; `roofline_warm` is
+the same figure on the one layer of the timed steps.
 """
 import argparse
 import hashlib
@@ -67,11 +74,12 @@ KERNEL_SOURCE = {"ffn_up_kernel": "ffn_gemv.hip", "ffn_down_kernel": "ffn_gemv.h
 
 
 def kernel_source_hash(kernel_name):
-    """Hash of the source that defines a kernel and of the shared headers: a
+    """Hash of the source that defines a kernel and of every shared header: a
     stored traffic figure is used only while these are unchanged."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "expert_weight_paging_amd", "csrc")
-    for f in (KERNEL_SOURCE[kernel_name], "internal.h", "wave.h"):
+    headers = sorted(f for f in os.listdir(d) if f.endswith(".h"))
+    for f in [KERNEL_SOURCE[kernel_name]] + headers:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -181,6 +189,28 @@ def oracle_threads():
         return 1
 
 
+def host_info():
+    """The host the CPU baseline ran on: cores visible to this process, the CPU
+    model and the BLAS library numpy calls (with its thread count)."""
+    info = {"nproc": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas"] = ["%s %s (%s, %d threads)" % (p.get("internal_api"), p.get("version"),
+                                                    p.get("threading_layer"), p.get("num_threads", 0))
+                        for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:
+        info["blas"] = None
+    return info
+
+
 def merge_timing(ts):
     out = {}
     for t in ts:
@@ -225,14 +255,11 @@ def bench_decode(args, torch, dev):
     x_d = torch.from_numpy(x.view(np.int16)).to(dev)
     out = torch.empty(B, cfg.H, dtype=torch.float32, device=dev)
 
+    step = step_fn(args)
+
     def run(t0, n):
         for t in range(t0, t0 + n):
-            if args.waves == "token":
-                layer.step_token_waves(plan, lg_d[t], x_d[t], out)
-            elif args.device:
-                layer.step_device(plan, lg_d[t], x_d[t], out)
-            else:
-                layer.step(plan, lg_d[t], x_d[t], out)
+            step(layer, plan, lg_d[t], x_d[t], out)
 
     run(0, args.warmup)
     torch.cuda.synchronize()
@@ -265,14 +292,14 @@ def bench_decode(args, torch, dev):
 
     def cpu(budget):
         from oracle.layer import PagedLayer
-        ref = PagedLayer(np.array(host.array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, K)
+        ref = PagedLayer(np.array(host.array), cfg.fmt, cfg.E, cfg.top_k, cfg.H, cfg.I, K, dtype=np.float32)
         # a longer decode sequence from the same seeded generator (same recipe),
         # so that the sample holds about `budget` seconds of oracle work
         lg_c, x_c = gen.decode_inputs(cfg, B, steps=max(total, 4096))
         n = 0
         t0 = time.perf_counter()
         while n < len(lg_c) and (time.perf_counter() - t0) < budget:
-            xv = gen.bf16_bits_to_f32(x_c[n]).astype(np.float64)
+            xv = gen.bf16_bits_to_f32(x_c[n])
             if args.waves == "token":
                 ref.step_token_waves(lg_c[n], xv, G)
             else:
@@ -281,11 +308,88 @@ def bench_decode(args, torch, dev):
         el = time.perf_counter() - t0
         return {"value": n * B / el, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
                 "sample": "%d decode steps (batch %d) of the same workload recipe from a cold table: "
-                          "float64 numpy oracle incl. routing, LRU plan, record copies (host memcpy, "
-                          "no PCIe) and SwiGLU experts, %.1f s" % (n, B, el)}
+                          "float32 numpy oracle incl. routing, LRU plan, record copies (host memcpy, "
+                          "no PCIe) and SwiGLU experts, %.1f s" % (n, B, el), **host_info()}
     res["cpu"] = cpu
     res["cleanup"] = host.free
+    res["pool"] = host.array
+    res["step_fn"] = step_fn(args)
     return res
+
+
+def step_fn(args):
+    """The per-layer decode step of the chosen mode."""
+    def step(layer, plan, lg, x, out):
+        if args.waves == "token":
+            layer.step_token_waves(plan, lg, x, out)
+        elif args.device:
+            layer.step_device(plan, lg, x, out)
+        else:
+            layer.step(plan, lg, x, out)
+    return step
+
+
+def bench_decode_cold(args, torch, dev, cfg, K, B, pool, step):
+    """The decode layer's FFN with the chip's caches cold: n independent layers
+    of the same shape (own pinned store, a permutation of the workload's
+    records, own slots and routing chain) taken in turn at every step, so that
+    between two steps of one layer the others stream n - 1 steps' experts
+    (at batch 1 and bf16, 75.5 MB each: 528 MB for n = 8, twice the 256 MB
+    last-level cache). Returns the timing of the expert kernels and the
+    layer-steps per second."""
+    import expert_weight_paging_amd as ewp
+    from workloads import gen
+    n = args.cold_layers
+    rec = pool.shape[1]
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    hosts, layers, plans = [], [], []
+    t0 = time.perf_counter()
+    for l in range(n):
+        h = ewp.HostStore(cfg.E, rec)
+        gen.fill_layer_store(cfg, l, h.array, pool)
+        slots, state = ewp.alloc_layer_buffers(cfg.E, K, rec, dev)
+        L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt, h, slots, state, compute, copy, compute)
+        hosts.append(h)
+        layers.append(L)
+        plans.append(ewp.Plan(L, B))
+    log("cold pass: %d layers built in %.1f s (%.1f GB pinned, %.1f GB of slots)"
+        % (n, time.perf_counter() - t0, n * cfg.E * rec / 1e9, n * K * rec / 1e9))
+    warm, steps = args.cold_warmup, args.cold_steps
+    logits, x = gen.cold_cycle_inputs(cfg, n, B, warm + steps)
+    lg_d = torch.from_numpy(logits).to(dev)
+    x_d = torch.from_numpy(x.view(np.int16)).to(dev)
+    out = torch.empty(B, cfg.H, dtype=torch.float32, device=dev)
+
+    def run(t0, m):
+        for t in range(t0, t0 + m):
+            for l in range(n):
+                step(layers[l], plans[l], lg_d[t, l], x_d[t], out)
+
+    run(0, warm)
+    torch.cuda.synchronize()
+    s0 = sum_stats(layers)
+    t1 = time.perf_counter()
+    run(warm, steps)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    s1 = sum_stats(layers)
+    for L in layers:
+        L.reset()
+    run(0, warm)
+    for L in layers:
+        L.timing_enable(True)
+    run(warm, steps)
+    torch.cuda.synchronize()
+    tm = merge_timing([L.timing_read() for L in layers])
+    for p in plans:
+        p.close()
+    for L in layers:
+        L.close()
+    for h in hosts:
+        h.free()
+    d = {k: s1[k] - s0[k] for k in s1}
+    return {"timing": tm, "layer_steps_per_s": steps * n / el, "ms_per_layer_step": el / (steps * n) * 1e3,
+            "layers": n, "steps": steps, "warmup": warm, "stats": d}
 
 
 # ---------------------------------------------------------------- 48-layer stacks
@@ -366,7 +470,7 @@ def bench_stack(args, torch, dev):
             ewp.stack_forward_device(layers, plans, lg_buf, x, out, lookahead=args.lookahead)
         torch.cuda.synchronize()
 
-    def run(t0, n, eager=False):
+    def run(t0, n, eager=False, lookahead=args.lookahead):
         with torch.cuda.stream(compute):  # inputs are written on the stream that reads them
             for t in range(t0, t0 + n):
                 x.copy_(x0_d[t])
@@ -374,9 +478,9 @@ def bench_stack(args, torch, dev):
                     lg_buf.copy_(lg_d[t])
                     graph.replay()
                 elif args.device:
-                    ewp.stack_forward_device(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
+                    ewp.stack_forward_device(layers, plans, lg_d[t], x, out, lookahead=lookahead)
                 else:
-                    ewp.stack_forward(layers, plans, lg_d[t], x, out, lookahead=args.lookahead)
+                    ewp.stack_forward(layers, plans, lg_d[t], x, out, lookahead=lookahead)
 
     run(0, args.warmup)
     torch.cuda.synchronize()
@@ -388,10 +492,14 @@ def bench_stack(args, torch, dev):
     s1 = sum_stats(layers)
     for L in layers:
         L.reset()
-    run(0, args.warmup, eager=True)
+    # timers need eager launches; with device lookahead the up projection shares
+    # its launch with the next layer's copies, so the kernels are timed in
+    # strict order (the same kernels, each launched on its own)
+    timed_la = args.lookahead and not args.device
+    run(0, args.warmup, eager=True, lookahead=timed_la)
     for L in layers:
         L.timing_enable(True)
-    run(args.warmup, args.steps, eager=True)  # timers need eager launches
+    run(args.warmup, args.steps, eager=True, lookahead=timed_la)
     torch.cuda.synchronize()
     tm = merge_timing([L.timing_read() for L in layers])
     floor_us = ewp.timing_floor()
@@ -399,7 +507,8 @@ def bench_stack(args, torch, dev):
     res = {"value": args.steps / el, "ms_per_step": el / args.steps * 1e3, "timing": tm, "stats": d,
            "floor_us": floor_us,
            "cfg": cfg, "B": 1,
-           "workload": "48-layer Qwen3-30B-A3B-shaped MoE stack (attention omitted), int4 asym g128 "
+           "workload": "48-layer Qwen3-30B-A3B-shaped MoE stack (attention omitted; each layer reads the "
+                       "unit-gain RMSNorm of the residual stream), int4 asym g128 "
                        "experts, E=128 top_k=8 hidden=2048 intermediate=768, K=92 slots per layer, "
                        "batch-1 decode, %s routing%s, %s, cold tables"
                        % ("correlated p=0.75" if args.routing == "correlated" else "uniform",
@@ -408,16 +517,16 @@ def bench_stack(args, torch, dev):
     def cpu(budget):
         from oracle.layer import PagedLayer
         refs = [PagedLayer(pool[gen.layer_permutation(cfg, l)], cfg.fmt, cfg.E, cfg.top_k, cfg.H,
-                           cfg.I, cfg.K) for l in range(4)]
-        from oracle.layer import bf16_rne
+                           cfg.I, cfg.K, dtype=np.float32) for l in range(4)]
+        from oracle.layer import bf16_rne, rms_norm
         t0 = time.perf_counter()
         nl = nt = 0
         # tokens in order through the first four layers (tables start cold),
         # until the budget is spent; the rate is scaled to 48 layers
         while nt < len(x0) and time.perf_counter() - t0 < budget:
-            xv = gen.bf16_bits_to_f32(x0[nt]).astype(np.float64)
+            xv = gen.bf16_bits_to_f32(x0[nt])
             for l in range(4):
-                o, *_ = refs[l].step(logits[nt, l], xv)
+                o, *_ = refs[l].step(logits[nt, l], bf16_rne(rms_norm(xv)))
                 xv = bf16_rne(xv + o)
                 nl += 1
             nt += 1
@@ -425,7 +534,7 @@ def bench_stack(args, torch, dev):
         per_token = el / nl * cfg.layers
         return {"value": 1.0 / per_token, "unit": "tok/s", "cores": oracle_threads(), "kind": "oracle",
                 "sample": "tokens 0..%d through the first 4 of 48 layers (tables start cold) with the "
-                          "float64 numpy oracle, %.1f s, scaled to 48 layers" % (nt - 1, el)}
+                          "float32 numpy oracle, %.1f s, scaled to 48 layers" % (nt - 1, el), **host_info()}
     res["cpu"] = cpu
 
     def cleanup():
@@ -482,19 +591,20 @@ def bench_prefill(args, torch, dev):
            "floor_us": floor_us,
            "stats": d, "cfg": cfg, "B": T,
            "workload": "prefill: one 2048-token chunk through a 48-layer Qwen3-30B-A3B-shaped bf16 "
-                       "MoE stack (attention omitted), E=128 top_k=8 hidden=2048 intermediate=768, "
+                       "MoE stack (attention omitted; each layer reads the unit-gain RMSNorm of the "
+                       "residual stream), E=128 top_k=8 hidden=2048 intermediate=768, "
                        "K=92 slots per layer warm with experts 0..91, uniform routing"}
 
     def cpu(budget):
-        from oracle.layer import PagedLayer, bf16_rne
+        from oracle.layer import PagedLayer, bf16_rne, rms_norm
         lg, x0 = chunks[0]
-        xv = gen.bf16_bits_to_f32(x0).astype(np.float64)
+        xv = gen.bf16_bits_to_f32(x0)
         t0 = time.perf_counter()
         nl = 0
         for l in range(cfg.layers):
             ref = PagedLayer(pool[gen.layer_permutation(cfg, l)], cfg.fmt, cfg.E, cfg.top_k, cfg.H,
-                             cfg.I, cfg.K, initial_fill=True)
-            o, *_ = ref.step(lg[l], xv)
+                             cfg.I, cfg.K, initial_fill=True, dtype=np.float32)
+            o, *_ = ref.step(lg[l], bf16_rne(rms_norm(xv)))
             xv = bf16_rne(xv + o)
             nl += 1
             if time.perf_counter() - t0 > budget:
@@ -502,8 +612,8 @@ def bench_prefill(args, torch, dev):
         el = time.perf_counter() - t0
         return {"value": T / (el / nl * cfg.layers), "unit": "tok/s", "cores": oracle_threads(),
                 "kind": "oracle",
-                "sample": "chunk 0 (2048 tokens) through the first %d of 48 layers with the float64 "
-                          "numpy oracle, %.1f s, scaled to 48 layers" % (nl, el)}
+                "sample": "chunk 0 (2048 tokens) through the first %d of 48 layers with the float32 "
+                          "numpy oracle, %.1f s, scaled to 48 layers" % (nl, el), **host_info()}
     res["cpu"] = cpu
 
     def cleanup():
@@ -542,22 +652,57 @@ def roofline(res, workload, variant):
                 "gemm_up_plus_down_TFLOPs": round(both, 1),
                 "gemm_up_plus_down_frac": round(both / BF16_MFMA_PEAK_TFLOPS, 4),
                 "launch_floor_us": round(res["floor_us"], 3)}
-    kinds = [k for k in ("ffn_up", "ffn_down") if tm[k]["count"]]
-    dom = max(kinds, key=lambda k: tm[k]["ms"])
-    sec = tm[dom]["ms"] * 1e-3
-    achieved = tm[dom]["bytes"] / sec / 1e9
-    kname = {"ffn_up": "ffn_up_kernel", "ffn_down": "ffn_down_kernel"}[dom]
-    both = (tm["ffn_up"]["bytes"] + tm["ffn_down"]["bytes"]) / ((tm["ffn_up"]["ms"] + tm["ffn_down"]["ms"]) * 1e-3) / 1e9
-    avg_us = tm[dom]["ms"] / tm[dom]["count"] * 1e3
-    per_launch = tm[dom]["bytes"] / tm[dom]["count"]
-    # launch_floor_us: what the same events report for an empty kernel (context only)
-    return {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_from_profiles(kname, variant),
-            "avg_launch_us": round(avg_us, 3),
-            "algorithmic_bytes_per_launch": per_launch,
-            "ffn_up_plus_down_GBps": round(both, 1),
-            "launch_floor_us": round(res["floor_us"], 3)}
+    return hbm_roofline(tm, res["floor_us"], variant)
+
+
+def hbm_roofline(tm, floor_us, variant, cache=None):
+    """The decode step's expert FFN, its two kernels (gate/up + SiLU, down +
+    weighted combine) together: algorithmic bytes (the weight bytes of the
+    experts each launch reads) over the summed event-measured durations of
+    both kernels, with each kernel's own figures beside it. `traffic` is the
+    counter-measured HBM bytes of one up launch plus one down launch."""
+    per, traffic = {}, 0.0
+    for k, name in (("ffn_up", "ffn_up_kernel"), ("ffn_down", "ffn_down_kernel")):
+        v = tm[k]
+        if not v["count"]:
+            return None
+        gbps = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+        t = traffic_from_profiles(name, variant)
+        traffic = None if (t is None or traffic is None) else traffic + t
+        per[name] = {"avg_launch_us": round(v["ms"] / v["count"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": v["bytes"] / v["count"],
+                     "achieved": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": t,
+                     "launches": v["count"]}
+    up, dn = tm["ffn_up"], tm["ffn_down"]
+    achieved = (up["bytes"] + dn["bytes"]) / ((up["ms"] + dn["ms"]) * 1e-3) / 1e9
+    r = {"bound": "hbm", "kernel": "ffn_up_kernel + ffn_down_kernel", "achieved": round(achieved, 1),
+         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+         "traffic": traffic,
+         "algorithmic_bytes_per_launch_pair": (up["bytes"] + dn["bytes"]) / up["count"],
+         "avg_launch_pair_us": round((up["ms"] + dn["ms"]) / up["count"] * 1e3, 3),
+         "kernels": per, "launch_floor_us": round(floor_us, 3)}
+    if cache:
+        r["cache"] = cache
+    return r
+
+
+def cold_only_line(args, torch, dev, variant):
+    """Only the cache-cold pass of a decode workload (what its profiles are taken on)."""
+    import workloads as W
+    from workloads import gen
+    cfg = W.CONFIGS[DECODE_CONFIG[args.workload]]
+    K = args.slots or cfg.K
+    pool = gen.pool_records(cfg)
+    cold = bench_decode_cold(args, torch, dev, cfg, K, args.batch, pool, step_fn(args))
+    import expert_weight_paging_amd as ewp
+    return {"metric": METRIC, "value": round(cold["layer_steps_per_s"] * args.batch, 2), "unit": "tok/s",
+            "n_gpus": 1, "steps": cold["steps"], "warmup": cold["warmup"],
+            "ms_per_step": round(cold["ms_per_layer_step"], 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": FMT_NAME[cfg.fmt], "data": "synthetic (seeded)",
+            "config": {"workload": "%d independent %s MoE layers of the Qwen3-30B-A3B shape taken in turn, "
+                                   "K=%d, batch %d; value = tokens/s of one layer (layer-steps/s x batch)"
+                                   % (cold["layers"], FMT_NAME[cfg.fmt], K, args.batch)},
+            "roofline": hbm_roofline(cold["timing"], ewp.timing_floor(), variant + " cold", cache="cold")}
 
 
 def main():
@@ -581,6 +726,14 @@ def main():
                     help="decode batches beyond one wave: expert-partitioned waves (host-driven, "
                          "default) or groups of K // top_k tokens as device-resolved steps")
     ap.add_argument("--slots", type=int, default=None, help="decode workloads: K instead of the config's")
+    ap.add_argument("--cold-layers", type=int, default=8,
+                    help="decode workloads: the headline roofline is measured on this many independent "
+                         "layers of the same shape taken in turn (caches cold between a layer's steps); "
+                         "0 = measure it on the one layer (caches warm)")
+    ap.add_argument("--cold-steps", type=int, default=64)
+    ap.add_argument("--cold-warmup", type=int, default=16)
+    ap.add_argument("--cold-only", action="store_true",
+                    help="decode workloads: run only the cache-cold pass (for profiling it alone)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
@@ -598,7 +751,7 @@ def main():
                         (" graph", args.graph), (" waves=token", args.waves == "token"),
                         (" K=%s" % args.slots, args.slots is not None)) if on)
     if args.ingest_pmc:
-        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], variant)
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], variant + (" cold" if args.cold_only else ""))
         return
     if args.graph:
         args.device = True
@@ -634,8 +787,20 @@ def main():
     fn = {"decode-bf16": bench_decode, "decode-fp8": bench_decode, "decode-mxfp4": bench_decode,
           "stack-int4": bench_stack,
           "prefill-bf16": bench_prefill}[args.workload]
+    decode = args.workload.startswith("decode")
+    if args.cold_only:
+        if not decode or args.cold_layers < 2:
+            print("--cold-only applies to the decode workloads with --cold-layers >= 2", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(cold_only_line(args, torch, dev, variant)), flush=True)
+        return
     res = fn(args, torch, dev)
     log("timed %d steps: %.3f ms/step" % (args.steps, res["ms_per_step"]))
+    cold = None
+    if decode and args.cold_layers >= 2:
+        cold = bench_decode_cold(args, torch, dev, res["cfg"], res["K"], res["B"], res["pool"], res["step_fn"])
+        log("cold pass: %d layers x %d steps, %.3f ms per layer-step"
+            % (cold["layers"], cold["steps"], cold["ms_per_layer_step"]))
     tm, st, cfg = res["timing"], res["stats"], res["cfg"]
     pin = tm["page_in"]
     line = {
@@ -656,8 +821,24 @@ def main():
         "config": {"workload": res["workload"], "batch": res["B"], "num_slots": res.get("K", cfg.K),
                    "experts": cfg.E, "top_k": cfg.top_k, "layers": cfg.layers,
                    "lookahead": bool(args.lookahead), "parallelism": "single GPU"},
-        "roofline": roofline(res, args.workload, variant),
+        "roofline": roofline(res, args.workload, variant) if cold is None else
+                    hbm_roofline(cold["timing"], res["floor_us"], variant + " cold",
+                                 cache="cold: %d independent layers of this shape taken in turn, %d steps "
+                                       "after %d, so each layer's experts are out of the 256 MB "
+                                       "last-level cache when it runs again" % (cold["layers"],
+                                                                                cold["steps"],
+                                                                                cold["warmup"])),
         "kernels_us": {k: round(v["ms"] / v["count"] * 1e3, 3) for k, v in tm.items() if v["count"]},
+        "roofline_warm": None if cold is None else
+                         hbm_roofline(tm, res["floor_us"], variant,
+                                      cache="warm: the one layer of the timed steps, whose step shares "
+                                            "most experts with the one before (last-level cache hits)"),
+        "cold_pass": None if cold is None else
+                     {"layers": cold["layers"], "steps": cold["steps"],
+                      "ms_per_layer_step": round(cold["ms_per_layer_step"], 4),
+                      "misses_per_layer_step": round(cold["stats"]["misses"] / max(cold["stats"]["steps"], 1), 4),
+                      "kernels_us": {k: round(v["ms"] / v["count"] * 1e3, 3)
+                                     for k, v in cold["timing"].items() if v["count"]}},
         # device-resolved copies are timed without their byte count (the host does not see
         # the plan); the timed pass pages the same bytes as the counted one
         "page_in": {"GBps": round((pin["bytes"] or st["bytes_paged"]) / max(pin["ms"], 1e-9) / 1e6, 2),
