@@ -71,7 +71,7 @@ moe_status resolve_scratch(int device) {
 // Offsets of a device-resolved step's arrays in one workspace (the same
 // arrays moe_plan_create allocates, sized for P = T * top_k pairs).
 struct StepWs {
-  size_t ids, w, sid, wo, oe, os, po, pl, pp, cnt, h, total;
+  size_t ids, w, sid, wo, oe, os, po, pl, pp, pw, cnt, h, total;
 };
 StepWs step_workspace(int E, int P, int I) {
   StepWs o{};
@@ -90,6 +90,7 @@ StepWs step_workspace(int E, int P, int I) {
   o.po = take(4 * ((size_t)E + 1));
   o.pl = take(4 * (size_t)P);
   o.pp = take(4 * (size_t)P);
+  o.pw = take(4 * (size_t)P);
   o.cnt = take(16);
   o.h = take(sizeof(float) * (size_t)P * I);
   o.total = off;
@@ -291,7 +292,8 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res = nullptr,
-                   const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr, int norm = 0);
+                   const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr, int norm = 0,
+                   const NextStep* next = nullptr);
 
 moe_status self_check(moe_layer* L);
 
@@ -494,7 +496,7 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   };
   const size_t o_ids = take(4 * P), o_w = take(4 * P), o_sid = take(4 * P), o_wo = take(4 * P),
                o_oe = take(4 * E), o_os = take(4 * E), o_po = take(4 * (E + 1)),
-               o_pl = take(4 * P), o_pp = take(4 * P), o_cnt = take(16);
+               o_pl = take(4 * P), o_pp = take(4 * P), o_pw = take(4 * P), o_cnt = take(16);
   p->gemv_pairs = (int)std::min<size_t>(P, (size_t)MOE_MAX_GEMV_TOKENS * L->k);
   const size_t o_h = take(sizeof(float) * (size_t)p->gemv_pairs * L->I);
   size_t o_hb = 0, o_hl = 0, o_y = 0, o_xn = 0;
@@ -523,6 +525,7 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->dev.pair_off = (int32_t*)(b + o_po);
   p->dev.pair_list = (int32_t*)(b + o_pl);
   p->dev.pair_pos = (int32_t*)(b + o_pp);
+  p->dev.pair_w = (float*)(b + o_pw);
   p->dev.counts = (int32_t*)(b + o_cnt);
   p->h = (float*)(b + o_h);
   p->hb = gemm ? (uint16_t*)(b + o_hb) : nullptr;
@@ -1090,6 +1093,7 @@ moe_status moe_step_device_static(moe_layer* L, const float* logits, int32_t T, 
   dev.pair_off = (int32_t*)(b + ws.po);
   dev.pair_list = (int32_t*)(b + ws.pl);
   dev.pair_pos = (int32_t*)(b + ws.pp);
+  dev.pair_w = (float*)(b + ws.pw);
   dev.counts = (int32_t*)(b + ws.cnt);
   return step_device_core(L, dev, (float*)(b + ws.h), logits, T, x, out, (uint16_t*)x_res, L->compute,
                           stream_capturing(L->compute), /*no_timers=*/true);
@@ -1136,32 +1140,92 @@ moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* p
     if (L->E != L0->E || L->k != L0->k || L->H != L0->H || L->fmt != L0->fmt ||
         L->compute != L0->compute)
       return fail(MOE_ERR_INVALID_ARG, "stack layers must share E, top_k, H, format and compute stream");
-    if (lookahead && L->copy != L0->copy)
-      return fail(MOE_ERR_INVALID_ARG, "lookahead needs one copy stream shared by the stack's layers");
   }
   if (L0->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
-  if (lookahead && L0->copy == L0->compute)
-    return fail(MOE_ERR_INVALID_ARG, "lookahead needs a copy stream distinct from the compute stream");
+  if (lookahead && !(route_page_in_ok(L0->E) && up_route_next_ok(L0->fmt, L0->H, L0->E, T * L0->k)))
+    return fail(MOE_ERR_INVALID_ARG, "lookahead needs E <= 256, T * top_k <= 256 and an up kernel of this shape");
   const size_t lstride = (size_t)T * L0->E;
   const hipStream_t cs = L0->compute;
   const bool cap = stream_capturing(cs);
-  // Lookahead: routes and copies of every layer run in order on the copy
-  // stream, each layer's FFN on the compute stream after its copies, so
-  // layer l+1's copies overlap layer l's math. The copy stream first waits
-  // for the compute stream's earlier work (the previous token's FFNs still
-  // read plans and slots that these copies rewrite; it is also the fork
-  // point of a capture).
-  hipStream_t ps = cs;
-  if (lookahead) {
-    ps = L0->copy;
-    if (hipEventRecord(layers[0]->ev_routed, cs) != hipSuccess ||
-        hipStreamWaitEvent(ps, layers[0]->ev_routed, 0) != hipSuccess)
-      return fail(MOE_ERR_HIP, "fork to the copy stream failed");
+  if (!lookahead) {
+    for (int l = 0; l < n; ++l) {
+      moe_status st = step_device_impl(layers[l], plans[l], logits + l * lstride, T, x, out, (uint16_t*)x, cs,
+                                       cap, /*norm=*/1);
+      if (st) return st;
+    }
+    return MOE_OK;
   }
+  // Lookahead, one stream: layer 0 is routed and paged in alone; then, for
+  // every layer l, one launch runs l's up projection and routes and pages in
+  // l + 1 ([PE] "TL;DR": the experts of the next layer cross PCIe while this
+  // layer's math runs), then l's down projection and residual. Valid only when
+  // the router logits do not depend on the previous layer's output (given in
+  // advance), the caller's promise.
+  auto next_of = [&](int l) {
+    moe_layer* M = layers[l];
+    moe_plan* q = plans[l];
+    NextStep ns{};
+    ns.logits = logits + l * lstride;
+    ns.T = T;
+    ns.E = M->E;
+    ns.k = M->k;
+    ns.K = M->K;
+    ns.state = M->state;
+    ns.sl = state_layout(M->E, M->K);
+    ns.dev = q->dev;
+    ns.dstats = M->dstats;
+    ns.ticket = (unsigned long long*)(M->dstats + 6);
+    ns.host = M->host_store_dev;
+    ns.slots = M->slots;
+    ns.stride = M->stride;
+    // the up launch copies the first half of each missed record, the down
+    // launch the rest (16-byte pieces; the stride is a multiple of 256)
+    ns.cp_len = M->stride / 2 / 16 * 16;
+    return ns;
+  };
+  std::vector<bool> timing(n);
   for (int l = 0; l < n; ++l) {
-    moe_status st = step_device_impl(layers[l], plans[l], logits + l * lstride, T, x, out, (uint16_t*)x, ps,
-                                     cap, /*norm=*/1);
-    if (st) return st;
+    timing[l] = layers[l]->timing;
+    if (cap) layers[l]->timing = false;  // dispatch-stamped events are not captured
+  }
+  moe_status st = MOE_OK;
+  {
+    moe_layer* M = layers[0];
+    TimerRec tc{};
+    if ((st = timer_events(M, &tc)) == MOE_OK) {
+      if (launch_route_plan_page_in(logits, T, M->E, M->k, M->K, M->state, plans[0]->dev, M->dstats,
+                                    (unsigned long long*)(M->dstats + 6), M->host_store_dev, M->slots, M->stride,
+                                    cs, tc.a, tc.b) != hipSuccess)
+        st = fail(MOE_ERR_HIP, "route and page-in launch failed");
+      else
+        timer_push(M, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
+    }
+  }
+  for (int l = 0; l < n && !st; ++l) {
+    moe_layer* L = layers[l];
+    moe_plan* p = plans[l];
+    NextStep ns{};
+    if (l + 1 < n) ns = next_of(l + 1);
+    const int n_max = std::min(T * L->k, L->E);
+    st = run_ffn(L, p->dev, p->h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr, nullptr, 0,
+                 T, false, (uint16_t*)x, p->dev.counts, nullptr, /*norm=*/1, l + 1 < n ? &ns : nullptr);
+  }
+  for (int l = 0; l < n; ++l) layers[l]->timing = timing[l];
+  if (st) return st;
+  for (int l = 0; l < n; ++l) {
+    moe_layer* L = layers[l];
+    moe_plan* p = plans[l];
+    if (!cap) {  // ordering for later host-driven calls on other streams
+      HIP_TRY(hipEventRecord(L->ev_fwd_done, cs));
+      L->fwd_recorded = true;
+      HIP_TRY(hipEventRecord(p->ev_consumed, cs));
+      p->consumed_recorded = true;
+    }
+    L->dev_steps = true;
+    L->dev_pending = true;
+    p->valid = false;
+    p->dev_routed = true;
+    p->dev_tokens = T;
   }
   return MOE_OK;
 }
@@ -1261,7 +1325,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev,
-                   uint8_t* wdq, int norm) {
+                   uint8_t* wdq, int norm, const NextStep* next) {
   FfnArgs a{};
   a.norm = norm;
   a.n_dev = n_dev;
@@ -1277,6 +1341,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
   a.pair_off = dev.pair_off;
   a.pair_list = dev.pair_list;
   a.weights = dev.weights;
+  a.pair_w = dev.pair_w;
   a.o_lo = o_lo;
   a.n_exp = n_exp;
   a.T = T;
@@ -1302,13 +1367,25 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     if ((st = timer_events(L, &t1)) || (st = timer_events(L, &t2))) return st;
     a.ev0 = t1.a;
     a.ev1 = t1.b;
-    HIP_TRY(launch_ffn_up(a, L->compute));
-    timer_push(L, &t1, MOE_T_FFN_UP, up_b, flop_up);
+    if (next) {
+      // the launch also routes and pages in the next layer; its length is
+      // mostly that layer's copies, so it is timed with the page-ins
+      HIP_TRY(launch_up_route_next(a, *next, L->compute));
+      timer_push(L, &t1, MOE_T_PAGE_IN, 0.0, 0.0);
+    } else {
+      HIP_TRY(launch_ffn_up(a, L->compute));
+      timer_push(L, &t1, MOE_T_FFN_UP, up_b, flop_up);
+    }
     a.ev0 = t2.a;
     a.ev1 = t2.b;
     a.x_res = x_res;  // the down kernel completes out
-    HIP_TRY(launch_ffn_down(a, L->compute));
-    timer_push(L, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn);
+    if (next) {  // ... and copies the rest of the next layer's missed records
+      HIP_TRY(launch_ffn_down_copy_next(a, *next, L->compute));
+      timer_push(L, &t2, MOE_T_PAGE_IN, 0.0, 0.0);
+    } else {
+      HIP_TRY(launch_ffn_down(a, L->compute));
+      timer_push(L, &t2, MOE_T_FFN_DOWN, dn_b, flop_dn);
+    }
   } else {
     TimerRec t1{}, t2{}, t3{};
     if (L->fmt != MOE_FMT_BF16) {  // quantised experts: expand the wave's records to bf16 first
@@ -1388,6 +1465,7 @@ moe_status self_check(moe_layer* L) {
     dev.pair_off = (int32_t*)(b + o_po);
     dev.pair_list = (int32_t*)(b + o_pl);
     dev.weights = (float*)(b + o_w);
+    dev.pair_w = dev.weights;  // the one pair is at CSR position 0
     const bool timing = L->timing;
     L->timing = false;
     for (int perm = 0; perm < 2 && !result; ++perm) {

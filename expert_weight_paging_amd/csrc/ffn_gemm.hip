@@ -291,7 +291,7 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
           a.hb_lo[at] = f32_to_bf16_rne(h - __uint_as_float((uint32_t)hi << 16));
         }
       } else if (col0 + wn * 64 < H) {  // the last tile may hold only 128 columns
-        const float w = a.weights[a.pair_list[q]];
+        const float w = a.pair_w[q];
 #pragma unroll
         for (int n = 0; n < 4; ++n)
           a.y[(size_t)q * H + col0 + wn * 64 + n * 16 + (lane & 15)] = w * acc[m][n][j];

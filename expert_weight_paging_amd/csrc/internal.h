@@ -53,6 +53,7 @@ struct PlanDev {
   int32_t* pair_off;     // [E+1] CSR offsets over wave order
   int32_t* pair_list;    // [T*k] pair index t*k+j, grouped by expert, ascending
   int32_t* pair_pos;     // [T*k] inverse of pair_list: CSR position of pair t*k+j
+  float* pair_w;         // [T*k] router weight of the pair at each CSR position
   int32_t* counts;       // [4]: num_distinct, num_hits, num_waves, num_tokens
 };
 
@@ -155,6 +156,7 @@ struct FfnArgs {
   const int32_t* pair_off;
   const int32_t* pair_list;
   const float* weights;
+  const float* pair_w;  // router weight by CSR position (pair_list order)
   int o_lo, n_exp;     // wave's range in wave order
   int T;
   const void* x;       // [T][H]
@@ -179,6 +181,30 @@ struct FfnArgs {
 };
 
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);
+
+// The next layer's device-resolved route and page-in (as launch_route_plan_page_in),
+// carried by extra workgroups of this layer's up-projection launch.
+struct NextStep {
+  const float* logits;
+  int T, E, k, K;
+  uint8_t* state;
+  StateLayout sl;
+  PlanDev dev;
+  long long* dstats;
+  unsigned long long* ticket;
+  const uint8_t* host;
+  uint8_t* slots;
+  size_t stride;
+  size_t cp_len;  // bytes of each missed record copied by the up launch; the down launch copies the rest
+};
+// Whether a layer of this format, hidden size, E and pairs per step can take
+// the merged launch (E <= 256, pairs <= 256, the shapes the up kernel is built for).
+bool up_route_next_ok(int fmt, int H, int E, int P);
+hipError_t launch_up_route_next(const FfnArgs& a, const NextStep& n, hipStream_t s);
+// This layer's down projection, with extra workgroups that copy bytes
+// [n.cp_len, n.stride) of every record the next layer's plan (already stored
+// by the up launch) misses.
+hipError_t launch_ffn_down_copy_next(const FfnArgs& a, const NextStep& n, hipStream_t s);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t s);
 bool ffn_shape_supported(int fmt, int H, int I);
 

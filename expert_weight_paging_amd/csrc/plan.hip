@@ -4,6 +4,7 @@
 // PCIe Math, and the 4-Request Cliff". [LRU] = "Locality of reference helped
 // 94GB Qwen3.8-Flash-Next runs at 68 tok/s on one RTX 5090".
 #include "copy.h"
+#include "gemv_up.h"
 #include "internal.h"
 #include "norm.h"
 #include "wave.h"
@@ -313,7 +314,8 @@ __device__ void plan_body(const int32_t* ids, int P, int T, int E, int K, uint8_
 // Publish the plan to pinned host memory: wavefront 0 writes the wave order
 // and the header, makes its writes visible at system scope, then stores seq.
 // Device-resolved steps pass no header: their plan stays on the device.
-__device__ void publish(const PlanSmem& sm, int E, int T, int P, int D, int nH, int n_waves,
+template <class SM>
+__device__ void publish(const SM& sm, int E, int T, int P, int D, int nH, int n_waves,
                         PlanHdr* hdr, int32_t seq) {
   if (!hdr || threadIdx.x >= kWave) return;
   int32_t* h_order_e = (int32_t*)(hdr + 1);
@@ -350,8 +352,11 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ id
 // round robin (wavefront W0 + r takes r, r + NWV - W0, ...) and collect each
 // position's pairs by ballots over the step's ids (in LDS), ascending, at the
 // CSR offsets the plan left in sm.cnt (indexed by order position).
-template <int NWV, int W0>
-__device__ inline void group_small(const PlanSmem& sm, const int32_t* s_ids, int P, int D, const PlanDev& dev) {
+// wts: the step's router weights by pair index (LDS, or global memory written
+// by this workgroup before a barrier); copied into CSR order as pair_w.
+template <int NWV, int W0, class SM>
+__device__ inline void group_small(const SM& sm, const int32_t* s_ids, const float* wts, int P, int D,
+                                   const PlanDev& dev) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -368,6 +373,7 @@ __device__ inline void group_small(const PlanSmem& sm, const int32_t* s_ids, int
         const int q = base + running + __popcll(mask & below);
         dev.pair_list[q] = p;
         dev.pair_pos[p] = q;
+        dev.pair_w[q] = wts[p];
       }
       running += __popcll(mask);
     }
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(NT) void route_plan_small_kernel(const float* __res
   for (int p = threadIdx.x; p < P; p += NT) dev.ids[p] = s_ids[p];
   int D, nH, nw;
   plan_body<NT>(s_ids, P, T, E, K, state, sl, pre, dev, sm, &D, &nH, &nw);
-  group_small<NWV, 0>(sm, s_ids, P, D, dev);
+  group_small<NWV, 0>(sm, s_ids, dev.weights, P, D, dev);
   add_dstats(dstats, T, P, D, nH, nw, 0);
   publish(sm, E, T, P, D, nH, nw, hdr, seq);
 }
@@ -545,6 +551,22 @@ __device__ inline LaneState<NJ> load_lane_state(const uint8_t* state, const Stat
 // exactly the slots of the hits (every hit is in wave 0 and no miss is resident
 // when its wave starts) and, in later waves, none; and a hit keeps the slot it
 // had at the start of the step during wave 0.
+// LDS of the one-wavefront route and plan for tables of E <= 64 * NJ experts
+// (and K <= E slots): per expert, per wave-order position, the router's
+// scratch (four wavefronts' packed logits) shared with the victim keys.
+template <int NJ>
+struct WavePlanSmem {
+  static constexpr int N = kWave * NJ;
+  int cnt[N];
+  int pos[N];
+  int order_e[N];
+  int order_s[N];
+  int expert_slot[N];
+  int cpos[N];
+  __attribute__((aligned(16))) unsigned long long vkey[4 * N];
+  int warp[4];
+};
+
 // What plan_wave leaves in registers for plan_wave_store.
 template <int NJ>
 struct PlanOut {
@@ -552,9 +574,9 @@ struct PlanOut {
   long long st[NJ], clock;
 };
 
-template <int NJ>
+template <int NJ, class SM>
 __device__ void plan_wave(const int32_t* ids, int P, int E, int K, const LaneState<NJ>& pre,
-                          PlanSmem& sm, PlanOut<NJ>& out) {
+                          SM& sm, PlanOut<NJ>& out) {
   const int lane = threadIdx.x & (kWave - 1);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   int se[NJ];
@@ -695,9 +717,9 @@ __device__ void plan_wave(const int32_t* ids, int P, int E, int K, const LaneSta
 // the wave order with its slots, the CSR offsets and the counters
 // (with_order). Issued together with the per-pair stores of the other
 // wavefronts, so their latencies overlap.
-template <int NJ>
+template <int NJ, class SM>
 __device__ void plan_wave_store(const PlanOut<NJ>& out, int P, int T, int E, int K, uint8_t* state,
-                                const StateLayout& sl, const PlanDev& dev, const PlanSmem& sm, int D,
+                                const StateLayout& sl, const PlanDev& dev, const SM& sm, int D,
                                 int nH, int n_waves, bool with_state = true, bool with_order = true) {
   int32_t* g_slot_expert = (int32_t*)(state + sl.slot_expert);
   int32_t* g_expert_slot = (int32_t*)(state + sl.expert_slot);
@@ -754,18 +776,23 @@ __device__ void plan_wave_store(const PlanOut<NJ>& out, int P, int T, int E, int
 // size per launch, so "last" is a ticket that is one below a multiple of it.
 constexpr int kPageInBlocks = 64;
 constexpr int kCopyUnroll = 4;
+constexpr int kPageInPairs = 256;  // a device-resolved step: T * top_k <= K <= E <= 256
 
-template <int NJ, bool PAGE_IN>
+// vblock / nblocks: this workgroup's index among the nblocks workgroups that
+// route, plan and page in the step (PAGE_IN), which may be a part of a larger
+// launch; PM: the most pairs (T * top_k) a step may have.
+template <int NJ, bool PAGE_IN, int PM>
 __device__ void route_plan_body(const float* __restrict__ logits, int T, int E, int k, int K, uint8_t* state,
                                 const StateLayout& sl, const PlanDev& dev, PlanHdr* hdr, int32_t seq,
                                 long long* dstats, unsigned long long* ticket, const uint8_t* __restrict__ host,
-                                uint8_t* __restrict__ slots, size_t stride) {
+                                uint8_t* __restrict__ slots, size_t stride, int vblock, int nblocks,
+                                size_t cp_len) {
   constexpr int NT = 256, NWV = NT / kWave;
-  __shared__ PlanSmem sm;
-  __shared__ int32_t s_ids[kSmallPairs];
+  __shared__ WavePlanSmem<NJ> sm;
+  __shared__ int32_t s_ids[PM];
   __shared__ float s_z[NWV][MOE_MAX_TOP_K];
   __shared__ int s_rank[NWV * kWave * NJ];
-  __shared__ float s_w[kSmallPairs];
+  __shared__ float s_w[PM];
   __shared__ int s_last;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
@@ -790,12 +817,12 @@ __device__ void route_plan_body(const float* __restrict__ logits, int T, int E, 
     if (PAGE_IN && lane == 0) {
       const unsigned long long tk =
           __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (tk + 1) % gridDim.x == 0;
+      s_last = (tk + 1) % nblocks == 0;
     }
   }
   lds_barrier();
   const int D = sm.warp[0], nH = sm.warp[1], nw = sm.warp[2];
-  const bool lead = !PAGE_IN || blockIdx.x == 0;  // stores the plan, pairs and counters
+  const bool lead = !PAGE_IN || vblock == 0;  // stores the plan, pairs and counters
   const bool last = !PAGE_IN || s_last != 0;      // stores the table state
   // wavefront 0 stores the plan while wavefronts 1 .. NWV-1 store the pairs
   if (wid == 0 && (lead || last)) plan_wave_store<NJ>(out, P, T, E, K, state, sl, dev, sm, D, nH, nw, last, lead);
@@ -810,15 +837,16 @@ __device__ void route_plan_body(const float* __restrict__ logits, int T, int E, 
         dev.wave_of[p] = pos / K;
       }
     }
-    group_small<NWV, 1>(sm, s_ids, P, D, dev);
+    group_small<NWV, 1>(sm, s_ids, s_w, P, D, dev);
     add_dstats(dstats, T, P, D, nH, nw, kWave);
   }
   if constexpr (PAGE_IN) {
-    // this workgroup's share of every missed record (the single wave's order
-    // positions nH .. D-1)
+    // this workgroup's share of the first cp_len bytes of every missed record
+    // (the single wave's order positions nH .. D-1; the rest, if any, is
+    // copied by the next launch)
     for (int m = nH; m < D; ++m)
       copy_record_share<NT, kCopyUnroll>(host + (size_t)sm.order_e[m] * stride, slots + (size_t)sm.order_s[m] * stride,
-                                         stride, blockIdx.x, gridDim.x);
+                                         cp_len, vblock, nblocks);
   } else {
     publish(sm, E, T, P, D, nH, nw, hdr, seq);
   }
@@ -829,7 +857,8 @@ __global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __res
                                                               int k, int K, uint8_t* state, StateLayout sl,
                                                               PlanDev dev, PlanHdr* hdr, int32_t seq,
                                                               long long* dstats) {
-  route_plan_body<NJ, false>(logits, T, E, k, K, state, sl, dev, hdr, seq, dstats, nullptr, nullptr, nullptr, 0);
+  route_plan_body<NJ, false, kSmallPairs>(logits, T, E, k, K, state, sl, dev, hdr, seq, dstats, nullptr,
+                                          nullptr, nullptr, 0, 0, 1, 0);
 }
 
 template <int NJ>
@@ -839,7 +868,52 @@ __global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __
                                                                  unsigned long long* ticket,
                                                                  const uint8_t* __restrict__ host,
                                                                  uint8_t* __restrict__ slots, size_t stride) {
-  route_plan_body<NJ, true>(logits, T, E, k, K, state, sl, dev, nullptr, 0, dstats, ticket, host, slots, stride);
+  route_plan_body<NJ, true, kPageInPairs>(logits, T, E, k, K, state, sl, dev, nullptr, 0, dstats, ticket, host,
+                                          slots, stride, blockIdx.x, gridDim.x, stride);
+}
+
+// One launch of a stack's device-resolved steps with lookahead ([PE] "TL;DR":
+// the expert math stays on the GPU while experts cross PCIe): workgroups
+// 0 .. kPageInBlocks-1 route and plan the NEXT layer exactly as
+// route_plan_page_in_kernel does and copy the first n.cp_len bytes of each of
+// its missed records (the down launch that follows copies the rest), the
+// others run THIS layer's up projection exactly as ffn_up_kernel does (its
+// gx x experts grid numbered row by row). The next layer's copies run beside
+// this layer's math in one queue; the launch's end orders both before this
+// layer's down projection and the next layer's up projection.
+template <int F, int NJ, int RPW, int NJR>
+__global__ __launch_bounds__(256) void up_route_next_kernel(FfnArgs a, int gx, NextStep n) {
+  const int b = blockIdx.x;
+  if (b < kPageInBlocks) {
+    route_plan_body<NJR, true, kPageInPairs>(n.logits, n.T, n.E, n.k, n.K, n.state, n.sl, n.dev, nullptr, 0,
+                                             n.dstats, n.ticket, n.host, n.slots, n.stride, b, kPageInBlocks,
+                                             n.cp_len);
+    return;
+  }
+  const int u = b - kPageInBlocks;
+  gemv::ffn_up_body<F, NJ, RPW, uint16_t>(a, u % gx, u / gx);
+}
+
+template <int F, int NJR>
+hipError_t up_route_next_nj(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+  constexpr int kRPW = gemv::rpw<F>();
+  const int nj = (a.H / gemv::Fmt<F>::CV1 + kWave - 1) / kWave;
+  const int gx = (a.I + 4 * kRPW - 1) / (4 * kRPW);
+  const dim3 grid(kPageInBlocks + gx * a.n_exp), block(256);
+  switch (nj) {
+    case 1: launch_k(up_route_next_kernel<F, 1, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n); break;
+    case 2: launch_k(up_route_next_kernel<F, 2, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n); break;
+    case 4: launch_k(up_route_next_kernel<F, 4, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int F>
+hipError_t up_route_next_fmt(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+  if (n.E <= 64) return up_route_next_nj<F, 1>(a, n, s);
+  if (n.E <= 128) return up_route_next_nj<F, 2>(a, n, s);
+  return up_route_next_nj<F, 4>(a, n, s);
 }
 
 // ------------------------------------------------------------------ grouping
@@ -878,6 +952,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
       m &= m - 1;
       dev.pair_list[q] = p;
       dev.pair_pos[p] = q;
+      dev.pair_w[q] = dev.weights[p];
       ++q;
     }
     running += total;
@@ -981,9 +1056,35 @@ hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int
 
 bool route_page_in_ok(int E) { return E <= 256; }
 
+bool up_route_next_ok(int fmt, int H, int E, int P) {
+  if (E > 256 || P > kPageInPairs) return false;
+  int cv1 = 0;
+  switch (fmt) {
+    case MOE_FMT_BF16: cv1 = 8; break;
+    case MOE_FMT_FP8_E4M3_B128: cv1 = 16; break;
+    case MOE_FMT_INT4_ASYM_G128:
+    case MOE_FMT_MXFP4_B32: cv1 = 32; break;
+    default: return false;
+  }
+  const int nj = (H / cv1 + kWave - 1) / kWave;
+  return nj == 1 || nj == 2 || nj == 4;
+}
+
+hipError_t launch_up_route_next(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+  if (a.n_exp <= 0 || !up_route_next_ok(a.fmt, a.H, n.E, n.T * n.k)) return hipErrorInvalidValue;
+  switch (a.fmt) {
+    case MOE_FMT_BF16: return up_route_next_fmt<MOE_FMT_BF16>(a, n, s);
+    case MOE_FMT_FP8_E4M3_B128: return up_route_next_fmt<MOE_FMT_FP8_E4M3_B128>(a, n, s);
+    case MOE_FMT_INT4_ASYM_G128: return up_route_next_fmt<MOE_FMT_INT4_ASYM_G128>(a, n, s);
+    case MOE_FMT_MXFP4_B32: return up_route_next_fmt<MOE_FMT_MXFP4_B32>(a, n, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_route_plan_page_in(const float* logits, int T, int E, int k, int K, void* state, PlanDev dev,
                                      long long* dstats, unsigned long long* ticket, const uint8_t* host_store_dev,
                                      uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (T * k > kPageInPairs) return hipErrorInvalidValue;
   const StateLayout sl = state_layout(E, K);
   uint8_t* st = (uint8_t*)state;
 #define MOE_FUSED(NJ)                                                                                    \

@@ -347,7 +347,7 @@ moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits
  * counters are the same.
  *   logits, x, out, x_res: as moe_step_device
  * Requirements: as moe_step_device, and a workspace of
- * 10 arrays (4 * T * top_k or 4 * E bytes each, 256-byte aligned) plus
+ * 11 arrays (4 * T * top_k or 4 * E bytes each, 256-byte aligned) plus
  * 4 * T * top_k * I bytes of h within MOE_STATIC_WORKSPACE_BYTES
  * (MOE_ERR_INVALID_ARG beyond it). Every call on one GPU shares that GPU's
  * array and leaves its contents behind: calls that overlap on one GPU (two
@@ -384,14 +384,17 @@ moe_status moe_step_token_waves(moe_layer* layer, moe_plan* plan, const float* l
  * launch, the same bits) and no host synchronisation (capturable). Same requirements per layer as
  * moe_step_device; logits device float32 [n_layers][T][E]; x bf16 [T][H]
  * updated in place; out float32 [T][H] holds the last layer's MoE output.
- *   lookahead: 0 = everything on the shared compute stream, layer after
- *              layer; 1 = the route and page-in kernels of all layers run in
- *              layer order on the copy stream (shared by the layers and
- *              distinct from the compute stream) and each layer's FFN waits
- *              for its own copies only, so layer l+1's copies overlap layer
- *              l's math. Like moe_stack_forward's lookahead this is valid only
- *              when the router logits do not depend on the previous layer's
- *              output (given in advance), the caller's promise. */
+ *   lookahead: 0 = each layer routed, paged in and computed in turn;
+ *              1 = layer 0 is routed and paged in alone, then for every
+ *              layer l one launch runs l's up projection while extra
+ *              workgroups of it route layer l + 1 and page its misses in
+ *              ([PE] "TL;DR": the next experts cross PCIe while the expert
+ *              math runs), then l's down projection and residual; everything
+ *              stays on the compute stream (no cross-stream hand-over), so a
+ *              captured token is one straight chain of launches. Needs E <= 256
+ *              and T * top_k <= 256. Like moe_stack_forward's lookahead this is
+ *              valid only when the router logits do not depend on the previous
+ *              layer's output (given in advance), the caller's promise. */
 moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans,
                                     int32_t n_layers, const float* logits, int32_t num_tokens,
                                     void* x, float* out, int32_t lookahead);

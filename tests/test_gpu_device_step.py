@@ -257,8 +257,8 @@ def test_int4_stack_device(lookahead):
 
 
 def test_int4_stack_device_lookahead_graph_replays_match_eager():
-    """A token through a 3-layer int4 stack with device lookahead (copy stream
-    forked from and joined to the compute stream) captured in a HIP graph;
+    """A token through a 3-layer int4 stack with device lookahead (the next
+    layer routed and paged in by the up launch of the layer before) captured in a HIP graph;
     6 replays, with eager input copies and synchronisations between them,
     must equal an eager twin stack bit for bit (x, out, plans, table state)."""
     cfg = W.CONFIGS[4]
