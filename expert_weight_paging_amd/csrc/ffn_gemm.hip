@@ -66,6 +66,19 @@ __device__ inline bf16x8 as_bf16x8(const uint4& v) {
   return r;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight e4m3 weights (one B fragment's k-run) to bf16 operands: each exact in
+// fp32, times its block scale in fp32, rounded to nearest even.
+__device__ inline bf16x8 fp8x8_to_bf16(uint2 q, float s) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+  bf16x8 r;
+  r[0] = (__bf16)(a.x * s); r[1] = (__bf16)(a.y * s); r[2] = (__bf16)(b.x * s); r[3] = (__bf16)(b.y * s);
+  r[4] = (__bf16)(c.x * s); r[5] = (__bf16)(c.y * s); r[6] = (__bf16)(d.x * s); r[7] = (__bf16)(d.y * s);
+  return r;
+}
+
 __device__ inline uint16_t f32_to_bf16_rne(float v) {
   uint32_t b = __float_as_uint(v);
   b += 0x7FFFu + ((b >> 16) & 1u);
@@ -79,12 +92,14 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
 // read touches over all 32 banks.
 template <int CPR>
 __device__ inline int lds_chunk(int r, int c) {
-  if constexpr (CPR == 4) return r * 4 + (c ^ ((r >> 1) & 3));
+  if constexpr (CPR == 2) return r * 2 + c;
+  else if constexpr (CPR == 4) return r * 4 + (c ^ ((r >> 1) & 3));
   else return r * 8 + (c ^ (r & 7));
 }
 template <int CPR>
 __device__ inline int src_chunk(int p) {
-  if constexpr (CPR == 4) return (p & 3) ^ ((p >> 3) & 3);
+  if constexpr (CPR == 2) return p & 1;
+  else if constexpr (CPR == 4) return (p & 3) ^ ((p >> 3) & 3);
   else return (p & 7) ^ ((p >> 3) & 7);
 }
 
@@ -123,22 +138,33 @@ __device__ inline void stage_barrier() {
 // The up GEMM (k = H) runs k-steps of 64, so that every copy instruction moves
 // whole 128-byte lines (8 rows); the down GEMM (k = I, two activation tiles)
 // keeps k-steps of 32 to fit its rings.
-template <bool UP>
+// WF: the weight tile's format in LDS. bf16 weights (MOE_FMT_BF16) are read
+// as MFMA operands directly; FP8 e4m3 weights (MOE_FMT_FP8_E4M3_B128) reach LDS
+// at one byte each and become bf16 operands in registers, each weight times
+// its 128 x 128 block scale in fp32, rounded to nearest even (the same bf16
+// values as an expanded bf16 record).
+template <int WF> struct WBytes { static constexpr int B = 2; };
+template <> struct WBytes<MOE_FMT_FP8_E4M3_B128> { static constexpr int B = 1; };
+
+template <bool UP, int WF = MOE_FMT_BF16>
 struct Tiles {
   static constexpr int NA = UP ? 1 : 2;  // activation tiles: x, or (h_hi, h_lo)
   static constexpr int BUDGET_CH = 160 * 1024 / 16;
   static constexpr int BK = UP ? 64 : 32;  // reduction elements per k-step
-  static constexpr int CPR = BK / 8;       // 16-byte chunks per tile row
-  static constexpr int W_CH = BN * CPR;    // chunks of the weight tile
+  static constexpr int CPR = BK / 8;       // 16-byte chunks per activation tile row
+  static constexpr int WB = WBytes<WF>::B;  // bytes per weight
+  static constexpr int CPRW = BK * WB / 16;  // 16-byte chunks per weight tile row
+  static constexpr int W_CH = BN * CPRW;   // chunks of the weight tile
   static constexpr int NW = W_CH / kThreads;  // weight copies per thread per stage
+  static_assert(NW >= 1 && W_CH % kThreads == 0, "whole weight copies per thread");
 };
-template <bool UP, int RG>
+template <bool UP, int RG, int WF = MOE_FMT_BF16>
 struct Ring {
-  static constexpr int W_CH = Tiles<UP>::W_CH;
-  static constexpr int A_CH = Tiles<UP>::NA * RG * 64 * Tiles<UP>::CPR;  // activation chunks per stage
-  static constexpr int SW3 = (Tiles<UP>::BUDGET_CH - 3 * A_CH) / W_CH;
+  static constexpr int W_CH = Tiles<UP, WF>::W_CH;
+  static constexpr int A_CH = Tiles<UP, WF>::NA * RG * 64 * Tiles<UP, WF>::CPR;  // activation chunks per stage
+  static constexpr int SW3 = (Tiles<UP, WF>::BUDGET_CH - 3 * A_CH) / W_CH;
   static constexpr int SA = SW3 > 3 ? 3 : 2;
-  static constexpr int SW_FIT = (Tiles<UP>::BUDGET_CH - SA * A_CH) / W_CH;
+  static constexpr int SW_FIT = (Tiles<UP, WF>::BUDGET_CH - SA * A_CH) / W_CH;
   static constexpr int SW = SW_FIT > 8 ? 8 : SW_FIT;
   static_assert(SW > SA && SA >= 2, "LDS budget too small for the two rings");
 };
@@ -148,14 +174,18 @@ struct Ring {
 // it + SW - 1]; since SW > SA, the activation copy of a stage is issued after
 // its weight copy, so "stage it has landed" is "all copies up to the
 // activation copy of stage it have completed" (copies complete in order).
-template <bool UP, int RG>
-__device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (&wsrc)[Tiles<UP>::NW],
-                          int col0, int q0, int mb, int mcnt) {
-  static_assert(RG >= 1 && RG <= 4 && (RG * 64 * Tiles<UP>::CPR) % kThreads == 0,
+// wsrc: byte addresses of this thread's weight copies of k-step 0. FP8
+// weights: sc0 (up: the gate rows' block row of scales; down: this
+// wavefront's) and sc1 (up: the up rows') point at the block-scale rows of
+// this tile, one float per 128 reduction elements.
+template <bool UP, int RG, int WF>
+__device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&wsrc)[Tiles<UP, WF>::NW],
+                          const float* sc0, const float* sc1, int col0, int q0, int mb, int mcnt) {
+  static_assert(RG >= 1 && RG <= 4 && (RG * 64 * Tiles<UP, WF>::CPR) % kThreads == 0,
                 "a pass covers 64 * RG rows, copied by whole 512-chunk instructions");
-  using R = Ring<UP, RG>;
-  using Tl = Tiles<UP>;
-  constexpr int NA = Tl::NA, SA = R::SA, SW = R::SW, BK = Tl::BK, CPR = Tl::CPR;
+  using R = Ring<UP, RG, WF>;
+  using Tl = Tiles<UP, WF>;
+  constexpr int NA = Tl::NA, SA = R::SA, SW = R::SW, BK = Tl::BK, CPR = Tl::CPR, CPRW = Tl::CPRW, WB = Tl::WB;
   constexpr int GI = RG * 64 * CPR / kThreads;  // activation copies per tile per thread
   constexpr int nA = NA * GI, nW = Tl::NW;      // copy instructions per thread per stage
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -196,7 +226,7 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
     if (s < 0 || s >= nit) return;
     const uint32_t st = ldsw + (s % SW) * R::W_CH * 16;
 #pragma unroll
-    for (int i = 0; i < nW; ++i) dma16(wsrc[i] + s * BK, st + (i * kThreads) * 16);
+    for (int i = 0; i < nW; ++i) dma16(wsrc[i] + (size_t)s * BK * WB, st + (i * kThreads) * 16);
   };
 
   constexpr int MT = RG * 2;  // 16-row sub-tiles per wavefront
@@ -232,6 +262,13 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
     issue_w(it + SW - 1);
     const uint4* st = smem + (it % SA) * R::A_CH;
     const uint4* wt = smem + SA * R::A_CH + (it % SW) * R::W_CH;
+    // FP8: the block scales of this k-step (wave-uniform, one per 128 elements)
+    float s_lo = 1.f, s_hi = 1.f;
+    if constexpr (WF == MOE_FMT_FP8_E4M3_B128) {
+      const int kb = it * BK / 128;
+      s_lo = sc0[kb];
+      s_hi = UP ? sc1[kb] : s_lo;
+    }
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {  // 32-element sub-steps of one MFMA each
       // B fragments: lane holds weight-tile row (lane % 16) of the sub-tile,
@@ -243,7 +280,14 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
         // rows 128 further down the tile for n >= 2); down: columns wn*64 + n*16 ..
         const int trow = UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15))
                             : (wn * 64 + n * 16 + (lane & 15));
-        bf[n] = as_bf16x8(wt[lds_chunk<CPR>(trow, 4 * ks + (lane >> 4))]);
+        if constexpr (WF == MOE_FMT_FP8_E4M3_B128) {
+          // elements 32 ks + 8 (lane / 16) .. + 7 of the row: half (lane / 16) % 2
+          // of chunk 2 ks + lane / 32
+          const uint2* w2 = (const uint2*)&wt[lds_chunk<CPRW>(trow, 2 * ks + (lane >> 5))];
+          bf[n] = fp8x8_to_bf16(w2[(lane >> 4) & 1], n < 2 ? s_lo : s_hi);
+        } else {
+          bf[n] = as_bf16x8(wt[lds_chunk<CPRW>(trow, 4 * ks + (lane >> 4))]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < NA; ++u) {
@@ -300,9 +344,9 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint16_t* const (
   }
 }
 
-template <bool UP>
+template <bool UP, int WF>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, int tiles_per_expert) {
-  __shared__ __attribute__((aligned(16))) uint4 smem[Tiles<UP>::BUDGET_CH];
+  __shared__ __attribute__((aligned(16))) uint4 smem[Tiles<UP, WF>::BUDGET_CH];
   constexpr int BMP = 256;  // rows per pass
   // XCD-contiguous numbering: hardware block b runs on XCD b % 8; give the
   // blocks of one XCD consecutive virtual ids.
@@ -316,31 +360,51 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
   if (M <= 0) return;  // uniform over the workgroup
   const int H = a.H, I = a.I;
   const int KD = UP ? H : I;
-  // bf16 records: the slot itself, or (quantised formats) the dequantised copy
+  // bf16 weights: the slot itself or (quantised formats expanded first) the
+  // dequantised copy; FP8 weights: the slot
   const uint8_t* rec = a.wbase ? a.wbase + (size_t)(o - a.o_lo) * a.wstride
                                : a.slots + (size_t)a.order_slot[o] * a.stride;
-  const uint16_t* W = (const uint16_t*)(rec + (UP ? (size_t)0 : (size_t)2 * I * H * 2));
+  constexpr int WB = Tiles<UP, WF>::WB;
+  const uint8_t* W = rec + (UP ? (size_t)0 : (size_t)2 * I * H * WB);
   const int col0 = tile * (UP ? UP_HCOLS : DN_COLS);
   // weight copy sources: chunk p = i * 512 + tid of the weight tile is tile row
-  // p / CPR (down: rows past H, in a last half-width tile, reread row H - 1)
-  constexpr int CPR = Tiles<UP>::CPR, NW = Tiles<UP>::NW;
-  const uint16_t* wsrc[NW];
+  // p / CPRW (down: rows past H, in a last half-width tile, reread row H - 1)
+  constexpr int CPRW = Tiles<UP, WF>::CPRW, NW = Tiles<UP, WF>::NW;
+  const uint8_t* wsrc[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int p = i * kThreads + threadIdx.x;
-    const int r = p / CPR, c = src_chunk<CPR>(p);
+    const int r = p / CPRW, c = src_chunk<CPRW>(p);
     const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
-    wsrc[i] = W + (size_t)wrow * KD + c * 8;
+    wsrc[i] = W + (size_t)wrow * KD * WB + c * 16;
+  }
+  // FP8 block-scale rows of this tile: up, the gate rows' and the up rows' (a
+  // tile's 128 gate rows are one block row, and so are its 128 up rows);
+  // down, the block row of this wavefront's 64 columns (clamped for a last
+  // half-width tile, whose extra columns are discarded)
+  const float* sc0 = nullptr;
+  const float* sc1 = nullptr;
+  if constexpr (WF == MOE_FMT_FP8_E4M3_B128) {
+    const RecLayout L = rec_layout(MOE_FMT_FP8_E4M3_B128, H, I);
+    const int wn = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)) & 3;
+    if (UP) {
+      const float* s13 = (const float*)(rec + L.s13);
+      sc0 = s13 + (size_t)(col0 / 128) * (H / 128);
+      sc1 = s13 + (size_t)((I + col0) / 128) * (H / 128);
+    } else {
+      const float* sd = (const float*)(rec + L.sd);
+      sc0 = sd + (size_t)min((col0 + wn * 64) / 128, H / 128 - 1) * (I / 128);
+    }
   }
   for (int mb = 0; mb < M; mb += BMP) {
     const int mcnt = min(BMP, M - mb);
     // uniform branches: the smallest pass shape that holds mcnt rows (up: any
     // number of 64-row groups; down, with 32-wide rows: an even number)
     const int rg = (mcnt + 63) >> 6;
-    if (UP && rg == 1) gemm_pass<UP, (UP ? 1 : 2)>(a, smem, wsrc, col0, q0, mb, mcnt);
-    else if (rg <= 2) gemm_pass<UP, 2>(a, smem, wsrc, col0, q0, mb, mcnt);
-    else if (UP && rg == 3) gemm_pass<UP, (UP ? 3 : 4)>(a, smem, wsrc, col0, q0, mb, mcnt);
-    else gemm_pass<UP, 4>(a, smem, wsrc, col0, q0, mb, mcnt);
+    if (UP && rg == 1) gemm_pass<UP, (UP ? 1 : 2), WF>(a, smem, wsrc, sc0, sc1, col0, q0, mb, mcnt);
+    else if (rg <= 2) gemm_pass<UP, 2, WF>(a, smem, wsrc, sc0, sc1, col0, q0, mb, mcnt);
+    else if (UP && rg == 3) gemm_pass<UP, (UP ? 3 : 4), WF>(a, smem, wsrc, sc0, sc1, col0, q0, mb, mcnt);
+    else gemm_pass<UP, 4, WF>(a, smem, wsrc, sc0, sc1, col0, q0, mb, mcnt);
   }
 }
 
@@ -383,17 +447,31 @@ bool gemm_shape_supported(int H, int I) {
   return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0;
 }
 
+// FP8 records are read in place (no expanded copy); bf16 records, and other
+// formats' expanded copies (a.wbase), as bf16.
+bool gemm_reads_fp8(const FfnArgs& a) { return a.fmt == MOE_FMT_FP8_E4M3_B128 && !a.wbase; }
+
 hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
   const int tpe = a.I / UP_HCOLS;
-  launch_k(grouped_gemm_kernel<true>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a, tpe);
+  if (gemm_reads_fp8(a))
+    launch_k(grouped_gemm_kernel<true, MOE_FMT_FP8_E4M3_B128>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0,
+             a.ev1, a, tpe);
+  else
+    launch_k(grouped_gemm_kernel<true, MOE_FMT_BF16>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a,
+             tpe);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
   const int tpe = (a.H + DN_COLS - 1) / DN_COLS;
-  launch_k(grouped_gemm_kernel<false>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a, tpe);
+  if (gemm_reads_fp8(a))
+    launch_k(grouped_gemm_kernel<false, MOE_FMT_FP8_E4M3_B128>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0,
+             a.ev1, a, tpe);
+  else
+    launch_k(grouped_gemm_kernel<false, MOE_FMT_BF16>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a,
+             tpe);
   return hipGetLastError();
 }
 

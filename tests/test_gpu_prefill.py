@@ -203,3 +203,48 @@ def test_rmsnorm_kernel():
         ewp.rmsnorm_bf16(xd, xd)                        # in place
         torch.cuda.synchronize()
         assert torch.equal(xd, ad)
+
+
+def test_prefill_fp8_qwen_layer_reads_records_in_place():
+    """FP8 prefill at the 2048-token Qwen shape (K=92 warm, two waves): the
+    GEMMs read the FP8 records in place and widen each weight to bf16 in
+    registers (value times block scale in fp32, rounded to nearest even).
+    Against the oracle to the FP8 tolerance, and bitwise against a bf16 layer
+    whose records hold exactly those bf16 values (the expansion a separate
+    pass would have written): the same matrix-core inputs in the same order."""
+    from oracle import formats
+    cfg = W.CONFIGS[3]
+    K, T = 92, 2048
+    say("case: prefill fp8 layer E=128 k=8 H=2048 I=768 K=92 warm, 2048 tokens, in place vs expanded bf16")
+    fp8 = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt, lambda a: gen.expert_store(cfg, out=a),
+                      max_tokens=T, initial_fill=True)
+
+    def expanded(a):
+        for e in range(cfg.E):
+            g, u, d = formats.decode_record(fp8.host.array[e], cfg.fmt, cfg.H, cfg.I)
+            w13 = np.concatenate([g, u]).astype(np.float32)       # exact products rounded to fp32
+            a[e] = gen.encode_record(gen.BF16, w13, d.astype(np.float32))
+    bf = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, gen.BF16, expanded, max_tokens=T, initial_fill=True)
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((T, cfg.E)).astype(np.float32)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((T, cfg.H)).astype(np.float32))
+    lg = torch.from_numpy(logits).cuda()
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    outs = []
+    for p in (fp8, bf):
+        out = torch.empty(T, cfg.H, dtype=torch.float32, device="cuda")
+        info = p.gpu.route(p.plan, lg)
+        assert info["num_waves"] == 2 and info["num_misses"] == 36
+        for w in range(info["num_waves"]):
+            p.gpu.page_in(p.plan, w)
+            p.gpu.forward(p.plan, w, xd, out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    o_ref, ids_ref, w_ref, p_ref = fp8.ref.step(logits, x_values(x, cfg.fmt))
+    fp8.check_plan(ids_ref, w_ref, p_ref, T)
+    e = rel_err(outs[0], o_ref)
+    say("fp8 in place == expanded bf16 bitwise; rel err vs oracle %.3g" % e)
+    assert e <= TOL[cfg.fmt]
+    fp8.close()
+    bf.close()
