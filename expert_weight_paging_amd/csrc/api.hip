@@ -506,9 +506,10 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
     o_hl = take(2 * P * L->I);
     o_y = take(4 * P * L->H);
     o_xn = take(2 * (size_t)max_tokens * L->H);
-    // a wave holds at most min(K, E) experts; int4 and MXFP4 ones are each
+    // a wave holds at most min(K, E) experts; those of formats the GEMMs do
+    // not read in place (int4, MXFP4 past the LDS scale region) are each
     // expanded to a bf16 record
-    if (L->fmt != MOE_FMT_BF16 && L->fmt != MOE_FMT_FP8_E4M3_B128)
+    if (!gemm_reads_record(L->fmt, L->H, L->I))
       o_wq = take((size_t)std::min(L->K, L->E) * rec_layout(MOE_FMT_BF16, L->H, L->I).stride);
   }
   auto cleanup = [&](moe_status s) {
@@ -533,7 +534,7 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
   p->hb_lo = gemm ? (uint16_t*)(b + o_hl) : nullptr;
   p->y = gemm ? (float*)(b + o_y) : nullptr;
   p->xn = gemm ? (uint16_t*)(b + o_xn) : nullptr;
-  p->wdq = (gemm && L->fmt != MOE_FMT_BF16 && L->fmt != MOE_FMT_FP8_E4M3_B128) ? b + o_wq : nullptr;
+  p->wdq = (gemm && !gemm_reads_record(L->fmt, L->H, L->I)) ? b + o_wq : nullptr;
   const size_t hbytes = sizeof(PlanHdr) + sizeof(int32_t) * (3 * E + 1);
   if (hipHostMalloc((void**)&p->hdr, hbytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
     return cleanup(fail(MOE_ERR_HIP, "hipHostMalloc plan header"));
@@ -1389,9 +1390,10 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     }
   } else {
     TimerRec t1{}, t2{}, t3{};
-    // int4 and MXFP4 experts: the wave's records are expanded to bf16 first; FP8
-    // records are read in place by the GEMMs (weights widened in registers)
-    if (L->fmt != MOE_FMT_BF16 && L->fmt != MOE_FMT_FP8_E4M3_B128) {
+    // int4 experts (and MXFP4 past the GEMMs' LDS scale region): the wave's
+    // records are expanded to bf16 first; FP8 and MXFP4 records are read in
+    // place by the GEMMs (weights widened in registers)
+    if (!gemm_reads_record(L->fmt, L->H, L->I)) {
       if (!wdq) return fail(MOE_ERR_STATE, "plan has no dequantisation scratch");
       const size_t ws = rec_layout(MOE_FMT_BF16, L->H, L->I).stride;
       HIP_TRY(launch_dequant_bf16(a, wdq, ws, L->compute));

@@ -43,6 +43,7 @@
 // Workgroups are numbered so that each XCD (which schedules every eighth
 // workgroup and has its own L2) works through a contiguous run of experts,
 // keeping an expert's activation rows in one L2.
+#include "gemv_up.h"
 #include "internal.h"
 
 namespace moepage {
@@ -79,26 +80,42 @@ __device__ inline bf16x8 fp8x8_to_bf16(uint2 q, float s) {
   return r;
 }
 
+// Eight E2M1 codes (one word, code 2b in the low nibble of byte b) to bf16
+// operands: each exact in e4m3 and then in fp32, times the block's E8M0 scale
+// in fp32, rounded to nearest even; the same arithmetic as the decode kernels'
+// expansion of MXFP4 records.
+__device__ inline bf16x8 fp4x8_to_bf16(uint32_t q, float s) {
+  uint32_t ev, od;
+  gemv::e2m1x8_to_e4m3(q, &ev, &od);
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);
+  bf16x8 r;
+  r[0] = (__bf16)(a.x * s); r[1] = (__bf16)(c.x * s); r[2] = (__bf16)(a.y * s); r[3] = (__bf16)(c.y * s);
+  r[4] = (__bf16)(b.x * s); r[5] = (__bf16)(d.x * s); r[6] = (__bf16)(b.y * s); r[7] = (__bf16)(d.y * s);
+  return r;
+}
+
 __device__ inline uint16_t f32_to_bf16_rne(float v) {
   uint32_t b = __float_as_uint(v);
   b += 0x7FFFu + ((b >> 16) & 1u);
   return (uint16_t)(b >> 16);
 }
 
-// Tile rows of CPR 16-byte chunks (CPR = 4: 32 bf16 per row, CPR = 8: 64).
+// Tile rows of CPR 16-byte chunks (CPR = 4: 32 bf16 per row, CPR = 8: 64;
+// CPR = 2: 32 FP8 or 64 FP4 weights per row).
 // LDS chunk of logical chunk c of tile row r; and, for LDS chunk p, the
 // logical chunk it holds (its row is p / CPR): the two are inverse of each
-// other. The XOR spreads the 8 rows that one quarter-wavefront of a fragment
-// read touches over all 32 banks.
+// other. The XOR spreads the rows that one fragment read touches over the
+// banks (CPR = 2: rows 8..15 of a sub-tile hold their two chunks swapped).
 template <int CPR>
 __device__ inline int lds_chunk(int r, int c) {
-  if constexpr (CPR == 2) return r * 2 + c;
+  if constexpr (CPR == 2) return r * 2 + (c ^ ((r >> 3) & 1));
   else if constexpr (CPR == 4) return r * 4 + (c ^ ((r >> 1) & 3));
   else return r * 8 + (c ^ (r & 7));
 }
 template <int CPR>
 __device__ inline int src_chunk(int p) {
-  if constexpr (CPR == 2) return p & 1;
+  if constexpr (CPR == 2) return (p & 1) ^ ((p >> 4) & 1);
   else if constexpr (CPR == 4) return (p & 3) ^ ((p >> 3) & 3);
   else return (p & 7) ^ ((p >> 3) & 7);
 }
@@ -143,20 +160,33 @@ __device__ inline void stage_barrier() {
 // at one byte each and become bf16 operands in registers, each weight times
 // its 128 x 128 block scale in fp32, rounded to nearest even (the same bf16
 // values as an expanded bf16 record).
-template <int WF> struct WBytes { static constexpr int B = 2; };
-template <> struct WBytes<MOE_FMT_FP8_E4M3_B128> { static constexpr int B = 1; };
+// MXFP4 weights (MOE_FMT_MXFP4_B32) reach LDS at half a byte each, and the
+// tile's E8M0 scales (one byte per 32 reduction elements of a row) are copied
+// to LDS once per workgroup; each weight becomes its value times 2^(scale -
+// 127) in fp32, rounded to nearest even. The scale region holds up to 64
+// bytes per row for the up GEMM (H <= 2048) and 32 for the down GEMM
+// (I <= 1024); larger shapes read expanded bf16 copies.
+template <int WF> struct WBits { static constexpr int B = 16; };
+template <> struct WBits<MOE_FMT_FP8_E4M3_B128> { static constexpr int B = 8; };
+template <> struct WBits<MOE_FMT_MXFP4_B32> { static constexpr int B = 4; };
+constexpr int kFp4ScRowUp = 64, kFp4ScRowDn = 32;  // scale-region bytes per tile row
 
 template <bool UP, int WF = MOE_FMT_BF16>
 struct Tiles {
+  static constexpr bool FP4 = WF == MOE_FMT_MXFP4_B32;
   static constexpr int NA = UP ? 1 : 2;  // activation tiles: x, or (h_hi, h_lo)
-  static constexpr int BUDGET_CH = 160 * 1024 / 16;
-  static constexpr int BK = UP ? 64 : 32;  // reduction elements per k-step
+  // the down GEMM's k-steps are 32 wide (two activation tiles per stage),
+  // except with FP4 weights, whose 32-wide tile rows would be 16 bytes
+  static constexpr int BK = (UP || FP4) ? 64 : 32;  // reduction elements per k-step
   static constexpr int CPR = BK / 8;       // 16-byte chunks per activation tile row
-  static constexpr int WB = WBytes<WF>::B;  // bytes per weight
-  static constexpr int CPRW = BK * WB / 16;  // 16-byte chunks per weight tile row
+  static constexpr int WBITS = WBits<WF>::B;  // bits per weight
+  static constexpr int CPRW = BK * WBITS / 128;  // 16-byte chunks per weight tile row
   static constexpr int W_CH = BN * CPRW;   // chunks of the weight tile
   static constexpr int NW = W_CH / kThreads;  // weight copies per thread per stage
   static_assert(NW >= 1 && W_CH % kThreads == 0, "whole weight copies per thread");
+  static constexpr int SC_ROW = FP4 ? (UP ? kFp4ScRowUp : kFp4ScRowDn) : 0;
+  static constexpr int SC_CH = BN * SC_ROW / 16;  // the FP4 scale region, after the rings
+  static constexpr int BUDGET_CH = 160 * 1024 / 16 - SC_CH;  // for the two rings
 };
 template <bool UP, int RG, int WF = MOE_FMT_BF16>
 struct Ring {
@@ -169,6 +199,14 @@ struct Ring {
   static_assert(SW > SA && SA >= 2, "LDS budget too small for the two rings");
 };
 
+// Weight-tile row of B fragment n for this lane. up: h columns wn*32 +
+// (n%2)*16 .. (gate rows for n < 2, the matching up rows 128 further down the
+// tile for n >= 2); down: columns wn*64 + n*16 ..
+template <bool UP>
+__device__ inline int frag_row(int n, int wn, int lane) {
+  return UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15)) : (wn * 64 + n * 16 + (lane & 15));
+}
+
 // One pass over rows [mb, mb + mcnt) of expert position o, mcnt <= 64 * RG.
 // Copies are issued per k-step as [activation stage it + SA - 1][weight stage
 // it + SW - 1]; since SW > SA, the activation copy of a stage is issued after
@@ -177,7 +215,8 @@ struct Ring {
 // wsrc: byte addresses of this thread's weight copies of k-step 0. FP8
 // weights: sc0 (up: the gate rows' block row of scales; down: this
 // wavefront's) and sc1 (up: the up rows') point at the block-scale rows of
-// this tile, one float per 128 reduction elements.
+// this tile, one float per 128 reduction elements. FP4 weights: the scales
+// are in the LDS scale region, row r of the weight tile at byte r * SC_ROW.
 template <bool UP, int RG, int WF>
 __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&wsrc)[Tiles<UP, WF>::NW],
                           const float* sc0, const float* sc1, int col0, int q0, int mb, int mcnt) {
@@ -185,7 +224,8 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
                 "a pass covers 64 * RG rows, copied by whole 512-chunk instructions");
   using R = Ring<UP, RG, WF>;
   using Tl = Tiles<UP, WF>;
-  constexpr int NA = Tl::NA, SA = R::SA, SW = R::SW, BK = Tl::BK, CPR = Tl::CPR, CPRW = Tl::CPRW, WB = Tl::WB;
+  constexpr int NA = Tl::NA, SA = R::SA, SW = R::SW, BK = Tl::BK, CPR = Tl::CPR, CPRW = Tl::CPRW;
+  constexpr int WBITS = Tl::WBITS;
   constexpr int GI = RG * 64 * CPR / kThreads;  // activation copies per tile per thread
   constexpr int nA = NA * GI, nW = Tl::NW;      // copy instructions per thread per stage
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -226,7 +266,7 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
     if (s < 0 || s >= nit) return;
     const uint32_t st = ldsw + (s % SW) * R::W_CH * 16;
 #pragma unroll
-    for (int i = 0; i < nW; ++i) dma16(wsrc[i] + (size_t)s * BK * WB, st + (i * kThreads) * 16);
+    for (int i = 0; i < nW; ++i) dma16(wsrc[i] + (size_t)s * BK * WBITS / 8, st + (i * kThreads) * 16);
   };
 
   constexpr int MT = RG * 2;  // 16-row sub-tiles per wavefront
@@ -269,6 +309,14 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
       s_lo = sc0[kb];
       s_hi = UP ? sc1[kb] : s_lo;
     }
+    // FP4: the two E8M0 scales of this k-step for each of the lane's rows
+    uint32_t sc2[4] = {0u, 0u, 0u, 0u};
+    if constexpr (Tl::FP4) {
+      const uint8_t* scl = (const uint8_t*)(smem + Tl::BUDGET_CH);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        sc2[n] = *(const uint16_t*)(scl + frag_row<UP>(n, wn, lane) * Tl::SC_ROW + it * 2);
+    }
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {  // 32-element sub-steps of one MFMA each
       // B fragments: lane holds weight-tile row (lane % 16) of the sub-tile,
@@ -276,11 +324,12 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
       bf16x8 bf[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        // up: h columns wn*32 + (n%2)*16 .. (gate rows for n < 2, the matching up
-        // rows 128 further down the tile for n >= 2); down: columns wn*64 + n*16 ..
-        const int trow = UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15))
-                            : (wn * 64 + n * 16 + (lane & 15));
-        if constexpr (WF == MOE_FMT_FP8_E4M3_B128) {
+        const int trow = frag_row<UP>(n, wn, lane);
+        if constexpr (Tl::FP4) {
+          // elements 32 ks + 8 (lane / 16) .. + 7 of the row: word lane / 16 of chunk ks
+          const uint32_t q = ((const uint32_t*)&wt[lds_chunk<CPRW>(trow, ks)])[lane >> 4];
+          bf[n] = fp4x8_to_bf16(q, gemv::e8m0_to_float((uint8_t)(sc2[n] >> (8 * ks))));
+        } else if constexpr (WF == MOE_FMT_FP8_E4M3_B128) {
           // elements 32 ks + 8 (lane / 16) .. + 7 of the row: half (lane / 16) % 2
           // of chunk 2 ks + lane / 32
           const uint2* w2 = (const uint2*)&wt[lds_chunk<CPRW>(trow, 2 * ks + (lane >> 5))];
@@ -346,7 +395,8 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
 
 template <bool UP, int WF>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, int tiles_per_expert) {
-  __shared__ __attribute__((aligned(16))) uint4 smem[Tiles<UP, WF>::BUDGET_CH];
+  using Tl = Tiles<UP, WF>;
+  __shared__ __attribute__((aligned(16))) uint4 smem[Tl::BUDGET_CH + Tl::SC_CH];
   constexpr int BMP = 256;  // rows per pass
   // XCD-contiguous numbering: hardware block b runs on XCD b % 8; give the
   // blocks of one XCD consecutive virtual ids.
@@ -361,22 +411,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
   const int H = a.H, I = a.I;
   const int KD = UP ? H : I;
   // bf16 weights: the slot itself or (quantised formats expanded first) the
-  // dequantised copy; FP8 weights: the slot
+  // dequantised copy; FP8 and FP4 weights: the slot
   const uint8_t* rec = a.wbase ? a.wbase + (size_t)(o - a.o_lo) * a.wstride
                                : a.slots + (size_t)a.order_slot[o] * a.stride;
-  constexpr int WB = Tiles<UP, WF>::WB;
-  const uint8_t* W = rec + (UP ? (size_t)0 : (size_t)2 * I * H * WB);
+  constexpr int WBITS = Tl::WBITS;
+  const uint8_t* W = rec + (UP ? (size_t)0 : (size_t)2 * I * H * WBITS / 8);
   const int col0 = tile * (UP ? UP_HCOLS : DN_COLS);
   // weight copy sources: chunk p = i * 512 + tid of the weight tile is tile row
   // p / CPRW (down: rows past H, in a last half-width tile, reread row H - 1)
-  constexpr int CPRW = Tiles<UP, WF>::CPRW, NW = Tiles<UP, WF>::NW;
+  constexpr int CPRW = Tl::CPRW, NW = Tl::NW;
   const uint8_t* wsrc[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int p = i * kThreads + threadIdx.x;
     const int r = p / CPRW, c = src_chunk<CPRW>(p);
     const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
-    wsrc[i] = W + (size_t)wrow * KD * WB + c * 16;
+    wsrc[i] = W + (size_t)wrow * KD * WBITS / 8 + c * 16;
   }
   // FP8 block-scale rows of this tile: up, the gate rows' and the up rows' (a
   // tile's 128 gate rows are one block row, and so are its 128 up rows);
@@ -395,6 +445,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
       const float* sd = (const float*)(rec + L.sd);
       sc0 = sd + (size_t)min((col0 + wn * 64) / 128, H / 128 - 1) * (I / 128);
     }
+  }
+  // FP4: the tile's E8M0 scales (KD / 32 bytes per weight row, in the row
+  // order of the weight tile) into the LDS scale region, once for all passes
+  if constexpr (Tl::FP4) {
+    const RecLayout L = rec_layout(MOE_FMT_MXFP4_B32, H, I);
+    const uint8_t* sb = rec + (UP ? L.s13 : L.sd);
+    uint8_t* scl = (uint8_t*)(smem + Tl::BUDGET_CH);
+    const int words = KD / 128;  // 4-byte words of scales per row
+    for (int i = threadIdx.x; i < BN * words; i += kThreads) {
+      const int r = i / words, w = i - r * words;
+      const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
+      *(uint32_t*)(scl + r * Tl::SC_ROW + 4 * w) = *(const uint32_t*)(sb + (size_t)wrow * (KD / 32) + 4 * w);
+    }
+    __syncthreads();
   }
   for (int mb = 0; mb < M; mb += BMP) {
     const int mcnt = min(BMP, M - mb);
@@ -447,33 +511,36 @@ bool gemm_shape_supported(int H, int I) {
   return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0;
 }
 
-// FP8 records are read in place (no expanded copy); bf16 records, and other
-// formats' expanded copies (a.wbase), as bf16.
-bool gemm_reads_fp8(const FfnArgs& a) { return a.fmt == MOE_FMT_FP8_E4M3_B128 && !a.wbase; }
+// The GEMMs read bf16 and FP8 records in place, and MXFP4 records whose scale
+// rows fit the LDS scale region; int4 records, and larger MXFP4 shapes, are
+// expanded to bf16 copies first (a.wbase).
+bool gemm_reads_record(int fmt, int H, int I) {
+  if (fmt == MOE_FMT_BF16 || fmt == MOE_FMT_FP8_E4M3_B128) return true;
+  return fmt == MOE_FMT_MXFP4_B32 && H / 32 <= kFp4ScRowUp && I / 32 <= kFp4ScRowDn;
+}
 
-hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s) {
+template <bool UP>
+static hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
   if (a.n_exp <= 0) return hipSuccess;
-  const int tpe = a.I / UP_HCOLS;
-  if (gemm_reads_fp8(a))
-    launch_k(grouped_gemm_kernel<true, MOE_FMT_FP8_E4M3_B128>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0,
-             a.ev1, a, tpe);
-  else
-    launch_k(grouped_gemm_kernel<true, MOE_FMT_BF16>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a,
-             tpe);
+  const int tpe = UP ? a.I / UP_HCOLS : (a.H + DN_COLS - 1) / DN_COLS;
+  const int wf = a.wbase ? MOE_FMT_BF16 : a.fmt;
+  if (!a.wbase && !gemm_reads_record(wf, a.H, a.I)) return hipErrorInvalidValue;
+  const dim3 grid(tpe * a.n_exp), block(kThreads);
+  switch (wf) {
+    case MOE_FMT_BF16: launch_k(grouped_gemm_kernel<UP, MOE_FMT_BF16>, grid, block, s, a.ev0, a.ev1, a, tpe); break;
+    case MOE_FMT_FP8_E4M3_B128:
+      launch_k(grouped_gemm_kernel<UP, MOE_FMT_FP8_E4M3_B128>, grid, block, s, a.ev0, a.ev1, a, tpe);
+      break;
+    case MOE_FMT_MXFP4_B32:
+      launch_k(grouped_gemm_kernel<UP, MOE_FMT_MXFP4_B32>, grid, block, s, a.ev0, a.ev1, a, tpe);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s) {
-  if (a.n_exp <= 0) return hipSuccess;
-  const int tpe = (a.H + DN_COLS - 1) / DN_COLS;
-  if (gemm_reads_fp8(a))
-    launch_k(grouped_gemm_kernel<false, MOE_FMT_FP8_E4M3_B128>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0,
-             a.ev1, a, tpe);
-  else
-    launch_k(grouped_gemm_kernel<false, MOE_FMT_BF16>, dim3(tpe * a.n_exp), dim3(kThreads), s, a.ev0, a.ev1, a,
-             tpe);
-  return hipGetLastError();
-}
+hipError_t launch_gemm_up(const FfnArgs& a, hipStream_t s) { return launch_gemm<true>(a, s); }
+hipError_t launch_gemm_down(const FfnArgs& a, hipStream_t s) { return launch_gemm<false>(a, s); }
 
 hipError_t launch_combine(const FfnArgs& a, const int32_t* pair_pos, const int32_t* wave_of,
                           int wave, hipStream_t s) {

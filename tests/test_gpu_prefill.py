@@ -45,13 +45,16 @@ def test_prefill_qwen_layer_2048_tokens():
     p.close()
 
 
+@pytest.mark.parametrize("H,I", [(256, 384), (640, 256)])
 @pytest.mark.parametrize("fmt", [gen.FP8, gen.INT4, gen.MXFP4])
-def test_prefill_quantised_formats(fmt):
-    """More than 64 tokens with FP8, int4 and MXFP4 experts: the wave's records
-    are expanded to bf16 and run through the MFMA GEMMs (two waves per step)."""
-    T, E, k, H, I, K = 300, 16, 2, 256, 384, 12
+def test_prefill_quantised_formats(fmt, H, I):
+    """More than 64 tokens with FP8, int4 and MXFP4 experts through the MFMA
+    GEMMs (two waves per step): FP8 and MXFP4 records read in place, int4
+    records expanded to bf16 first. H = 640 leaves the down GEMM a last tile
+    of 128 columns (its weight and scale rows past H are clamped)."""
+    T, E, k, K = 300, 16, 2, 12
     say("case: prefill %s T=%d E=%d k=%d H=%d I=%d K=%d" % ({gen.FP8: "fp8", gen.INT4: "int4", gen.MXFP4: "mxfp4"}[fmt], T, E, k, H, I, K))
-    rng = np.random.default_rng(40 + fmt)
+    rng = np.random.default_rng(40 + fmt + H)
     recs = [gen.encode_record(fmt, (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32),
                               (rng.standard_normal((H, I)) * 0.02).astype(np.float32)) for _ in range(E)]
 
@@ -205,23 +208,26 @@ def test_rmsnorm_kernel():
         assert torch.equal(xd, ad)
 
 
-def test_prefill_fp8_qwen_layer_reads_records_in_place():
-    """FP8 prefill at the 2048-token Qwen shape (K=92 warm, two waves): the
-    GEMMs read the FP8 records in place and widen each weight to bf16 in
-    registers (value times block scale in fp32, rounded to nearest even).
-    Against the oracle to the FP8 tolerance, and bitwise against a bf16 layer
-    whose records hold exactly those bf16 values (the expansion a separate
-    pass would have written): the same matrix-core inputs in the same order."""
+@pytest.mark.parametrize("cid", [3, 6], ids=["fp8", "mxfp4"])
+def test_prefill_quantised_qwen_layer_reads_records_in_place(cid):
+    """FP8 and MXFP4 prefill at the 2048-token Qwen shape (K=92 warm, two
+    waves): the GEMMs read the records in place and widen each weight to bf16
+    in registers (value times its block scale in fp32, rounded to nearest
+    even). Against the oracle to the format's tolerance, and bitwise against a
+    bf16 layer whose records hold exactly those bf16 values (the expansion a
+    separate pass would have written): the same matrix-core inputs in the
+    same order."""
     from oracle import formats
-    cfg = W.CONFIGS[3]
+    cfg = W.CONFIGS[cid]
     K, T = 92, 2048
-    say("case: prefill fp8 layer E=128 k=8 H=2048 I=768 K=92 warm, 2048 tokens, in place vs expanded bf16")
-    fp8 = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt, lambda a: gen.expert_store(cfg, out=a),
-                      max_tokens=T, initial_fill=True)
+    say("case: prefill %s layer E=128 k=8 H=2048 I=768 K=92 warm, 2048 tokens, in place vs expanded bf16"
+        % cfg.name)
+    ql = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, cfg.fmt, lambda a: gen.expert_store(cfg, out=a),
+                     max_tokens=T, initial_fill=True)
 
     def expanded(a):
         for e in range(cfg.E):
-            g, u, d = formats.decode_record(fp8.host.array[e], cfg.fmt, cfg.H, cfg.I)
+            g, u, d = formats.decode_record(ql.host.array[e], cfg.fmt, cfg.H, cfg.I)
             w13 = np.concatenate([g, u]).astype(np.float32)       # exact products rounded to fp32
             a[e] = gen.encode_record(gen.BF16, w13, d.astype(np.float32))
     bf = PairedLayer(cfg.E, cfg.top_k, cfg.H, cfg.I, K, gen.BF16, expanded, max_tokens=T, initial_fill=True)
@@ -231,7 +237,7 @@ def test_prefill_fp8_qwen_layer_reads_records_in_place():
     lg = torch.from_numpy(logits).cuda()
     xd = torch.from_numpy(x.view(np.int16)).cuda()
     outs = []
-    for p in (fp8, bf):
+    for p in (ql, bf):
         out = torch.empty(T, cfg.H, dtype=torch.float32, device="cuda")
         info = p.gpu.route(p.plan, lg)
         assert info["num_waves"] == 2 and info["num_misses"] == 36
@@ -241,10 +247,10 @@ def test_prefill_fp8_qwen_layer_reads_records_in_place():
         torch.cuda.synchronize()
         outs.append(out.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
-    o_ref, ids_ref, w_ref, p_ref = fp8.ref.step(logits, x_values(x, cfg.fmt))
-    fp8.check_plan(ids_ref, w_ref, p_ref, T)
+    o_ref, ids_ref, w_ref, p_ref = ql.ref.step(logits, x_values(x, cfg.fmt))
+    ql.check_plan(ids_ref, w_ref, p_ref, T)
     e = rel_err(outs[0], o_ref)
-    say("fp8 in place == expanded bf16 bitwise; rel err vs oracle %.3g" % e)
+    say("%s in place == expanded bf16 bitwise; rel err vs oracle %.3g" % (cfg.name, e))
     assert e <= TOL[cfg.fmt]
-    fp8.close()
+    ql.close()
     bf.close()
