@@ -642,16 +642,30 @@ def roofline(res, workload, variant):
         kname = "grouped_gemm_kernel<%s>" % ("true" if dom == "gemm_up" else "false")
         # both GEMMs of the expert FFN together (the down GEMM's flops count h once)
         both = sum(tm[k]["flops"] for k in kinds) / (sum(tm[k]["ms"] for k in kinds) * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": kname, "achieved": round(flops, 1),
-                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(flops / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profiles(kname, variant),
-                "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
-                "algorithmic_flops_per_launch": tm[dom]["flops"] / tm[dom]["count"],
-                "weight_GBps": round(gbps, 1), "weight_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-                "gemm_up_plus_down_TFLOPs": round(both, 1),
-                "gemm_up_plus_down_frac": round(both / BF16_MFMA_PEAK_TFLOPS, 4),
-                "launch_floor_us": round(res["floor_us"], 3)}
+        both_gbps = sum(tm[k]["bytes"] for k in kinds) / (sum(tm[k]["ms"] for k in kinds) * 1e-3) / 1e9
+        # flops per weight byte = 2 x the routed rows per expert (about 2 x 128 at
+        # 2048 tokens, top-8 of 128): below the ridge of bf16 MFMA over HBM
+        # (2500 TFLOP/s / 8 TB/s = 312.5 flop/B), so the GEMMs are bound by
+        # streaming their weights, and the roofline is the HBM one
+        ai = tm[dom]["flops"] / tm[dom]["bytes"]
+        ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        common = {"kernel": kname, "traffic": traffic_from_profiles(kname, variant),
+                  "avg_launch_us": round(tm[dom]["ms"] / tm[dom]["count"] * 1e3, 3),
+                  "launches": tm[dom]["count"],
+                  "algorithmic_bytes_per_launch": tm[dom]["bytes"] / tm[dom]["count"],
+                  "algorithmic_flops_per_launch": tm[dom]["flops"] / tm[dom]["count"],
+                  "flop_per_weight_byte": round(ai, 1), "ridge_flop_per_byte": round(ridge, 1),
+                  "mfma_TFLOPs": round(flops, 1), "mfma_frac": round(flops / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "gemm_up_plus_down_GBps": round(both_gbps, 1),
+                  "gemm_up_plus_down_hbm_frac": round(both_gbps / HBM_PEAK_GBPS, 4),
+                  "gemm_up_plus_down_TFLOPs": round(both, 1),
+                  "gemm_up_plus_down_mfma_frac": round(both / BF16_MFMA_PEAK_TFLOPS, 4),
+                  "launch_floor_us": round(res["floor_us"], 3)}
+        if ai < ridge:
+            return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4), **common}
+        return {"bound": "mfma", "achieved": round(flops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / BF16_MFMA_PEAK_TFLOPS, 4), **common}
     return hbm_roofline(tm, res["floor_us"], variant)
 
 

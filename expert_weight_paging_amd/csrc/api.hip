@@ -293,7 +293,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res = nullptr,
                    const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr, int norm = 0,
-                   const NextStep* next = nullptr);
+                   const NextStep* next = nullptr, const NextStep* route2 = nullptr);
 
 moe_status self_check(moe_layer* L);
 
@@ -1157,12 +1157,14 @@ moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* p
     }
     return MOE_OK;
   }
-  // Lookahead, one stream: layer 0 is routed and paged in alone; then, for
-  // every layer l, one launch runs l's up projection and routes and pages in
-  // l + 1 ([PE] "TL;DR": the experts of the next layer cross PCIe while this
-  // layer's math runs), then l's down projection and residual. Valid only when
-  // the router logits do not depend on the previous layer's output (given in
-  // advance), the caller's promise.
+  // Lookahead, one stream: layer 0 is routed and paged in alone and layer 1
+  // routed; then, for every layer l, one launch runs l's up projection, copies
+  // the first half of each record l + 1 misses and routes l + 2, and one runs
+  // l's down projection and residual and copies the second halves ([PE]
+  // "TL;DR": the experts of the next layer cross PCIe while this layer's math
+  // runs; routing a layer before its copies are due keeps the router off the
+  // copies' path). Valid only when the router logits do not depend on the
+  // previous layers' outputs (given in advance), the caller's promise.
   auto next_of = [&](int l) {
     moe_layer* M = layers[l];
     moe_plan* q = plans[l];
@@ -1203,14 +1205,23 @@ moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* p
         timer_push(M, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
     }
   }
+  if (!st && n > 1) {  // layer 1: routed and planned only; layer 0's launches copy it
+    moe_layer* M = layers[1];
+    if (launch_route_plan_page_in(logits + lstride, T, M->E, M->k, M->K, M->state, plans[1]->dev, M->dstats,
+                                  (unsigned long long*)(M->dstats + 6), M->host_store_dev, M->slots, M->stride, cs,
+                                  nullptr, nullptr, 0) != hipSuccess)
+      st = fail(MOE_ERR_HIP, "route launch failed");
+  }
   for (int l = 0; l < n && !st; ++l) {
     moe_layer* L = layers[l];
     moe_plan* p = plans[l];
-    NextStep ns{};
+    NextStep ns{}, rs{};
     if (l + 1 < n) ns = next_of(l + 1);
+    if (l + 2 < n) rs = next_of(l + 2);
     const int n_max = std::min(T * L->k, L->E);
     st = run_ffn(L, p->dev, p->h, nullptr, nullptr, nullptr, 0, n_max, T * L->k, T, x, out, 0, nullptr, nullptr, 0,
-                 T, false, (uint16_t*)x, p->dev.counts, nullptr, /*norm=*/1, l + 1 < n ? &ns : nullptr);
+                 T, false, (uint16_t*)x, p->dev.counts, nullptr, /*norm=*/1, l + 1 < n ? &ns : nullptr,
+                 l + 2 < n ? &rs : nullptr);
   }
   for (int l = 0; l < n; ++l) layers[l]->timing = timing[l];
   if (st) return st;
@@ -1327,7 +1338,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev,
-                   uint8_t* wdq, int norm, const NextStep* next) {
+                   uint8_t* wdq, int norm, const NextStep* next, const NextStep* route2) {
   FfnArgs a{};
   a.norm = norm;
   a.n_dev = n_dev;
@@ -1372,7 +1383,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     if (next) {
       // the launch also routes and pages in the next layer; its length is
       // mostly that layer's copies, so it is timed with the page-ins
-      HIP_TRY(launch_up_route_next(a, *next, L->compute));
+      HIP_TRY(launch_up_route_next(a, *next, route2, L->compute));
       timer_push(L, &t1, MOE_T_PAGE_IN, 0.0, 0.0);
     } else {
       HIP_TRY(launch_ffn_up(a, L->compute));

@@ -250,8 +250,9 @@ __global__ __launch_bounds__(512) void down_copy_next_kernel(FfnArgs a, NextStep
   if (b < kCopyBlocks) {
     const int D = n.dev.counts[0], nH = n.dev.counts[1];
     for (int m = nH; m < D; ++m) {
-      const size_t e = (size_t)n.dev.order_expert[m], sl = (size_t)n.dev.order_slot[m];
-      copy_record_share<512, 4>(n.host + e * n.stride + n.cp_len, n.slots + sl * n.stride + n.cp_len,
+      const int e = n.dev.order_expert[m], sl = n.dev.order_slot[m];
+      if (e < 0 || e >= n.E || sl < 0 || sl >= n.K) continue;  // never produced by the plan
+      copy_record_share<512, 4>(n.host + (size_t)e * n.stride + n.cp_len, n.slots + (size_t)sl * n.stride + n.cp_len,
                                 n.stride - n.cp_len, b, kCopyBlocks);
     }
     return;

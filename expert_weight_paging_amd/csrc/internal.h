@@ -140,7 +140,8 @@ hipError_t launch_route_plan_small(const float* logits, int T, int E, int k, int
 bool route_page_in_ok(int E);
 hipError_t launch_route_plan_page_in(const float* logits, int T, int E, int k, int K, void* state, PlanDev dev,
                                      long long* dstats, unsigned long long* ticket, const uint8_t* host_store_dev,
-                                     uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+                                     uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                                     size_t cp_len = ~(size_t)0);
 // Device-resolved page-in of a single-wave plan: copies the records of wave
 // order positions [counts[1], counts[0]) (the misses) from the device-mapped
 // host store into their slots.
@@ -182,8 +183,9 @@ struct FfnArgs {
 
 hipError_t launch_ffn_up(const FfnArgs& a, hipStream_t s);
 
-// The next layer's device-resolved route and page-in (as launch_route_plan_page_in),
-// carried by extra workgroups of this layer's up-projection launch.
+// A layer of a stack whose device-resolved route and page-in (as
+// launch_route_plan_page_in) run in extra workgroups of an earlier layer's
+// launches.
 struct NextStep {
   const float* logits;
   int T, E, k, K;
@@ -200,7 +202,10 @@ struct NextStep {
 // Whether a layer of this format, hidden size, E and pairs per step can take
 // the merged launch (E <= 256, pairs <= 256, the shapes the up kernel is built for).
 bool up_route_next_ok(int fmt, int H, int E, int P);
-hipError_t launch_up_route_next(const FfnArgs& a, const NextStep& n, hipStream_t s);
+// This layer's up projection, with extra workgroups that copy the first
+// n.cp_len bytes of every record the next layer's plan (already stored)
+// misses and, with r, workgroups that route and plan the layer r (route only).
+hipError_t launch_up_route_next(const FfnArgs& a, const NextStep& n, const NextStep* r, hipStream_t s);
 // This layer's down projection, with extra workgroups that copy bytes
 // [n.cp_len, n.stride) of every record the next layer's plan (already stored
 // by the up launch) misses.

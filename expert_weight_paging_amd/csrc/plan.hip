@@ -861,59 +861,78 @@ __global__ __launch_bounds__(256) void route_plan_wave_kernel(const float* __res
                                           nullptr, nullptr, 0, 0, 1, 0);
 }
 
+// cp_len: bytes of each missed record copied (the record stride for a whole
+// page-in, 0 to route and plan only).
 template <int NJ>
 __global__ __launch_bounds__(256) void route_plan_page_in_kernel(const float* __restrict__ logits, int T,
                                                                  int E, int k, int K, uint8_t* state,
                                                                  StateLayout sl, PlanDev dev, long long* dstats,
                                                                  unsigned long long* ticket,
                                                                  const uint8_t* __restrict__ host,
-                                                                 uint8_t* __restrict__ slots, size_t stride) {
+                                                                 uint8_t* __restrict__ slots, size_t stride,
+                                                                 size_t cp_len) {
   route_plan_body<NJ, true, kPageInPairs>(logits, T, E, k, K, state, sl, dev, nullptr, 0, dstats, ticket, host,
-                                          slots, stride, blockIdx.x, gridDim.x, stride);
+                                          slots, stride, blockIdx.x, gridDim.x, cp_len);
 }
 
 // One launch of a stack's device-resolved steps with lookahead ([PE] "TL;DR":
-// the expert math stays on the GPU while experts cross PCIe): workgroups
-// 0 .. kPageInBlocks-1 route and plan the NEXT layer exactly as
-// route_plan_page_in_kernel does and copy the first n.cp_len bytes of each of
-// its missed records (the down launch that follows copies the rest), the
-// others run THIS layer's up projection exactly as ffn_up_kernel does (its
-// gx x experts grid numbered row by row). The next layer's copies run beside
-// this layer's math in one queue; the launch's end orders both before this
-// layer's down projection and the next layer's up projection.
+// the expert math stays on the GPU while experts cross PCIe), three groups of
+// workgroups: 0 .. kPageInBlocks-1 copy the first n.cp_len bytes of each
+// record that the NEXT layer's plan (stored by an earlier launch) pages in
+// (the down launch that follows copies the rest); the next nroute route and
+// plan the layer AFTER the next one exactly as route_plan_page_in_kernel
+// does, without copying, so that its copies can start at the beginning of the
+// next layer's up launch; the others run THIS layer's up projection exactly
+// as ffn_up_kernel does (its gx x experts grid numbered row by row). The
+// copies and the routing run beside this layer's math in one queue; the
+// launch's end orders them before this layer's down projection and the next
+// layer's up projection.
 template <int F, int NJ, int RPW, int NJR>
-__global__ __launch_bounds__(256) void up_route_next_kernel(FfnArgs a, int gx, NextStep n) {
+__global__ __launch_bounds__(256) void up_route_next_kernel(FfnArgs a, int gx, NextStep n, NextStep r,
+                                                            int nroute) {
   const int b = blockIdx.x;
   if (b < kPageInBlocks) {
-    route_plan_body<NJR, true, kPageInPairs>(n.logits, n.T, n.E, n.k, n.K, n.state, n.sl, n.dev, nullptr, 0,
-                                             n.dstats, n.ticket, n.host, n.slots, n.stride, b, kPageInBlocks,
-                                             n.cp_len);
+    const int D = n.dev.counts[0], nH = n.dev.counts[1];
+    for (int m = nH; m < D; ++m) {
+      const int e = n.dev.order_expert[m], sl = n.dev.order_slot[m];
+      if (e < 0 || e >= n.E || sl < 0 || sl >= n.K) continue;  // never produced by the plan
+      copy_record_share<256, kCopyUnroll>(n.host + (size_t)e * n.stride, n.slots + (size_t)sl * n.stride,
+                                          n.cp_len, b, kPageInBlocks);
+    }
     return;
   }
-  const int u = b - kPageInBlocks;
+  if (b < kPageInBlocks + nroute) {
+    route_plan_body<NJR, true, kPageInPairs>(r.logits, r.T, r.E, r.k, r.K, r.state, r.sl, r.dev, nullptr, 0,
+                                             r.dstats, r.ticket, r.host, r.slots, r.stride, b - kPageInBlocks,
+                                             nroute, 0);
+    return;
+  }
+  const int u = b - kPageInBlocks - nroute;
   gemv::ffn_up_body<F, NJ, RPW, uint16_t>(a, u % gx, u / gx);
 }
 
 template <int F, int NJR>
-hipError_t up_route_next_nj(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+hipError_t up_route_next_nj(const FfnArgs& a, const NextStep& n, const NextStep* r, hipStream_t s) {
   constexpr int kRPW = gemv::rpw<F>();
   const int nj = (a.H / gemv::Fmt<F>::CV1 + kWave - 1) / kWave;
   const int gx = (a.I + 4 * kRPW - 1) / (4 * kRPW);
-  const dim3 grid(kPageInBlocks + gx * a.n_exp), block(256);
+  const int nroute = r ? kPageInBlocks : 0;
+  const NextStep rr = r ? *r : n;
+  const dim3 grid(kPageInBlocks + nroute + gx * a.n_exp), block(256);
   switch (nj) {
-    case 1: launch_k(up_route_next_kernel<F, 1, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n); break;
-    case 2: launch_k(up_route_next_kernel<F, 2, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n); break;
-    case 4: launch_k(up_route_next_kernel<F, 4, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n); break;
+    case 1: launch_k(up_route_next_kernel<F, 1, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n, rr, nroute); break;
+    case 2: launch_k(up_route_next_kernel<F, 2, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n, rr, nroute); break;
+    case 4: launch_k(up_route_next_kernel<F, 4, kRPW, NJR>, grid, block, s, a.ev0, a.ev1, a, gx, n, rr, nroute); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int F>
-hipError_t up_route_next_fmt(const FfnArgs& a, const NextStep& n, hipStream_t s) {
-  if (n.E <= 64) return up_route_next_nj<F, 1>(a, n, s);
-  if (n.E <= 128) return up_route_next_nj<F, 2>(a, n, s);
-  return up_route_next_nj<F, 4>(a, n, s);
+hipError_t up_route_next_fmt(const FfnArgs& a, const NextStep& n, const NextStep* r, hipStream_t s) {
+  if (n.E <= 64) return up_route_next_nj<F, 1>(a, n, r, s);
+  if (n.E <= 128) return up_route_next_nj<F, 2>(a, n, r, s);
+  return up_route_next_nj<F, 4>(a, n, r, s);
 }
 
 // ------------------------------------------------------------------ grouping
@@ -1070,26 +1089,29 @@ bool up_route_next_ok(int fmt, int H, int E, int P) {
   return nj == 1 || nj == 2 || nj == 4;
 }
 
-hipError_t launch_up_route_next(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+hipError_t launch_up_route_next(const FfnArgs& a, const NextStep& n, const NextStep* r, hipStream_t s) {
   if (a.n_exp <= 0 || !up_route_next_ok(a.fmt, a.H, n.E, n.T * n.k)) return hipErrorInvalidValue;
+  if (r && (r->E != n.E || !up_route_next_ok(a.fmt, a.H, r->E, r->T * r->k))) return hipErrorInvalidValue;
   switch (a.fmt) {
-    case MOE_FMT_BF16: return up_route_next_fmt<MOE_FMT_BF16>(a, n, s);
-    case MOE_FMT_FP8_E4M3_B128: return up_route_next_fmt<MOE_FMT_FP8_E4M3_B128>(a, n, s);
-    case MOE_FMT_INT4_ASYM_G128: return up_route_next_fmt<MOE_FMT_INT4_ASYM_G128>(a, n, s);
-    case MOE_FMT_MXFP4_B32: return up_route_next_fmt<MOE_FMT_MXFP4_B32>(a, n, s);
+    case MOE_FMT_BF16: return up_route_next_fmt<MOE_FMT_BF16>(a, n, r, s);
+    case MOE_FMT_FP8_E4M3_B128: return up_route_next_fmt<MOE_FMT_FP8_E4M3_B128>(a, n, r, s);
+    case MOE_FMT_INT4_ASYM_G128: return up_route_next_fmt<MOE_FMT_INT4_ASYM_G128>(a, n, r, s);
+    case MOE_FMT_MXFP4_B32: return up_route_next_fmt<MOE_FMT_MXFP4_B32>(a, n, r, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_route_plan_page_in(const float* logits, int T, int E, int k, int K, void* state, PlanDev dev,
                                      long long* dstats, unsigned long long* ticket, const uint8_t* host_store_dev,
-                                     uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                                     uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                                     size_t cp_len) {
   if (T * k > kPageInPairs) return hipErrorInvalidValue;
+  cp_len = cp_len < stride ? cp_len / 16 * 16 : stride;
   const StateLayout sl = state_layout(E, K);
   uint8_t* st = (uint8_t*)state;
 #define MOE_FUSED(NJ)                                                                                    \
   launch_k(route_plan_page_in_kernel<NJ>, dim3(kPageInBlocks), dim3(256), s, ev0, ev1, logits, T, E, k, K, st, \
-           sl, dev, dstats, ticket, host_store_dev, slots, stride)
+           sl, dev, dstats, ticket, host_store_dev, slots, stride, cp_len)
   if (E <= 64) MOE_FUSED(1);
   else if (E <= 128) MOE_FUSED(2);
   else if (E <= 256) MOE_FUSED(4);

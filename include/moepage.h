@@ -389,16 +389,19 @@ moe_status moe_step_token_waves(moe_layer* layer, moe_plan* plan, const float* l
  * moe_step_device; logits device float32 [n_layers][T][E]; x bf16 [T][H]
  * updated in place; out float32 [T][H] holds the last layer's MoE output.
  *   lookahead: 0 = each layer routed, paged in and computed in turn;
- *              1 = layer 0 is routed and paged in alone, then for every
- *              layer l one launch runs l's up projection while extra
- *              workgroups of it route layer l + 1 and page its misses in
- *              ([PE] "TL;DR": the next experts cross PCIe while the expert
- *              math runs), then l's down projection and residual; everything
+ *              1 = layer 0 is routed and paged in alone and layer 1 routed,
+ *              then for every layer l one launch runs l's up projection while
+ *              extra workgroups of it copy the first half of each record
+ *              layer l + 1 misses and route layer l + 2, and one launch runs
+ *              l's down projection and residual while extra workgroups copy
+ *              the second halves ([PE] "TL;DR": the next experts cross PCIe
+ *              while the expert math runs; a layer is routed one launch pair
+ *              before its copies, so they start with the launch); everything
  *              stays on the compute stream (no cross-stream hand-over), so a
  *              captured token is one straight chain of launches. Needs E <= 256
  *              and T * top_k <= 256. Like moe_stack_forward's lookahead this is
  *              valid only when the router logits do not depend on the previous
- *              layer's output (given in advance), the caller's promise. */
+ *              layers' outputs (given in advance), the caller's promise. */
 moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* plans,
                                     int32_t n_layers, const float* logits, int32_t num_tokens,
                                     void* x, float* out, int32_t lookahead);

@@ -4,8 +4,9 @@ output within the format's tolerance of the oracle on that layer's GPU input,
 the residual exact up to rare one-ulp flips, and the hidden state within the
 accumulated bound of an independent oracle chain. The product paths the
 benchmark times (a HIP graph of device-resolved steps per decode token, the
-strict-order stack driver for the prefill chunk) must then give bitwise the
-same hidden states as the checked layer-by-layer runs.
+strict-order stack driver for the prefill chunk; for the decode stack also
+the graph with lookahead) must then give bitwise the same hidden states as
+the checked layer-by-layer runs.
 
 [PE] "What does Paged Experts actually do?": 48 MoE layers of 128 experts,
 8 per token."""
@@ -69,6 +70,25 @@ def test_int4_stack_48_layers_every_layer():
     s2 = _stats(pair.layers)
     assert {k: s2[k] - s1[k] for k in s1} == s1
     say("graph replays equal the checked layer-by-layer run; stats %s" % s1)
+    del g
+    # the same with lookahead (copies of layer l + 1 beside layer l's math,
+    # routing two layers ahead): the same plans, so the same bits and counters
+    pair.reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=compute):
+        ewp.stack_forward_device(pair.layers, pair.plans, lg_buf, xg, og, lookahead=True)
+    torch.cuda.synchronize()
+    for t in range(tokens):
+        with torch.cuda.stream(compute):
+            lg_buf.copy_(lg_all[t])
+            xg.copy_(x0_all[t])
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xg, finals[t]) and torch.equal(og, lasts[t]), t
+    s3 = _stats(pair.layers)
+    assert {k: s3[k] - s2[k] for k in s1} == s1
+    say("lookahead graph replays equal the checked run too")
     del g
     pair.close()
 
