@@ -67,7 +67,8 @@ def log(*a):
 
 # source file of each kernel whose counters are stored (plus the shared headers)
 KERNEL_SOURCE = {"ffn_up_kernel": "ffn_gemv.hip", "ffn_down_kernel": "ffn_gemv.hip",
-                 "grouped_gemm_kernel<true>": "ffn_gemm.hip", "grouped_gemm_kernel<false>": "ffn_gemm.hip",
+                 # the bf16-weight instances (second template argument: the weight format)
+                 "grouped_gemm_kernel<true,1>": "ffn_gemm.hip", "grouped_gemm_kernel<false,1>": "ffn_gemm.hip",
                  "combine_kernel": "ffn_gemm.hip", "route_plan_small_kernel": "plan.hip",
                  "route_plan_wave_kernel": "plan.hip", "route_plan_page_in_kernel": "plan.hip",
                  "page_in_kernel": "page_in.hip"}
@@ -639,7 +640,7 @@ def roofline(res, workload, variant):
         sec = tm[dom]["ms"] * 1e-3
         flops = tm[dom]["flops"] / sec / 1e12
         gbps = tm[dom]["bytes"] / sec / 1e9
-        kname = "grouped_gemm_kernel<%s>" % ("true" if dom == "gemm_up" else "false")
+        kname = "grouped_gemm_kernel<%s,1>" % ("true" if dom == "gemm_up" else "false")
         # both GEMMs of the expert FFN together (the down GEMM's flops count h once)
         both = sum(tm[k]["flops"] for k in kinds) / (sum(tm[k]["ms"] for k in kinds) * 1e-3) / 1e12
         both_gbps = sum(tm[k]["bytes"] for k in kinds) / (sum(tm[k]["ms"] for k in kinds) * 1e-3) / 1e9
