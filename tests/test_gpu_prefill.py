@@ -45,13 +45,15 @@ def test_prefill_qwen_layer_2048_tokens():
     p.close()
 
 
-@pytest.mark.parametrize("H,I", [(256, 384), (640, 256)])
+@pytest.mark.parametrize("H,I", [(256, 384), (640, 256), (2176, 128)])
 @pytest.mark.parametrize("fmt", [gen.FP8, gen.INT4, gen.MXFP4])
 def test_prefill_quantised_formats(fmt, H, I):
     """More than 64 tokens with FP8, int4 and MXFP4 experts through the MFMA
     GEMMs (two waves per step): FP8 and MXFP4 records read in place, int4
     records expanded to bf16 first. H = 640 leaves the down GEMM a last tile
-    of 128 columns (its weight and scale rows past H are clamped)."""
+    of 128 columns (its weight and scale rows past H are clamped); H = 2176
+    gives MXFP4 68 scale bytes per up row, past the GEMM's LDS scale region,
+    so those records take the expansion pass instead."""
     T, E, k, K = 300, 16, 2, 12
     say("case: prefill %s T=%d E=%d k=%d H=%d I=%d K=%d" % ({gen.FP8: "fp8", gen.INT4: "int4", gen.MXFP4: "mxfp4"}[fmt], T, E, k, H, I, K))
     rng = np.random.default_rng(40 + fmt + H)
