@@ -506,8 +506,8 @@ moe_status moe_plan_create(const moe_layer* L, int32_t max_tokens, moe_plan** ou
     o_hl = take(2 * P * L->I);
     o_y = take(4 * P * L->H);
     o_xn = take(2 * (size_t)max_tokens * L->H);
-    // a wave holds at most min(K, E) experts; those of formats the GEMMs do
-    // not read in place (int4, MXFP4 past the LDS scale region) are each
+    // a wave holds at most min(K, E) experts; those of shapes the GEMMs do
+    // not read in place (4-bit formats past the LDS scale region) are each
     // expanded to a bf16 record
     if (!gemm_reads_record(L->fmt, L->H, L->I))
       o_wq = take((size_t)std::min(L->K, L->E) * rec_layout(MOE_FMT_BF16, L->H, L->I).stride);
@@ -1401,9 +1401,9 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
     }
   } else {
     TimerRec t1{}, t2{}, t3{};
-    // int4 experts (and MXFP4 past the GEMMs' LDS scale region): the wave's
-    // records are expanded to bf16 first; FP8 and MXFP4 records are read in
-    // place by the GEMMs (weights widened in registers)
+    // 4-bit experts past the GEMMs' LDS scale region: the wave's records are
+    // expanded to bf16 first; otherwise the GEMMs read the records in place
+    // (weights widened in registers)
     if (!gemm_reads_record(L->fmt, L->H, L->I)) {
       if (!wdq) return fail(MOE_ERR_STATE, "plan has no dequantisation scratch");
       const size_t ws = rec_layout(MOE_FMT_BF16, L->H, L->I).stride;

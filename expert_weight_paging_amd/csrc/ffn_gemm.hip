@@ -95,6 +95,24 @@ __device__ inline bf16x8 fp4x8_to_bf16(uint32_t q, float s) {
   return r;
 }
 
+// Eight int4 codes (one word, code 2b in the low nibble of byte b) of one
+// 128-group to bf16 operands: (q - z) * s in fp32 with the group's fp16 scale
+// and zero point (exact in fp32), rounded to nearest even; the same arithmetic
+// as the decode kernels' expansion of int4 records.
+__device__ inline bf16x8 int4x8_to_bf16(uint32_t q, float s, float z) {
+  const uint32_t ev = q & 0x0F0F0F0Fu, od = (q >> 4) & 0x0F0F0F0Fu;
+  bf16x8 r;
+  r[0] = (__bf16)(((float)(ev & 0xFFu) - z) * s);
+  r[1] = (__bf16)(((float)(od & 0xFFu) - z) * s);
+  r[2] = (__bf16)(((float)((ev >> 8) & 0xFFu) - z) * s);
+  r[3] = (__bf16)(((float)((od >> 8) & 0xFFu) - z) * s);
+  r[4] = (__bf16)(((float)((ev >> 16) & 0xFFu) - z) * s);
+  r[5] = (__bf16)(((float)((od >> 16) & 0xFFu) - z) * s);
+  r[6] = (__bf16)(((float)((ev >> 24) & 0xFFu) - z) * s);
+  r[7] = (__bf16)(((float)((od >> 24) & 0xFFu) - z) * s);
+  return r;
+}
+
 __device__ inline uint16_t f32_to_bf16_rne(float v) {
   uint32_t b = __float_as_uint(v);
   b += 0x7FFFu + ((b >> 16) & 1u);
@@ -160,32 +178,36 @@ __device__ inline void stage_barrier() {
 // at one byte each and become bf16 operands in registers, each weight times
 // its 128 x 128 block scale in fp32, rounded to nearest even (the same bf16
 // values as an expanded bf16 record).
-// MXFP4 weights (MOE_FMT_MXFP4_B32) reach LDS at half a byte each, and the
-// tile's E8M0 scales (one byte per 32 reduction elements of a row) are copied
-// to LDS once per workgroup; each weight becomes its value times 2^(scale -
-// 127) in fp32, rounded to nearest even. The scale region holds up to 64
-// bytes per row for the up GEMM (H <= 2048) and 32 for the down GEMM
-// (I <= 1024); larger shapes read expanded bf16 copies.
+// MXFP4 weights (MOE_FMT_MXFP4_B32) and int4 weights (MOE_FMT_INT4_ASYM_G128)
+// reach LDS at half a byte each, and the tile's scale rows are copied to an
+// LDS region once per workgroup: MXFP4, one E8M0 byte per 32 reduction
+// elements of a row (each weight becomes its value times 2^(scale - 127) in
+// fp32); int4, the row's fp16 scales then its fp16 zero points, one each per
+// 128-group (each weight becomes (q - z) * s in fp32); either way rounded to
+// nearest even. Both take KD / 32 bytes per row; the scale region holds up to
+// 64 bytes per row for the up GEMM and 32 for the down GEMM (H <= 2048, I <=
+// 1024); larger shapes read expanded bf16 copies.
 template <int WF> struct WBits { static constexpr int B = 16; };
 template <> struct WBits<MOE_FMT_FP8_E4M3_B128> { static constexpr int B = 8; };
 template <> struct WBits<MOE_FMT_MXFP4_B32> { static constexpr int B = 4; };
-constexpr int kFp4ScRowUp = 64, kFp4ScRowDn = 32;  // scale-region bytes per tile row
+template <> struct WBits<MOE_FMT_INT4_ASYM_G128> { static constexpr int B = 4; };
+constexpr int kQ4ScRowUp = 64, kQ4ScRowDn = 32;  // scale-region bytes per tile row
 
 template <bool UP, int WF = MOE_FMT_BF16>
 struct Tiles {
-  static constexpr bool FP4 = WF == MOE_FMT_MXFP4_B32;
+  static constexpr bool Q4 = WF == MOE_FMT_MXFP4_B32 || WF == MOE_FMT_INT4_ASYM_G128;  // 4-bit weights
   static constexpr int NA = UP ? 1 : 2;  // activation tiles: x, or (h_hi, h_lo)
   // the down GEMM's k-steps are 32 wide (two activation tiles per stage),
-  // except with FP4 weights, whose 32-wide tile rows would be 16 bytes
-  static constexpr int BK = (UP || FP4) ? 64 : 32;  // reduction elements per k-step
+  // except with 4-bit weights, whose 32-wide tile rows would be 16 bytes
+  static constexpr int BK = (UP || Q4) ? 64 : 32;  // reduction elements per k-step
   static constexpr int CPR = BK / 8;       // 16-byte chunks per activation tile row
   static constexpr int WBITS = WBits<WF>::B;  // bits per weight
   static constexpr int CPRW = BK * WBITS / 128;  // 16-byte chunks per weight tile row
   static constexpr int W_CH = BN * CPRW;   // chunks of the weight tile
   static constexpr int NW = W_CH / kThreads;  // weight copies per thread per stage
   static_assert(NW >= 1 && W_CH % kThreads == 0, "whole weight copies per thread");
-  static constexpr int SC_ROW = FP4 ? (UP ? kFp4ScRowUp : kFp4ScRowDn) : 0;
-  static constexpr int SC_CH = BN * SC_ROW / 16;  // the FP4 scale region, after the rings
+  static constexpr int SC_ROW = Q4 ? (UP ? kQ4ScRowUp : kQ4ScRowDn) : 0;
+  static constexpr int SC_CH = BN * SC_ROW / 16;  // the 4-bit formats' scale region, after the rings
   static constexpr int BUDGET_CH = 160 * 1024 / 16 - SC_CH;  // for the two rings
 };
 template <bool UP, int RG, int WF = MOE_FMT_BF16>
@@ -215,8 +237,9 @@ __device__ inline int frag_row(int n, int wn, int lane) {
 // wsrc: byte addresses of this thread's weight copies of k-step 0. FP8
 // weights: sc0 (up: the gate rows' block row of scales; down: this
 // wavefront's) and sc1 (up: the up rows') point at the block-scale rows of
-// this tile, one float per 128 reduction elements. FP4 weights: the scales
-// are in the LDS scale region, row r of the weight tile at byte r * SC_ROW.
+// this tile, one float per 128 reduction elements. 4-bit weights: the scales
+// (and int4 zero points) are in the LDS scale region, row r of the weight
+// tile at byte r * SC_ROW.
 template <bool UP, int RG, int WF>
 __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&wsrc)[Tiles<UP, WF>::NW],
                           const float* sc0, const float* sc1, int col0, int q0, int mb, int mcnt) {
@@ -309,13 +332,18 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
       s_lo = sc0[kb];
       s_hi = UP ? sc1[kb] : s_lo;
     }
-    // FP4: the two E8M0 scales of this k-step for each of the lane's rows
+    // MXFP4: the two E8M0 scales of this k-step for each of the lane's rows;
+    // int4: the fp16 scale (low half) and zero point (high half) of the
+    // 128-group holding this k-step
     uint32_t sc2[4] = {0u, 0u, 0u, 0u};
-    if constexpr (Tl::FP4) {
+    if constexpr (Tl::Q4) {
       const uint8_t* scl = (const uint8_t*)(smem + Tl::BUDGET_CH);
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        sc2[n] = *(const uint16_t*)(scl + frag_row<UP>(n, wn, lane) * Tl::SC_ROW + it * 2);
+      for (int n = 0; n < 4; ++n) {
+        const uint8_t* rr = scl + frag_row<UP>(n, wn, lane) * Tl::SC_ROW;
+        if constexpr (WF == MOE_FMT_MXFP4_B32) sc2[n] = *(const uint16_t*)(rr + it * 2);
+        else sc2[n] = *(const uint32_t*)(rr + (it >> 1) * 4);
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {  // 32-element sub-steps of one MFMA each
@@ -325,10 +353,14 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int trow = frag_row<UP>(n, wn, lane);
-        if constexpr (Tl::FP4) {
+        if constexpr (Tl::Q4) {
           // elements 32 ks + 8 (lane / 16) .. + 7 of the row: word lane / 16 of chunk ks
           const uint32_t q = ((const uint32_t*)&wt[lds_chunk<CPRW>(trow, ks)])[lane >> 4];
-          bf[n] = fp4x8_to_bf16(q, gemv::e8m0_to_float((uint8_t)(sc2[n] >> (8 * ks))));
+          if constexpr (WF == MOE_FMT_MXFP4_B32)
+            bf[n] = fp4x8_to_bf16(q, gemv::e8m0_to_float((uint8_t)(sc2[n] >> (8 * ks))));
+          else
+            bf[n] = int4x8_to_bf16(q, gemv::half_to_float((uint16_t)sc2[n]),
+                                   gemv::half_to_float((uint16_t)(sc2[n] >> 16)));
         } else if constexpr (WF == MOE_FMT_FP8_E4M3_B128) {
           // elements 32 ks + 8 (lane / 16) .. + 7 of the row: half (lane / 16) % 2
           // of chunk 2 ks + lane / 32
@@ -411,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
   const int H = a.H, I = a.I;
   const int KD = UP ? H : I;
   // bf16 weights: the slot itself or (quantised formats expanded first) the
-  // dequantised copy; FP8 and FP4 weights: the slot
+  // dequantised copy; FP8 and 4-bit weights: the slot
   const uint8_t* rec = a.wbase ? a.wbase + (size_t)(o - a.o_lo) * a.wstride
                                : a.slots + (size_t)a.order_slot[o] * a.stride;
   constexpr int WBITS = Tl::WBITS;
@@ -446,17 +478,34 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(FfnArgs a, in
       sc0 = sd + (size_t)min((col0 + wn * 64) / 128, H / 128 - 1) * (I / 128);
     }
   }
-  // FP4: the tile's E8M0 scales (KD / 32 bytes per weight row, in the row
-  // order of the weight tile) into the LDS scale region, once for all passes
-  if constexpr (Tl::FP4) {
-    const RecLayout L = rec_layout(MOE_FMT_MXFP4_B32, H, I);
-    const uint8_t* sb = rec + (UP ? L.s13 : L.sd);
+  // 4-bit formats: the tile's scale rows (in the row order of the weight
+  // tile) into the LDS scale region, once for all passes. MXFP4: KD / 32
+  // E8M0 bytes per row; int4: per 128-group its fp16 scale then its fp16
+  // zero point (KD / 32 bytes per row)
+  if constexpr (Tl::Q4) {
     uint8_t* scl = (uint8_t*)(smem + Tl::BUDGET_CH);
-    const int words = KD / 128;  // 4-byte words of scales per row
-    for (int i = threadIdx.x; i < BN * words; i += kThreads) {
-      const int r = i / words, w = i - r * words;
-      const int wrow = UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
-      *(uint32_t*)(scl + r * Tl::SC_ROW + 4 * w) = *(const uint32_t*)(sb + (size_t)wrow * (KD / 32) + 4 * w);
+    auto tile_row = [&](int r) {
+      return UP ? (r < UP_HCOLS ? col0 + r : I + col0 + (r - UP_HCOLS)) : min(col0 + r, H - 1);
+    };
+    if constexpr (WF == MOE_FMT_MXFP4_B32) {
+      const RecLayout L = rec_layout(MOE_FMT_MXFP4_B32, H, I);
+      const uint8_t* sb = rec + (UP ? L.s13 : L.sd);
+      const int words = KD / 128;  // 4-byte words of scales per row
+      for (int i = threadIdx.x; i < BN * words; i += kThreads) {
+        const int r = i / words, w = i - r * words;
+        *(uint32_t*)(scl + r * Tl::SC_ROW + 4 * w) =
+            *(const uint32_t*)(sb + (size_t)tile_row(r) * (KD / 32) + 4 * w);
+      }
+    } else {
+      const RecLayout L = rec_layout(MOE_FMT_INT4_ASYM_G128, H, I);
+      const uint16_t* sb = (const uint16_t*)(rec + (UP ? L.s13 : L.sd));
+      const uint16_t* zb = (const uint16_t*)(rec + (UP ? L.z13 : L.zd));
+      const int G = KD / 128;  // groups per row
+      for (int i = threadIdx.x; i < BN * 2 * G; i += kThreads) {
+        const int r = i / (2 * G), c = i - r * 2 * G;
+        const size_t at = (size_t)tile_row(r) * G + (c >> 1);
+        ((uint16_t*)(scl + r * Tl::SC_ROW))[c] = (c & 1) ? zb[at] : sb[at];
+      }
     }
     __syncthreads();
   }
@@ -511,12 +560,16 @@ bool gemm_shape_supported(int H, int I) {
   return H > 0 && I > 0 && H % 128 == 0 && I % 128 == 0;
 }
 
-// The GEMMs read bf16 and FP8 records in place, and MXFP4 records whose scale
-// rows fit the LDS scale region; int4 records, and larger MXFP4 shapes, are
-// expanded to bf16 copies first (a.wbase).
+// The GEMMs read bf16 and FP8 records in place, and MXFP4 and int4 records
+// whose scale rows fit the LDS scale region; larger 4-bit shapes are expanded
+// to bf16 copies first (a.wbase).
 bool gemm_reads_record(int fmt, int H, int I) {
   if (fmt == MOE_FMT_BF16 || fmt == MOE_FMT_FP8_E4M3_B128) return true;
-  return fmt == MOE_FMT_MXFP4_B32 && H / 32 <= kFp4ScRowUp && I / 32 <= kFp4ScRowDn;
+  // scale-region bytes per row: MXFP4 KD / 32 E8M0 bytes; int4 KD / 128 fp16
+  // scales and as many zero points, KD / 32 bytes too
+  if (fmt == MOE_FMT_MXFP4_B32 || fmt == MOE_FMT_INT4_ASYM_G128)
+    return H / 32 <= kQ4ScRowUp && I / 32 <= kQ4ScRowDn;
+  return false;
 }
 
 template <bool UP>
@@ -533,6 +586,9 @@ static hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
       break;
     case MOE_FMT_MXFP4_B32:
       launch_k(grouped_gemm_kernel<UP, MOE_FMT_MXFP4_B32>, grid, block, s, a.ev0, a.ev1, a, tpe);
+      break;
+    case MOE_FMT_INT4_ASYM_G128:
+      launch_k(grouped_gemm_kernel<UP, MOE_FMT_INT4_ASYM_G128>, grid, block, s, a.ev0, a.ev1, a, tpe);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -223,7 +223,8 @@ hipError_t launch_combine(const FfnArgs& a, const int32_t* pair_pos, const int32
                           hipStream_t s);
 bool gemm_shape_supported(int H, int I);
 // Whether the grouped GEMMs read this format's records in their slots (bf16,
-// FP8, and MXFP4 with H <= 2048 and I <= 1024) rather than bf16 expansions.
+// FP8, and int4 and MXFP4 with H <= 2048 and I <= 1024) rather than bf16
+// expansions.
 bool gemm_reads_record(int fmt, int H, int I);
 
 hipError_t launch_residual(const uint16_t* x_in, const float* out, uint16_t* x_out, int64_t n,

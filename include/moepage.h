@@ -177,9 +177,9 @@ void moe_layer_destroy(moe_layer* layer);
 /* Create a plan for up to max_tokens tokens per route call with this layer.
  * Allocates small device arrays (ids, weights, slot map, grouping), the
  * pinned host-visible plan and the FFN workspace; with max_tokens above
- * MOE_MAX_GEMV_TOKENS the GEMM workspace too (for int4 layers, and MXFP4
- * layers with H > 2048 or I > 1024, it includes min(K, E) bf16 records,
- * 6 * H * I bytes each). Errors:
+ * MOE_MAX_GEMV_TOKENS the GEMM workspace too (for int4 and MXFP4 layers
+ * with H > 2048 or I > 1024 it includes min(K, E) bf16 records, 6 * H * I
+ * bytes each). Errors:
  * MOE_ERR_INVALID_ARG (max_tokens < 1; more than MOE_MAX_GEMV_TOKENS tokens
  * on an f32 layer or with H or I not a multiple of 128), MOE_ERR_HIP. */
 moe_status moe_plan_create(const moe_layer* layer, int32_t max_tokens, moe_plan** out);
@@ -256,11 +256,11 @@ moe_status moe_page_in(moe_layer* layer, const moe_plan* plan, int32_t wave);
  * (W_up x_t)), reading each expert from its slot. For T <= MOE_MAX_GEMV_TOKENS
  * the weights are streamed once per wave (GEMV path); with more tokens the
  * token-grouped bf16 MFMA GEMM runs (H and I multiples of 128): FP8 records,
- * and MXFP4 records with H <= 2048 and I <= 1024, are read in place and
- * widened to bf16 in registers; int4 records (and larger MXFP4 shapes) are
- * first expanded to bf16 in the plan's workspace (either way each weight
- * times its scale, rounded to nearest even); f32 layers are limited to the
- * GEMV path.
+ * and int4 and MXFP4 records with H <= 2048 and I <= 1024, are read in place
+ * and widened to bf16 in registers; larger int4 and MXFP4 shapes are first
+ * expanded to bf16 in the plan's workspace (either way each weight is its
+ * dequantised value in fp32 rounded to nearest even); f32 layers are limited
+ * to the GEMV path.
  * A wave with both resident and missed experts is computed in two launches on
  * the GEMV path (residents first, while the copies are in flight), decided
  * from the plan alone, so results are bitwise reproducible.

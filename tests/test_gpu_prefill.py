@@ -49,11 +49,11 @@ def test_prefill_qwen_layer_2048_tokens():
 @pytest.mark.parametrize("fmt", [gen.FP8, gen.INT4, gen.MXFP4])
 def test_prefill_quantised_formats(fmt, H, I):
     """More than 64 tokens with FP8, int4 and MXFP4 experts through the MFMA
-    GEMMs (two waves per step): FP8 and MXFP4 records read in place, int4
-    records expanded to bf16 first. H = 640 leaves the down GEMM a last tile
-    of 128 columns (its weight and scale rows past H are clamped); H = 2176
-    gives MXFP4 68 scale bytes per up row, past the GEMM's LDS scale region,
-    so those records take the expansion pass instead."""
+    GEMMs (two waves per step), the records read in place. H = 640 leaves the
+    down GEMM a last tile of 128 columns (its weight and scale rows past H are
+    clamped); H = 2176 gives the 4-bit formats 68 bytes of scales (and zero
+    points) per up row, past the GEMM's LDS scale region, so their records
+    take the expansion pass to bf16 instead."""
     T, E, k, K = 300, 16, 2, 12
     say("case: prefill %s T=%d E=%d k=%d H=%d I=%d K=%d" % ({gen.FP8: "fp8", gen.INT4: "int4", gen.MXFP4: "mxfp4"}[fmt], T, E, k, H, I, K))
     rng = np.random.default_rng(40 + fmt + H)
@@ -210,12 +210,12 @@ def test_rmsnorm_kernel():
         assert torch.equal(xd, ad)
 
 
-@pytest.mark.parametrize("cid", [3, 6], ids=["fp8", "mxfp4"])
+@pytest.mark.parametrize("cid", [3, 4, 6], ids=["fp8", "int4", "mxfp4"])
 def test_prefill_quantised_qwen_layer_reads_records_in_place(cid):
-    """FP8 and MXFP4 prefill at the 2048-token Qwen shape (K=92 warm, two
-    waves): the GEMMs read the records in place and widen each weight to bf16
-    in registers (value times its block scale in fp32, rounded to nearest
-    even). Against the oracle to the format's tolerance, and bitwise against a
+    """FP8, int4 and MXFP4 prefill at the 2048-token Qwen shape (K=92 warm,
+    two waves): the GEMMs read the records in place and widen each weight to
+    bf16 in registers (value times its block scale, or (q - z) times s, in
+    fp32, rounded to nearest even). Against the oracle to the format's tolerance, and bitwise against a
     bf16 layer whose records hold exactly those bf16 values (the expansion a
     separate pass would have written): the same matrix-core inputs in the
     same order."""
