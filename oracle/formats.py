@@ -15,7 +15,7 @@ Record of one expert (H = hidden, I = intermediate), in this order:
 The record stride is the payload rounded up to a multiple of 256 bytes; the
 padding is zero.
 
-Formats (readings, the design doc lists them):
+Formats (readings where the pages name a format but not its layout):
   f32   : float32 weights.
   bf16  : bfloat16 weights.
   fp8   : OCP float8 e4m3fn codes (bias 7, max 448, no infinities, NaN = S.1111.111),

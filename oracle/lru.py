@@ -12,7 +12,7 @@ own page-in.
 State per layer: slot_expert[K] (-1 = empty), expert_slot[E] (-1 = absent),
 stamp[K] (-1 = empty slot), clock (starts at 0).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * distinct set D = sorted distinct routed ids; hits H = resident members of D,
     misses M = the rest, both ascending; the wave order is H followed by M and
     waves are consecutive chunks of K of it, so n_waves = ceil(|D| / K) and a
