@@ -44,3 +44,53 @@ def test_default_mode_follows_the_one_wave_condition():
     assert mode("stack-int4") == (False, True)
     assert mode("stack-int4", lookahead=True) == (False, False)
     assert mode("prefill-bf16") == (False, False)
+
+
+def _bench_module():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    return b
+
+
+def _timing(entries):
+    names = ("route", "page_in", "ffn_up", "ffn_down", "gemm_up", "gemm_down", "combine")
+    t = {k: {"count": 0, "ms": 0.0, "bytes": 0.0, "flops": 0.0} for k in names}
+    for k, v in entries.items():
+        t[k].update(v)
+    return t
+
+
+def test_decode_roofline_is_the_ffn_pair_over_hbm():
+    """Achieved = the weight bytes of both FFN launches over their summed
+    event time; each kernel's own figure beside it."""
+    b = _bench_module()
+    tm = _timing({"ffn_up": {"count": 4, "ms": 4 * 10e-3, "bytes": 4 * 50331648.0},
+                  "ffn_down": {"count": 4, "ms": 4 * 7e-3, "bytes": 4 * 25165824.0}})
+    r = b.hbm_roofline(tm, 3.9, "no such variant")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - 75497472.0 / 17e-6 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+    assert abs(r["kernels"]["ffn_up_kernel"]["achieved"] - 50331648.0 / 10e-6 / 1e9) < 0.1
+    assert r["traffic"] is None  # no counters stored for this variant
+
+
+def test_prefill_roofline_takes_the_binding_roof():
+    """A grouped GEMM below the bf16 MFMA ridge (312.5 flop per weight byte) is
+    reported against HBM, one above it against the matrix cores; the other
+    roof's figure is kept beside it."""
+    b = _bench_module()
+    W = 268435456.0  # weight bytes per launch
+    res = {"floor_us": 3.9}
+    for ai, bound in ((128.0, "hbm"), (400.0, "mfma")):
+        res["timing"] = _timing({"gemm_up": {"count": 3, "ms": 3 * 0.08, "bytes": 3 * W, "flops": 3 * W * ai},
+                                 "gemm_down": {"count": 3, "ms": 3 * 0.07, "bytes": 3 * W / 2,
+                                               "flops": 3 * W / 2 * ai}})
+        r = b.roofline(res, "prefill-bf16", "no such variant")
+        assert r["bound"] == bound and r["kernel"] == "grouped_gemm_kernel<true,1>"
+        assert abs(r["flop_per_weight_byte"] - ai) < 0.1
+        gbps, tflops = W / 80e-6 / 1e9, W * ai / 80e-6 / 1e12
+        if bound == "hbm":
+            assert abs(r["achieved"] - gbps) < 0.2 and abs(r["mfma_TFLOPs"] - tflops) < 0.2
+        else:
+            assert abs(r["achieved"] - tflops) < 0.2 and r["unit"] == "TFLOP/s"
