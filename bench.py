@@ -420,16 +420,17 @@ def build_stack(cfg, dev, torch, max_tokens, initial_fill):
 
 
 def resolve_default_mode(args):
-    """Without a mode flag, a decode step whose batch fits one wave (B * top_k <= K)
-    runs as a device-resolved step, the stack as one HIP graph per token (the
-    captured single-wave path); batches beyond one wave, --lookahead and
+    """Without a mode flag, a decode step runs device-resolved (one wave when
+    B * top_k <= K, else the expert waves it needs, at most 16), the stack as
+    one HIP graph per token (the captured single-wave path); --lookahead and
     prefill run host-driven."""
     if args.host or args.device or args.graph or args.waves == "token":
         return
     import workloads as W
     if args.workload.startswith("decode"):
         cfg = W.CONFIGS[DECODE_CONFIG[args.workload]]
-        if args.batch * cfg.top_k <= (args.slots or cfg.K):
+        K = args.slots or cfg.K
+        if args.batch <= 64 and -(-min(args.batch * cfg.top_k, cfg.E) // K) <= 16:
             args.device = True
     elif args.workload == "stack-int4" and not args.lookahead:
         args.graph = True
@@ -443,7 +444,7 @@ def mode_name(args):
     if args.graph:
         return "device-resolved steps (kernel page-in) captured in one HIP graph per token" + la
     if args.device:
-        return "device-resolved steps (kernel page-in, no host synchronisation)" + la
+        return "device-resolved steps (kernel page-in, no host synchronisation; expert waves when B * top_k > K)" + la
     return "one-layer lookahead" if args.lookahead else "strict layer order"
 
 
@@ -670,6 +671,38 @@ def roofline(res, workload, variant):
     return hbm_roofline(tm, res["floor_us"], variant)
 
 
+def expert_ffn_bytes(fmt, H, I):
+    """Weight bytes one expert's up launch (W13 and its scales / zero points)
+    and down launch (W_d and its tables) read, by the record formats."""
+    n13, nd = 2 * I * H, H * I
+    if fmt == 0:   # f32
+        return 4 * n13, 4 * nd
+    if fmt == 1:   # bf16
+        return 2 * n13, 2 * nd
+    if fmt == 2:   # FP8 e4m3, fp32 scales per 128 x 128 block
+        return n13 + 4 * (n13 // (128 * 128)), nd + 4 * (nd // (128 * 128))
+    if fmt == 3:   # int4, fp16 scale and zero point per 128 weights
+        return n13 // 2 + 4 * (n13 // 128), nd // 2 + 4 * (nd // 128)
+    if fmt == 4:   # MXFP4, one E8M0 byte per 32 weights
+        return n13 // 2 + n13 // 32, nd // 2 + nd // 32
+    raise ValueError(fmt)
+
+
+def exact_ffn_bytes(tm, refs, cfg):
+    """The decode FFN timers of device-resolved steps count the most experts a
+    step can route (the host does not see the plan); the timed steps' exact
+    bytes are their distinct experts (the layer counters' refs, summed over
+    the steps, which the event-timed pass replays) times each expert's bytes.
+    Host-driven launches count exactly, and this gives the same figure."""
+    up, dn = expert_ffn_bytes(cfg.fmt, cfg.H, cfg.I)
+    out = {k: dict(v) for k, v in tm.items()}
+    if out["ffn_up"]["count"]:
+        out["ffn_up"]["bytes"] = float(refs * up)
+    if out["ffn_down"]["count"]:
+        out["ffn_down"]["bytes"] = float(refs * dn)
+    return out
+
+
 def hbm_roofline(tm, floor_us, variant, cache=None):
     """The decode step's expert FFN, its two kernels (gate/up + SiLU, down +
     weighted combine) together: algorithmic bytes (the weight bytes of the
@@ -717,7 +750,8 @@ def cold_only_line(args, torch, dev, variant):
             "config": {"workload": "%d independent %s MoE layers of the Qwen3-30B-A3B shape taken in turn, "
                                    "K=%d, batch %d; value = tokens/s of one layer (layer-steps/s x batch)"
                                    % (cold["layers"], FMT_NAME[cfg.fmt], K, args.batch)},
-            "roofline": hbm_roofline(cold["timing"], ewp.timing_floor(), variant + " cold", cache="cold")}
+            "roofline": hbm_roofline(exact_ffn_bytes(cold["timing"], cold["stats"]["refs"], cfg),
+                                     ewp.timing_floor(), variant + " cold", cache="cold")}
 
 
 def main():
@@ -817,6 +851,11 @@ def main():
         log("cold pass: %d layers x %d steps, %.3f ms per layer-step"
             % (cold["layers"], cold["steps"], cold["ms_per_layer_step"]))
     tm, st, cfg = res["timing"], res["stats"], res["cfg"]
+    if args.workload.startswith("decode"):
+        tm = exact_ffn_bytes(tm, st["refs"], cfg)
+        res["timing"] = tm
+        if cold is not None:
+            cold["timing"] = exact_ffn_bytes(cold["timing"], cold["stats"]["refs"], cfg)
     pin = tm["page_in"]
     line = {
         "metric": METRIC,

@@ -293,7 +293,7 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res = nullptr,
                    const int32_t* n_dev = nullptr, uint8_t* wdq = nullptr, int norm = 0,
-                   const NextStep* next = nullptr, const NextStep* route2 = nullptr);
+                   const NextStep* next = nullptr, const NextStep* route2 = nullptr, int res_last = 0);
 
 moe_status self_check(moe_layer* L);
 
@@ -953,25 +953,69 @@ bool stream_capturing(hipStream_t s) {
   return c != hipStreamCaptureStatusNone;
 }
 
+// Waves a device-resolved step of T tokens may need: its distinct experts
+// (at most min(T * top_k, E)) in chunks of K.
+constexpr int kMaxDeviceWaves = 16;
+int device_waves(const moe_layer* L, int T) {
+  const int D = std::min(T * L->k, L->E);
+  return (D + L->K - 1) / L->K;
+}
+
+// Device-resolved step that may need more than one wave ([PE] "What happens
+// with more than one request?": each wave pages in its misses, then computes
+// its experts; the plan is the host-driven one): one launch routes and plans
+// every wave, then, for each wave w the step may have, a kernel page-in of
+// w's misses and w's FFN over wave-order positions w * K .., all on the
+// compute stream, so wave w + 1's copies follow wave w's math (they may
+// overwrite its slots). Launches for waves the step does not have find no
+// work (the counts are read on the device). Wave 0 writes out and later waves
+// add to it; the stack residual is applied by the launch holding the step's
+// last expert.
+moe_status step_device_waves(moe_layer* L, const PlanDev& dev, float* h, const float* logits, int32_t T,
+                             const void* x, float* out, uint16_t* x_res, int nw, int norm) {
+  const hipStream_t cs = L->compute;
+  TimerRec tr{};
+  moe_status st = timer_events(L, &tr);
+  if (st) return st;
+  if (launch_route_plan_small(logits, T, L->E, L->k, L->K, L->state, dev, nullptr, 0, cs, tr.a, tr.b,
+                              L->dstats) != hipSuccess)
+    return fail(MOE_ERR_HIP, "route launch failed");
+  timer_push(L, &tr, MOE_T_ROUTE, 0.0, 0.0);
+  for (int w = 0; w < nw; ++w) {
+    TimerRec tc{};
+    if ((st = timer_events(L, &tc))) return st;
+    if (launch_page_in_device(L->host_store_dev, L->slots, L->stride, dev, L->E, L->K, cs, tc.a, tc.b, w) !=
+        hipSuccess)
+      return fail(MOE_ERR_HIP, "page-in launch failed");
+    timer_push(L, &tc, MOE_T_PAGE_IN, 0.0, 0.0);
+    st = run_ffn(L, dev, h, nullptr, nullptr, nullptr, w * L->K, L->K, T * L->k, T, x, out, w > 0, nullptr,
+                 nullptr, 0, T, false, x_res, dev.counts, nullptr, norm, nullptr, nullptr, /*res_last=*/1);
+    if (st) return st;
+  }
+  return MOE_OK;
+}
+
 moe_status step_device_check(const moe_layer* L, const moe_plan* p, int32_t T) {
   if (!L || !p) return fail(MOE_ERR_INVALID_ARG, "null layer or plan");
   if (p->layer != L) return fail(MOE_ERR_INVALID_ARG, "plan was created for another layer");
   if (T < 1 || T > p->max_tokens || T > MOE_MAX_GEMV_TOKENS)
     return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in 1..min(max_tokens, 64)");
-  if ((int64_t)T * L->k > L->K)
-    return fail(MOE_ERR_INVALID_ARG, "T * top_k exceeds K: the step may need more than one wave");
   if (!route_small_ok(T, L->k)) return fail(MOE_ERR_INVALID_ARG, "too many pairs for one route launch");
+  if (device_waves(L, T) > kMaxDeviceWaves)
+    return fail(MOE_ERR_INVALID_ARG, "the step may need more than " + std::to_string(kMaxDeviceWaves) +
+                                         " waves (T * top_k far above K)");
   if (!L->host_store_dev) return fail(MOE_ERR_STATE, "host store is not mapped into the device");
   if (L->cur_plan) return fail(MOE_ERR_STATE, "a host-driven step of this layer is unfinished");
   return MOE_OK;
 }
 
-// Device-resolved single-wave step: route + plan (kept on the device,
-// counters in dstats) and the kernel page-in of the misses on stream `ps`,
-// then the expert FFN (expert count read on the device) and the optional stack
-// residual on the compute stream. With ps != compute the host records
-// L->ev_copied on ps and the compute stream waits for it (under capture the
-// pair becomes a graph dependency).
+// Device-resolved step: route + plan (kept on the device, counters in
+// dstats) and the kernel page-in of the misses on stream `ps`, then the expert
+// FFN (expert count read on the device) and the optional stack residual on the
+// compute stream. With ps != compute the host records L->ev_copied on ps and
+// the compute stream waits for it (under capture the pair becomes a graph
+// dependency). A step that may need several waves runs step_device_waves, all
+// on the compute stream.
 moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const float* logits, int32_t T,
                             const void* x, float* out, uint16_t* x_res, hipStream_t ps, bool cap,
                             bool no_timers, int norm = 0) {
@@ -979,7 +1023,10 @@ moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const fl
   const bool timing = L->timing;
   if (cap || no_timers) L->timing = false;  // dispatch-stamped events are not captured
   moe_status st = MOE_OK;
-  do {
+  const int nw = device_waves(L, T);
+  if (nw > 1) {
+    st = step_device_waves(L, dev, h, logits, T, x, out, x_res, nw, norm);
+  } else do {
     TimerRec tr{}, tc{};
     if (ps == cs && route_page_in_ok(L->E)) {
       // one launch routes, plans and pages in (timed as the page-in; its ticket
@@ -1029,12 +1076,8 @@ moe_status step_device_core(moe_layer* L, const PlanDev& dev, float* h, const fl
   return MOE_OK;
 }
 
-// Device-resolved single-wave step: route + plan (kept on the device,
-// counters in dstats) and the kernel page-in of the misses on stream `ps`,
-// then the expert FFN (expert count read on the device) and the optional stack
-// residual on the compute stream. With ps != compute the host records
-// L->ev_copied on ps and the compute stream waits for it (under capture the
-// pair becomes a graph dependency).
+// Device-resolved step with a plan's arrays (step_device_core), then the
+// plan's consumption event.
 moe_status step_device_impl(moe_layer* L, moe_plan* p, const float* logits, int32_t T, const void* x,
                             float* out, uint16_t* x_res, hipStream_t ps, bool cap, int norm = 0) {
   moe_status st = step_device_core(L, p->dev, p->h, logits, T, x, out, x_res, ps, cap, false, norm);
@@ -1146,6 +1189,9 @@ moe_status moe_stack_forward_device(moe_layer* const* layers, moe_plan* const* p
   if (L0->fmt == MOE_FMT_F32) return fail(MOE_ERR_FORMAT, "the stack residual is bf16");
   if (lookahead && !(route_page_in_ok(L0->E) && up_route_next_ok(L0->fmt, L0->H, L0->E, T * L0->k)))
     return fail(MOE_ERR_INVALID_ARG, "lookahead needs E <= 256, T * top_k <= 256 and an up kernel of this shape");
+  for (int l = 0; lookahead && l < n; ++l)
+    if (device_waves(layers[l], T) > 1)
+      return fail(MOE_ERR_INVALID_ARG, "lookahead needs single-wave steps (T * top_k <= K)");
   const size_t lstride = (size_t)T * L0->E;
   const hipStream_t cs = L0->compute;
   const bool cap = stream_capturing(cs);
@@ -1338,9 +1384,10 @@ moe_status run_ffn(moe_layer* L, const PlanDev& dev, float* h, uint16_t* hb, uin
                    float* y, int o_lo, int n_exp, int n_pairs, int T, const void* x, float* out,
                    int accumulate, const int32_t* pair_pos, const int32_t* wave_of, int wave,
                    int max_rows, bool combine, uint16_t* x_res, const int32_t* n_dev,
-                   uint8_t* wdq, int norm, const NextStep* next, const NextStep* route2) {
+                   uint8_t* wdq, int norm, const NextStep* next, const NextStep* route2, int res_last) {
   FfnArgs a{};
   a.norm = norm;
+  a.res_last = res_last;
   a.n_dev = n_dev;
   a.fmt = L->fmt;
   a.E = L->E;

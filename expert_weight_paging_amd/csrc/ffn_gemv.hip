@@ -115,13 +115,16 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
   const int T = a.T;
   const int my_t = threadIdx.x / RW, my_r = threadIdx.x % RW;
   const bool mine = (int)threadIdx.x < T * RW && r0 + my_r < H;
+  // device-resolved steps: the step's distinct experts D, read on the device
+  const int D = a.n_dev ? *a.n_dev : a.o_lo + a.n_exp;
+  const bool res = a.x_res && (!a.res_last || (a.o_lo < D && D <= a.o_lo + a.n_exp));
   float o_prev = 0.f;
   uint16_t x_prev = 0;
   if (mine) {
     if (a.accumulate) o_prev = a.out[(size_t)my_t * H + r0 + my_r];
-    if (a.x_res) x_prev = a.x_res[(size_t)my_t * H + r0 + my_r];
+    if (res) x_prev = a.x_res[(size_t)my_t * H + r0 + my_r];
   }
-  const int n_exp = a.n_dev ? min(a.n_exp, *a.n_dev) : a.n_exp;
+  const int n_exp = min(a.n_exp, D - a.o_lo);  // none past the step's last expert
   if (wid < n_exp) load_expert(wid, cur);
   for (int e = wid; e < n_exp; e += 8) {
     if (e + 8 < n_exp) load_expert(e + 8, nxt);
@@ -228,7 +231,7 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
     for (int w = 0; w < 8; ++w) v += part[w][my_t][my_r];
     const float ov = o_prev + v;
     a.out[(size_t)my_t * H + r0 + my_r] = ov;
-    if (a.x_res)  // stack residual on the final value of out
+    if (res)  // stack residual on the final value of out
       a.x_res[(size_t)my_t * H + r0 + my_r] = f32_to_bf16_rne(__uint_as_float((uint32_t)x_prev << 16) + ov);
   }
 }

@@ -211,7 +211,7 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
   __shared__ uint4 xs[kWave * NJ * CV1 * sizeof(XT) / 16];
   __shared__ float red[4];
   const int nx16 = H * (int)sizeof(XT) / 16;  // 16-byte chunks of one activation row
-  if (a.n_dev && by >= *a.n_dev) return;  // device-resolved count: uniform per block
+  if (a.n_dev && by >= *a.n_dev - a.o_lo) return;  // device-resolved count: uniform per block
   const int o = a.o_lo + by;
   const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
   const RecLayout L = rec_layout(F, H, I);

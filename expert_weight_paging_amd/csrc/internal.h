@@ -142,12 +142,13 @@ hipError_t launch_route_plan_page_in(const float* logits, int T, int E, int k, i
                                      long long* dstats, unsigned long long* ticket, const uint8_t* host_store_dev,
                                      uint8_t* slots, size_t stride, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                                      size_t cp_len = ~(size_t)0);
-// Device-resolved page-in of a single-wave plan: copies the records of wave
-// order positions [counts[1], counts[0]) (the misses) from the device-mapped
-// host store into their slots.
+// Device-resolved page-in of wave `wave` of a plan: copies the records of the
+// misses among wave order positions [wave * K, (wave + 1) * K), i.e. positions
+// max(counts[1], wave * K) .. min(counts[0], (wave + 1) * K) - 1, from the
+// device-mapped host store into their slots (none for a wave past the step's).
 hipError_t launch_page_in_device(const uint8_t* host_store_dev, uint8_t* slots, size_t stride,
                                  const PlanDev& dev, int E, int K, hipStream_t s, hipEvent_t ev0,
-                                 hipEvent_t ev1);
+                                 hipEvent_t ev1, int wave = 0);
 
 struct FfnArgs {
   int fmt, E, k, H, I, K;
@@ -168,10 +169,13 @@ struct FfnArgs {
   uint16_t* hb_lo;     // GEMM scratch bf16 [T*k][I], low part of h
   float* y;            // GEMM scratch fp32 [T*k][H]
   int max_rows;        // upper bound on pairs of one expert in this wave (GEMM)
-  const int32_t* n_dev; // optional (device-resolved steps): the number of experts,
-                       // read on the device; n_exp is then only an upper bound
+  const int32_t* n_dev; // optional (device-resolved steps): the step's number of distinct
+                       // experts D, read on the device; the launch then covers wave-order
+                       // positions o_lo .. min(o_lo + n_exp, D) - 1 (none if D <= o_lo)
   uint16_t* x_res;     // optional: the launch that completes out also applies the
                        // stack residual x_res = bf16_rne(x_res + out), bf16 [T][H]
+  int res_last;        // with x_res and n_dev: only the launch that holds the step's last
+                       // expert (o_lo < D <= o_lo + n_exp) applies it
   int norm;            // GEMV path, bf16 activations: the up kernel applies the unit-gain
                        // RMSNorm to each staged activation row (a stack layer's input)
   // optional (GEMM path, quantised formats): the wave's records dequantised to

@@ -33,9 +33,12 @@ __global__ __launch_bounds__(kCopyThreads) void page_in_kernel(const uint8_t* __
                                                                const int32_t* __restrict__ order_expert,
                                                                const int32_t* __restrict__ order_slot,
                                                                const int32_t* __restrict__ counts, int E,
-                                                               int K) {
+                                                               int K, int wave) {
+  // the misses of this wave, in wave order: positions wave * K .. of the
+  // order that come after the hits (all hits are in wave 0)
   const int D = counts[0], nH = counts[1];
-  for (int m = nH; m < D; ++m) {  // the misses of the single wave, in wave order
+  const int m0 = max(nH, wave * K), m1 = min(D, (wave + 1) * K);
+  for (int m = m0; m < m1; ++m) {
     const int e = order_expert[m], s = order_slot[m];
     if (e < 0 || e >= E || s < 0 || s >= K) continue;  // never produced by the plan
     copy_record_share<kCopyThreads, kCopyUnroll>(host + (size_t)e * stride, slots + (size_t)s * stride, stride,
@@ -47,10 +50,10 @@ __global__ __launch_bounds__(kCopyThreads) void page_in_kernel(const uint8_t* __
 
 hipError_t launch_page_in_device(const uint8_t* host_store_dev, uint8_t* slots, size_t stride,
                                  const PlanDev& dev, int E, int K, hipStream_t s, hipEvent_t ev0,
-                                 hipEvent_t ev1) {
+                                 hipEvent_t ev1, int wave) {
   launch_k(page_in_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), s, ev0, ev1, host_store_dev, slots,
            stride, (const int32_t*)dev.order_expert, (const int32_t*)dev.order_slot,
-           (const int32_t*)dev.counts, E, K);
+           (const int32_t*)dev.counts, E, K, wave);
   return hipGetLastError();
 }
 

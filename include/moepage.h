@@ -310,21 +310,25 @@ moe_status moe_stack_forward(moe_layer* const* layers, moe_plan* const* plans, i
                              const float* logits, int32_t num_tokens, void* x, float* out,
                              int32_t lookahead);
 
-/* Device-resolved step: the graph-capturable single-wave path ([PE] "What
- * happens with more than one request?": a step whose experts fit in the slots
- * is one wave, the case a graph can capture). Routes the T tokens, plans the
- * step, pages the misses in and runs the experts, all on the layer's compute
- * stream, with the plan kept on the device: the miss list is read by a copy
- * kernel from device memory and the records are read from the host store
- * through its device mapping, so there is no host synchronisation and no
- * allocation, and the call may be captured in a HIP graph (timers are skipped
- * while the stream captures).
+/* Device-resolved step: the graph-capturable path ([PE] "What happens with
+ * more than one request?": a step whose experts fit in the slots is one wave,
+ * the case a graph can capture; a larger step runs several waves, each paging
+ * in its misses before it computes). Routes the T tokens, plans the step,
+ * pages the misses in and runs the experts, all on the layer's compute stream,
+ * with the plan kept on the device: the miss list is read by a copy kernel
+ * from device memory and the records are read from the host store through its
+ * device mapping, so there is no host synchronisation and no allocation, and
+ * the call may be captured in a HIP graph (timers are skipped while the
+ * stream captures). When T * top_k > K the step may need several waves: one
+ * launch plans them all, then for each wave the step may have (up to
+ * ceil(min(T * top_k, E) / K)) a page-in launch and the FFN launches follow
+ * in order; launches for waves the step turns out not to have find no work.
  *   logits: device float32 [T][E]; x: device bf16 [T][H] (fp32 for the f32
  *           format); out: device float32 [T][H], overwritten (16-byte aligned)
  *   x_res:  NULL, or device bf16 [T][H] that receives bf16_rne(x_res + out)
  *           (the stack residual; may alias x)
- * Requirements: 1 <= T <= min(max_tokens, MOE_MAX_GEMV_TOKENS) and
- * T * top_k <= K, so the step is always one wave; a host store that is mapped
+ * Requirements: 1 <= T <= min(max_tokens, MOE_MAX_GEMV_TOKENS), at most 16
+ * possible waves (ceil(min(T * top_k, E) / K) <= 16); a host store that is mapped
  * into the device (moe_host_alloc memory is); no unfinished host-driven step
  * of the layer. Results (plan arrays, table state, out) are the same as a
  * host-driven step; the plan's host view is not updated (moe_plan_get_info
@@ -350,7 +354,7 @@ moe_status moe_step_device(moe_layer* layer, moe_plan* plan, const float* logits
  * the same kernels as moe_step_device, so out, the table state and the
  * counters are the same.
  *   logits, x, out, x_res: as moe_step_device
- * Requirements: as moe_step_device, and a workspace of
+ * Requirements: as moe_step_device with T * top_k <= K (one wave), and a workspace of
  * 11 arrays (4 * T * top_k or 4 * E bytes each, 256-byte aligned) plus
  * 4 * T * top_k * I bytes of h within MOE_STATIC_WORKSPACE_BYTES
  * (MOE_ERR_INVALID_ARG beyond it). Every call on one GPU shares that GPU's

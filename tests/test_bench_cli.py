@@ -38,8 +38,9 @@ def test_default_mode_follows_the_one_wave_condition():
         return a.device, a.graph
     assert mode("decode-bf16") == (True, False)              # 1 x 8 <= 40
     assert mode("decode-fp8", batch=5) == (True, False)      # 5 x 8 <= 40
-    assert mode("decode-fp8", batch=6) == (False, False)     # 48 > 40: host-driven waves
-    assert mode("decode-fp8", batch=4, slots=24) == (False, False)
+    assert mode("decode-fp8", batch=6) == (True, False)      # 48 > 40: two device-resolved waves
+    assert mode("decode-fp8", batch=4, slots=24) == (True, False)
+    assert mode("decode-fp8", batch=8, slots=3) == (False, False)  # 22 possible waves of 3: host-driven
     assert mode("decode-bf16", host=True) == (False, False)
     assert mode("stack-int4") == (False, True)
     assert mode("stack-int4", lookahead=True) == (False, False)
@@ -94,3 +95,18 @@ def test_prefill_roofline_takes_the_binding_roof():
             assert abs(r["achieved"] - gbps) < 0.2 and abs(r["mfma_TFLOPs"] - tflops) < 0.2
         else:
             assert abs(r["achieved"] - tflops) < 0.2 and r["unit"] == "TFLOP/s"
+
+
+def test_expert_ffn_bytes_match_the_record_layouts():
+    """The per-expert bytes the decode roofline counts are the record's
+    sections: W13 plus its tables for the up launch, W_d plus its tables for
+    the down launch; together they are the record's payload."""
+    b = _bench_module()
+    import expert_weight_paging_amd as ewp
+    H, I = 2048, 768
+    for fmt in range(5):
+        up, dn = b.expert_ffn_bytes(fmt, H, I)
+        rec = ewp.record_bytes(fmt, H, I)
+        assert up + dn <= rec < up + dn + 256, fmt  # the stride pads the payload to 256 bytes
+    assert b.expert_ffn_bytes(1, H, I) == (6291456, 3145728)
+    assert b.expert_ffn_bytes(3, H, I) == (1671168, 835584)

@@ -1,7 +1,8 @@
-"""GPU parity of the device-resolved single-wave path (moe_step_device and
+"""GPU parity of the device-resolved path (moe_step_device and
 moe_stack_forward_device: route, slot plan, kernel page-in and FFN with no host
-synchronisation) against the oracle, its interleaving with host-driven steps,
-and its HIP-graph capture against eager runs, all through the C ABI."""
+synchronisation; one wave, or several when T * top_k > K) against the oracle,
+its interleaving with host-driven steps, and its HIP-graph capture against
+eager runs, all through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -29,7 +30,6 @@ def _dev(a):
 
 
 def _check_device_plan(p, ids_ref, w_ref, p_ref):
-    assert p_ref.n_waves == 1
     ids, wts, sid, wof = p.plan.read()
     assert np.array_equal(ids, ids_ref), (ids, ids_ref)
     assert np.array_equal(sid, p_ref.slot_ids)
@@ -184,12 +184,34 @@ def test_int4_device_steps_interleaved_with_host_steps():
     p.close()
 
 
-def test_device_step_rejects_multi_wave_batches():
+@pytest.mark.parametrize("cid,B,K,steps", [(3, 6, 40, 32), (3, 8, 40, 32), (1, 5, 4, 16), (2, 1, 4, 12),
+                                           (3, 8, 24, 16)])
+def test_multi_wave_device_steps(cid, B, K, steps):
+    """Batches whose routed experts can exceed K ([PE] "What happens with more
+    than one request?"): device-resolved expert waves, each wave's misses paged
+    in before its experts run; every step's plan (ids, weights, slot and wave of
+    each pair), the table state and sampled outputs against the oracle, with
+    every fifth step host-driven. Covers B * top_k just past K (B = 6), well
+    past it (B = 8, K = 24: up to three waves), one token with K < top_k, and
+    the tiny f32 layer (up to three waves of four)."""
+    cfg = W.CONFIGS[cid]
+    say("case: multi-wave device steps, %s B=%d K=%d, %d steps" % (cfg.name, B, K, steps))
+    p = _layer(cfg, B, K=K)
+    logits, x = gen.decode_inputs(cfg, B, steps=steps)
+    worst, hits, misses = _run_device(p, logits, x, sample=lambda t: t % 4 == 0 or t == steps - 1,
+                                      host_every=5)
+    st = p.gpu.stats()
+    say("worst rel err %.3g hits %d misses %d waves %d" % (worst, hits, misses, st["waves"]))
+    assert st["hits"] == hits and st["misses"] == misses and st["waves"] > steps
+    p.close()
+
+
+def test_device_step_rejects_too_many_waves():
     cfg = W.CONFIGS[3]
-    say("case: device step with B * top_k > K is rejected")
-    p = _layer(cfg, 6)
-    logits, x = gen.decode_inputs(cfg, 6, steps=1)
-    out = torch.empty(6, cfg.H, dtype=torch.float32, device="cuda")
+    say("case: device step that may need more than 16 waves is rejected")
+    p = _layer(cfg, 9, K=4)  # min(9 * 8, 128) / 4 = 18 possible waves
+    logits, x = gen.decode_inputs(cfg, 9, steps=1)
+    out = torch.empty(9, cfg.H, dtype=torch.float32, device="cuda")
     with pytest.raises(ewp.MoeError) as ei:
         p.gpu.step_device(p.plan, _dev(logits[0]), _dev(x[0]), out)
     assert ei.value.status == -1  # MOE_ERR_INVALID_ARG
@@ -304,14 +326,16 @@ def test_int4_stack_device_lookahead_graph_replays_match_eager():
     _close_stack(B[0], B[1], B[2])
 
 
-def test_bf16_device_step_graph_replays_match_eager():
+@pytest.mark.parametrize("cid,B", [(2, 1), (3, 6)], ids=["bf16-one-wave", "fp8-B6-waves"])
+def test_device_step_graph_replays_match_eager(cid, B):
     """One device-resolved step captured in a HIP graph, replayed for 10
     decode steps with eager input copies and synchronisations between the
     replays; every replay's output, plan and table state must equal an eager
-    twin layer's bit for bit."""
-    cfg = W.CONFIGS[2]
+    twin layer's bit for bit. At B = 6 (48 pairs, K = 40) the graph holds the
+    launches of two possible waves."""
+    cfg = W.CONFIGS[cid]
     steps = 10
-    say("case: bf16 device step captured in a graph, %d replays vs eager" % steps)
+    say("case: %s device step at B=%d captured in a graph, %d replays vs eager" % (cfg.name, B, steps))
     rec = ewp.record_bytes(cfg.fmt, cfg.H, cfg.I)
     host = ewp.HostStore(cfg.E, rec)
     gen.expert_store(cfg, out=host.array)
@@ -322,14 +346,14 @@ def test_bf16_device_step_graph_replays_match_eager():
         slots, state = ewp.alloc_layer_buffers(cfg.E, cfg.K, rec, "cuda")
         L = ewp.Layer(cfg.E, cfg.top_k, cfg.H, cfg.I, cfg.K, cfg.fmt, host, slots, state, s,
                       torch.cuda.Stream(), s)
-        mk.append((L, ewp.Plan(L, 1), slots, state))
+        mk.append((L, ewp.Plan(L, B), slots, state))
     (La, Pa, _, _), (Lb, Pb, _, _) = mk
-    logits, x = gen.decode_inputs(cfg, 1, steps=steps)
+    logits, x = gen.decode_inputs(cfg, B, steps=steps)
     lg, xd = _dev(logits), _dev(x)
-    lg_buf = torch.zeros(1, cfg.E, dtype=torch.float32, device="cuda")
-    x_buf = torch.zeros(1, cfg.H, dtype=torch.int16, device="cuda")
-    out_b = torch.zeros(1, cfg.H, dtype=torch.float32, device="cuda")
-    out_a = torch.zeros(1, cfg.H, dtype=torch.float32, device="cuda")
+    lg_buf = torch.zeros(B, cfg.E, dtype=torch.float32, device="cuda")
+    x_buf = torch.zeros(B, cfg.H, dtype=torch.int16, device="cuda")
+    out_b = torch.zeros(B, cfg.H, dtype=torch.float32, device="cuda")
+    out_a = torch.zeros(B, cfg.H, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s_cap):
