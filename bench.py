@@ -182,6 +182,31 @@ def measured_peaks(torch, dev):
     return {"hbm_copy_read_plus_write_GBps": round(hbm, 1), "h2d_pinned_GBps": round(h2d, 2)}
 
 
+def one_launch_read_reference(torch, dev, roof):
+    """The FFN launches against a plain one-launch streaming read of the same
+    bytes (moe_read_probe: every load issued up front, nothing computed or
+    stored), timed by the same dispatch-stamped events, each launch reading
+    memory the previous ones did not (a 2 GiB buffer, eight times the
+    last-level cache): what one launch of that many cold bytes takes on this
+    box, fixed costs included. ratio = the kernels' time over the reads'."""
+    import expert_weight_paging_amd as ewp
+    buf = torch.zeros(2 << 30, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    out, k_us, r_us = {}, 0.0, 0.0
+    for name, v in roof["kernels"].items():
+        nb = int(v["algorithmic_bytes_per_launch"]) // 16 * 16
+        us = ewp.read_probe(buf, nb, stream=torch.cuda.current_stream())
+        out[name] = {"bytes": nb, "read_us": round(us, 3), "kernel_us": v["avg_launch_us"],
+                     "ratio": round(v["avg_launch_us"] / us, 3)}
+        k_us += v["avg_launch_us"]
+        r_us += us
+    pair = sum(v["bytes"] for v in out.values())
+    out["pair_as_one_read_us"] = round(ewp.read_probe(buf, pair // 16 * 16, stream=torch.cuda.current_stream()), 3)
+    out["pair_ratio"] = round(k_us / r_us, 3)
+    del buf
+    return out
+
+
 def oracle_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -903,6 +928,8 @@ def main():
         "waves_per_layer_step": round(st["waves"] / max(st["steps"], 1), 4),
         "measured_peaks": peaks,
     }
+    if peaks is not None and line["roofline"] and "kernels" in line["roofline"]:
+        line["roofline"]["one_launch_read"] = one_launch_read_reference(torch, dev, line["roofline"])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (budget %.0f s)" % args.cpu_budget)
         line["cpu_baseline"] = res["cpu"](args.cpu_budget)

@@ -106,6 +106,8 @@ EXPORTS = {
     "moe_stack_forward_device": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
+    "moe_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t,
+                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]),
     "moe_host_alloc": (ctypes.c_void_p, [ctypes.c_size_t]),
     "moe_host_free": (None, [ctypes.c_void_p]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -368,6 +370,16 @@ def timing_floor(stream=None, reps=100):
     the per-launch floor included in every timing_read figure."""
     us = ctypes.c_double()
     _check(lib().moe_timing_floor(_stream(stream), int(reps), ctypes.byref(us)))
+    return us.value
+
+
+def read_probe(buf, nbytes, stream=None, reps=40):
+    """Median microseconds of one launch that plainly streams `nbytes` bytes of
+    the device buffer `buf` (a torch uint8 tensor), each launch reading a part
+    the previous ones did not: the reference for the FFN launches' times."""
+    us = ctypes.c_double()
+    _check(lib().moe_read_probe(_stream(stream), _ptr(buf), buf.numel(), int(nbytes), int(reps),
+                                ctypes.byref(us)))
     return us.value
 
 

@@ -302,6 +302,24 @@ moe_status self_check(moe_layer* L);
 namespace {
 // Does nothing: its timed duration is the floor of every timed launch.
 __global__ void empty_kernel() {}
+
+// A plain streaming read for moe_read_probe: every thread loads its four
+// 16-byte chunks up front (consecutive threads read consecutive chunks), then
+// folds them; nothing is stored unless the fold hits a sentinel value.
+__global__ __launch_bounds__(512) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+                                                         uint32_t* sink) {
+  const size_t base = (size_t)blockIdx.x * 2048 + threadIdx.x;
+  uint4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t i = base + (size_t)u * 512;
+    v[u] = i < n16 ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  if (s == 0x9E3779B9u) sink[0] = s;
+}
 }  // namespace
 
 extern "C" {
@@ -1344,6 +1362,49 @@ moe_status moe_timing_read(moe_layer* L, moe_timing* out) {
   *out = L->acc;
   std::memset(&L->acc, 0, sizeof(L->acc));
   return MOE_OK;
+}
+
+moe_status moe_read_probe(void* stream, void* buf, size_t buf_bytes, size_t bytes, int32_t reps,
+                          double* us) {
+  if (!us || !buf) return fail(MOE_ERR_INVALID_ARG, "null buffer or output");
+  if (reps < 1 || reps > 10000) return fail(MOE_ERR_INVALID_ARG, "reps must be in 1..10000");
+  if (bytes < 16 || bytes % 16 || ((uintptr_t)buf & 255) || buf_bytes < 2 * bytes)
+    return fail(MOE_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and at most half of a "
+                                     "256-byte aligned buffer");
+  const size_t n16 = bytes / 16;
+  const size_t nwg = (n16 + 2047) / 2048;
+  if (nwg > 0x7FFFFFFFu) return fail(MOE_ERR_INVALID_ARG, "read too large");
+  // each launch starts one read's length plus 64 MB further on (wrapping), so
+  // what it reads was not read by the launches just before
+  const size_t hop = (bytes + 255) / 256 * 256 + ((size_t)64 << 20);
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t a = nullptr, b = nullptr;
+  moe_status st = MOE_OK;
+  std::vector<double> t;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    st = fail(MOE_ERR_HIP, "event creation failed");
+  } else {
+    size_t off = 0;
+    for (int r = 0; r <= reps && !st; ++r) {  // launch 0 warms up, untimed
+      if (off + bytes > buf_bytes) off = 0;
+      hipExtLaunchKernelGGL(read_probe_kernel, dim3((unsigned)nwg), dim3(512), 0, s, a, b, 0,
+                            (const uint4*)((const uint8_t*)buf + off), n16, (uint32_t*)buf);
+      off += hop;
+      float ms = 0.f;
+      if (hipGetLastError() != hipSuccess || hipEventSynchronize(b) != hipSuccess ||
+          hipEventElapsedTime(&ms, a, b) != hipSuccess)
+        st = fail(MOE_ERR_HIP, "read-probe timing failed");
+      else if (r > 0)
+        t.push_back(ms * 1e3);
+    }
+    if (!st) {
+      std::sort(t.begin(), t.end());
+      *us = t[t.size() / 2];
+    }
+  }
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  return st;
 }
 
 moe_status moe_timing_floor(void* stream, int32_t reps, double* us) {

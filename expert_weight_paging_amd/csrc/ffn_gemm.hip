@@ -143,14 +143,24 @@ __device__ inline int src_chunk(int p) {
 // assembly so that the compiler neither waits for it before every LDS read nor
 // counts it: the pipeline below does its own waiting on the vector-memory
 // counter. M0 is saved and restored around the copy (the compiler reserves it).
+// NT: a streaming (non-temporal) read, for weights that are read once.
+template <bool NT = false>
 __device__ inline void dma16(const void* src, uint32_t lds) {
   uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(src), "s"(lds)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(src), "s"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(src), "s"(lds)
+        : "memory");
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
@@ -229,6 +239,13 @@ __device__ inline int frag_row(int n, int wn, int lane) {
   return UP ? ((n < 2 ? 0 : UP_HCOLS) + wn * 32 + (n & 1) * 16 + (lane & 15)) : (wn * 64 + n * 16 + (lane & 15));
 }
 
+// Weight copies as streaming reads: measured on the all-resident 2048-token
+// layer, they shorten the bf16 up GEMM (180 -> 170 us) but lengthen the down
+// GEMM (173 -> 197 us) and every quantised format's GEMMs, so only the bf16
+// up GEMM takes them.
+template <bool UP, int WF>
+constexpr bool kNtWeights = UP && WF == MOE_FMT_BF16;
+
 // One pass over rows [mb, mb + mcnt) of expert position o, mcnt <= 64 * RG.
 // Copies are issued per k-step as [activation stage it + SA - 1][weight stage
 // it + SW - 1]; since SW > SA, the activation copy of a stage is issued after
@@ -289,7 +306,7 @@ __device__ void gemm_pass(const FfnArgs& a, uint4* smem, const uint8_t* const (&
     if (s < 0 || s >= nit) return;
     const uint32_t st = ldsw + (s % SW) * R::W_CH * 16;
 #pragma unroll
-    for (int i = 0; i < nW; ++i) dma16(wsrc[i] + (size_t)s * BK * WBITS / 8, st + (i * kThreads) * 16);
+    for (int i = 0; i < nW; ++i) dma16<kNtWeights<UP, WF>>(wsrc[i] + (size_t)s * BK * WBITS / 8, st + (i * kThreads) * 16);
   };
 
   constexpr int MT = RG * 2;  // 16-row sub-tiles per wavefront

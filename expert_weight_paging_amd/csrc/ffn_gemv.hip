@@ -37,13 +37,13 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FfnArgs a) {
 template <int F>
 __device__ inline void load_w2(const uint8_t* p, uint32_t* w) {
   if constexpr (Fmt<F>::CB2 == 16) {
-    const uint4 v = *(const uint4*)p;
+    const uint4 v = nt_load16(p);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (Fmt<F>::CB2 == 8) {
-    const uint2 v = *(const uint2*)p;
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
     w[0] = v.x; w[1] = v.y;
   } else {
-    w[0] = *(const uint32_t*)p;
+    w[0] = __builtin_nontemporal_load((const uint32_t*)p);
   }
 }
 

@@ -21,6 +21,15 @@ __device__ inline uint16_t f32_to_bf16_rne(float v) {
 }
 
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// 16 bytes of weights read once per step: a streaming load, so the L2 keeps
+// the small tables the next launch reads (slot map, h)
+__device__ inline uint4 nt_load16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -227,8 +236,8 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
     for (int j = 0; j < NJ; ++j) {
       const int c = lane + kWave * j;
       if (c < nch) {
-        wg[r][j] = *(const uint4*)(w13 + (size_t)i * row_bytes + (size_t)c * 16);
-        wu[r][j] = *(const uint4*)(w13 + (size_t)(I + i) * row_bytes + (size_t)c * 16);
+        wg[r][j] = nt_load16(w13 + (size_t)i * row_bytes + (size_t)c * 16);
+        wu[r][j] = nt_load16(w13 + (size_t)(I + i) * row_bytes + (size_t)c * 16);
       } else {
         wg[r][j] = make_uint4(0, 0, 0, 0);
         wu[r][j] = make_uint4(0, 0, 0, 0);

@@ -471,6 +471,20 @@ moe_status moe_timing_read(moe_layer* layer, moe_timing* out);
  * range, MOE_ERR_HIP if a launch or event call fails. */
 moe_status moe_timing_floor(void* stream, int32_t reps, double* us);
 
+/* Reference for the FFN launches' durations: the median duration, by the same
+ * dispatch-stamped events, of one launch of a plain streaming read of `bytes`
+ * bytes (16 per lane, every load issued before any is used, nothing stored),
+ * over `reps` (1..10000) launches on `stream`, each reading a different part
+ * of the caller's device buffer `buf` of buf_bytes (each launch starts the
+ * read's length plus 64 MB past the previous one, wrapping): with buf_bytes
+ * several times the 256 MB last-level cache every read comes from HBM, as in
+ * the caches-cold decode pass. bytes: a positive multiple of 16, at most
+ * buf_bytes / 2; buf 256-byte aligned; its first 4 bytes may be overwritten.
+ * Synchronous; *us receives microseconds. MOE_ERR_INVALID_ARG for bad sizes
+ * or pointers, MOE_ERR_HIP if a launch or event call fails. */
+moe_status moe_read_probe(void* stream, void* buf, size_t buf_bytes, size_t bytes, int32_t reps,
+                          double* us);
+
 /* Page-locked host memory for expert stores (hipHostMalloc), and its release. */
 void* moe_host_alloc(size_t bytes);
 void moe_host_free(void* p);

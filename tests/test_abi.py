@@ -143,3 +143,16 @@ def test_null_handles_are_refused_without_a_gpu():
     assert b"null" in L.moe_last_error()
     assert L.moe_rmsnorm_bf16(None, None, 1, 2048, None) == -1        # null rows
     assert L.moe_rmsnorm_bf16(None, None, 0, 2044, None) == -1        # H not a multiple of 8
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_read_probe_refuses_bad_arguments():
+    """The measurement helper validates before any launch (no GPU needed)."""
+    lib = ctypes.CDLL(LIB)
+    lib.moe_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t,
+                                   ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
+    us = ctypes.c_double()
+    assert lib.moe_read_probe(None, None, 1 << 20, 4096, 10, ctypes.byref(us)) == -1
+    assert lib.moe_read_probe(None, ctypes.c_void_p(256), 1 << 20, 100, 10, ctypes.byref(us)) == -1  # not 16-aligned size
+    assert lib.moe_read_probe(None, ctypes.c_void_p(256), 4096, 4096, 10, ctypes.byref(us)) == -1     # over half the buffer
+    assert lib.moe_read_probe(None, ctypes.c_void_p(256), 1 << 20, 4096, 0, ctypes.byref(us)) == -1   # reps
