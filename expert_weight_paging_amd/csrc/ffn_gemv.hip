@@ -93,8 +93,8 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
 #pragma unroll
   for (int r = 0; r < RW; ++r) acc[r] = 0.f;
   uint32_t cur[RW][NJ][NW], nxt[RW][NJ][NW];
-  auto load_expert = [&](int e, uint32_t (&dst)[RW][NJ][NW]) {
-    const uint8_t* wd = a.slots + (size_t)a.order_slot[a.o_lo + e] * a.stride + L.wd;
+  auto load_expert = [&](int slot, uint32_t (&dst)[RW][NJ][NW]) {
+    const uint8_t* wd = a.slots + (size_t)slot * a.stride + L.wd;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int row = min(r0 + r, H - 1);
@@ -115,21 +115,30 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
   const int T = a.T;
   const int my_t = threadIdx.x / RW, my_r = threadIdx.x % RW;
   const bool mine = (int)threadIdx.x < T * RW && r0 + my_r < H;
+  // The slot of this wavefront's first expert is read with the step's expert
+  // count (one round trip ahead of the weight loads instead of two); the
+  // position is clamped into the array and the value is used only when the
+  // expert exists.
+  int slot_cur = a.order_slot[min(a.o_lo + wid, a.E - 1)];
   // device-resolved steps: the step's distinct experts D, read on the device
   const int D = a.n_dev ? *a.n_dev : a.o_lo + a.n_exp;
   const bool res = a.x_res && (!a.res_last || (a.o_lo < D && D <= a.o_lo + a.n_exp));
   float o_prev = 0.f;
-  uint16_t x_prev = 0;
+  uint32_t x_prev = 0;
   if (mine) {
     if (a.accumulate) o_prev = a.out[(size_t)my_t * H + r0 + my_r];
     if (res) x_prev = a.x_res[(size_t)my_t * H + r0 + my_r];
   }
   const int n_exp = min(a.n_exp, D - a.o_lo);  // none past the step's last expert
-  if (wid < n_exp) load_expert(wid, cur);
+  if (wid < n_exp) load_expert(slot_cur, cur);
   for (int e = wid; e < n_exp; e += 8) {
-    if (e + 8 < n_exp) load_expert(e + 8, nxt);
+    int slot_nxt = 0;
+    if (e + 8 < n_exp) {
+      slot_nxt = a.order_slot[a.o_lo + e + 8];
+      load_expert(slot_nxt, nxt);
+    }
     const int o = a.o_lo + e;
-    const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
+    const uint8_t* rec = a.slots + (size_t)slot_cur * a.stride;
     float sc[RW][NJ], zc[RW][NJ];
     if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
       const float* sd = (const float*)(rec + L.sd);
@@ -220,6 +229,7 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int n = 0; n < NW; ++n) cur[r][j][n] = nxt[r][j][n];
+      slot_cur = slot_nxt;
     }
   }
 #pragma unroll
@@ -231,8 +241,14 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
     for (int w = 0; w < 8; ++w) v += part[w][my_t][my_r];
     const float ov = o_prev + v;
     a.out[(size_t)my_t * H + r0 + my_r] = ov;
-    if (res)  // stack residual on the final value of out
-      a.x_res[(size_t)my_t * H + r0 + my_r] = f32_to_bf16_rne(__uint_as_float((uint32_t)x_prev << 16) + ov);
+    if (res) {  // stack residual on the final value of out
+      // x_prev passes through an empty asm here, at its use, so that the
+      // compiler cannot widen it next to its load, which would make this
+      // wavefront wait for that load before it issues its weight loads
+      uint32_t xp = x_prev;
+      asm volatile("" : "+v"(xp));
+      a.x_res[(size_t)my_t * H + r0 + my_r] = f32_to_bf16_rne(__uint_as_float(xp << 16) + ov);
+    }
   }
 }
 

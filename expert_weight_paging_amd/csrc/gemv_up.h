@@ -220,9 +220,14 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
   __shared__ uint4 xs[kWave * NJ * CV1 * sizeof(XT) / 16];
   __shared__ float red[4];
   const int nx16 = H * (int)sizeof(XT) / 16;  // 16-byte chunks of one activation row
-  if (a.n_dev && by >= *a.n_dev - a.o_lo) return;  // device-resolved count: uniform per block
   const int o = a.o_lo + by;
-  const uint8_t* rec = a.slots + (size_t)a.order_slot[o] * a.stride;
+  // The expert's slot is read before the device-resolved count is tested, so
+  // the two reads share one round trip ahead of the weight loads; the
+  // position is clamped into the array, and the value is used only when the
+  // expert exists.
+  const int slot = a.order_slot[min(o, a.E - 1)];
+  if (a.n_dev && by >= *a.n_dev - a.o_lo) return;  // device-resolved count: uniform per block
+  const uint8_t* rec = a.slots + (size_t)slot * a.stride;
   const RecLayout L = rec_layout(F, H, I);
   const int nch = H / CV1;
   const size_t row_bytes = (size_t)H * fmt_elem_bits(F) / 8;
