@@ -221,12 +221,16 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
   __shared__ float red[4];
   const int nx16 = H * (int)sizeof(XT) / 16;  // 16-byte chunks of one activation row
   const int o = a.o_lo + by;
-  // The expert's slot is read before the device-resolved count is tested, so
-  // the two reads share one round trip ahead of the weight loads; the
-  // position is clamped into the array, and the value is used only when the
-  // expert exists.
-  const int slot = a.order_slot[min(o, a.E - 1)];
-  if (a.n_dev && by >= *a.n_dev - a.o_lo) return;  // device-resolved count: uniform per block
+  // The expert's slot and the device-resolved expert count are both read
+  // before either is used, so they share one round trip ahead of the weight
+  // loads (the empty asm keeps the compiler from moving the slot's read below
+  // the count's test). The slot's position is clamped into the array and its
+  // value used only when the expert exists; without a device count the read
+  // goes to the slot map and is ignored.
+  int slot = a.order_slot[min(o, a.E - 1)];
+  int nd = *(a.n_dev ? a.n_dev : a.order_slot);
+  asm volatile("" : "+s"(slot), "+s"(nd));
+  if (a.n_dev && by >= nd - a.o_lo) return;  // device-resolved count: uniform per block
   const uint8_t* rec = a.slots + (size_t)slot * a.stride;
   const RecLayout L = rec_layout(F, H, I);
   const int nch = H / CV1;
