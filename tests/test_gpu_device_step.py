@@ -379,3 +379,37 @@ def test_device_step_graph_replays_match_eager(cid, B):
         P.close()
         L.close()
     host.free()
+
+
+def test_multi_wave_device_step_applies_the_residual_once():
+    """x_res on a device step that may need two waves (B = 6, 48 pairs, K = 40):
+    the residual is applied exactly once, by the launch holding the step's
+    last expert, to the final out: x_res == bf16_rne(x + out) computed in fp32
+    from the GPU's own out, bit for bit; out itself within the oracle's
+    tolerance. Steps with one and with two actual waves both occur."""
+    cfg = W.CONFIGS[3]
+    B, steps = 6, 12
+    say("case: multi-wave device steps with the stack residual, fp8 B=%d K=40, %d steps" % (B, steps))
+    p = _layer(cfg, B)
+    logits, x = gen.decode_inputs(cfg, B, steps=steps)
+    lg, xd = _dev(logits), _dev(x)
+    out = torch.empty(B, cfg.H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    waves_seen = set()
+    for t in range(steps):
+        xr = xd[t].clone()
+        w0 = p.gpu.stats()["waves"]
+        p.gpu.step_device(p.plan, lg[t], xd[t], out, x_res=xr)
+        torch.cuda.synchronize()
+        waves_seen.add(p.gpu.stats()["waves"] - w0)
+        o = out.cpu().numpy()
+        xs = gen.bf16_bits_to_f32(x[t]).astype(np.float32)
+        want = gen.f32_to_bf16_bits(xs + o)
+        assert np.array_equal(xr.cpu().numpy().view(np.uint16), want), t
+        o_ref, ids_ref, w_ref, p_ref = p.ref.step(logits[t], x_values(x[t], p.fmt))
+        _check_device_plan(p, ids_ref, w_ref, p_ref)
+        assert rel_err(o, o_ref) <= TOL[p.fmt], t
+    say("waves per step seen: %s" % sorted(waves_seen))
+    assert waves_seen == {1, 2}
+    p.check_state()
+    p.close()
