@@ -74,16 +74,37 @@ __device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
 }
 
 // Down projection: a workgroup of 8 wavefronts owns RW output rows;
-// wavefront w takes experts w, w+8, ... of the wave (the next one's rows
-// prefetched while the current ones are used), keeps the per-token sums in
-// lane t, and the eight partial sums are added in LDS in wavefront order
+// wavefront w takes experts w, w+8, ... of the wave, keeps the per-token sums
+// in lane t, and the eight partial sums are added in LDS in wavefront order
 // (fixed, so the result is bitwise reproducible).
+// Loads are arranged so that an expert costs no dependent round trip of its
+// own: each wavefront first reads the slot and the CSR pair range of all of
+// its experts (one per lane) in one round trip, and (MULTI: launches of more
+// than 8 experts, several per wavefront) while it computes one expert it has
+// the next one's rows, scales, first pair's h, token and router weight in
+// flight. An expert's second and later pairs are read when they are reached
+// (decode batches rarely have them).
 template <int F, int NJ, int RW>
+struct DownStage {
+  uint32_t w[RW][NJ][Fmt<F>::CB2 / 4];  // the expert's RW rows of W_d, chunk lane + 64 j
+  // scales of chunk lane + 64 j, kept as stored: FP8, the fp32 block scale
+  // (row 0's entry: the RW rows share a 128-row block); int4, the fp16 scale
+  // (low half) and zero point (high half) of row r's group; MXFP4, row r's
+  // E8M0 byte
+  uint32_t sc[RW][NJ];
+  float hv[NJ][Fmt<F>::CV2];            // h of the pair being computed (first: the expert's first)
+  int t;                                // that pair's token
+  float wq;                             // and its router weight
+};
+
+template <int F, int NJ, int RW, bool MULTI>
 __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
   constexpr int CB2 = Fmt<F>::CB2, CV2 = Fmt<F>::CV2, NW = CB2 / 4;
+  static_assert(128 % RW == 0, "a workgroup's rows lie in one 128-row block");
+  using Stage = DownStage<F, NJ, RW>;
   __shared__ float part[8][kWave][RW];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int H = a.H, I = a.I;
   const int r0 = bx * RW;
   const RecLayout L = rec_layout(F, H, I);
@@ -92,64 +113,52 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
   float acc[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) acc[r] = 0.f;
-  uint32_t cur[RW][NJ][NW], nxt[RW][NJ][NW];
-  auto load_expert = [&](int slot, uint32_t (&dst)[RW][NJ][NW]) {
-    const uint8_t* wd = a.slots + (size_t)slot * a.stride + L.wd;
+  const int T = a.T;
+
+  // h, token and router weight of CSR position q
+  auto load_pair = [&](int q, float (&hv)[NJ][CV2], int& t, float& wq) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = lane + kWave * j;
+      if (c < nch) {
+#pragma unroll
+        for (int v = 0; v < CV2; v += 4) {
+          const float4 f = *(const float4*)(a.h + (size_t)q * I + c * CV2 + v);
+          hv[j][v] = f.x; hv[j][v + 1] = f.y; hv[j][v + 2] = f.z; hv[j][v + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < CV2; ++v) hv[j][v] = 0.f;
+      }
+    }
+    t = T == 1 ? 0 : a.pair_list[q] / a.k;  // one token: every pair is token 0's
+    wq = a.pair_w[q];
+  };
+  // everything an expert's first pair needs, from its slot and CSR position
+  auto load_stage = [&](int slot, int p0, Stage& s) {
+    const uint8_t* rec = a.slots + (size_t)slot * a.stride;
+    const uint8_t* wd = rec + L.wd;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int row = min(r0 + r, H - 1);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int c = lane + kWave * j;
-        if (c < nch) load_w2<F>(wd + (size_t)row * row_bytes + (size_t)c * CB2, dst[r][j]);
+        if (c < nch) load_w2<F>(wd + (size_t)row * row_bytes + (size_t)c * CB2, s.w[r][j]);
         else {
 #pragma unroll
-          for (int n = 0; n < NW; ++n) dst[r][j][n] = 0u;
+          for (int n = 0; n < NW; ++n) s.w[r][j][n] = 0u;
         }
       }
     }
-  };
-  // The final value of each (token, row) this thread stores (at most one: T *
-  // RW <= 256 < 512 threads): its previous out and x_res values are loaded now,
-  // so their latency overlaps the weight stream instead of ending the kernel.
-  const int T = a.T;
-  const int my_t = threadIdx.x / RW, my_r = threadIdx.x % RW;
-  const bool mine = (int)threadIdx.x < T * RW && r0 + my_r < H;
-  // The slot of this wavefront's first expert is read with the step's expert
-  // count (one round trip ahead of the weight loads instead of two); the
-  // position is clamped into the array and the value is used only when the
-  // expert exists.
-  int slot_cur = a.order_slot[min(a.o_lo + wid, a.E - 1)];
-  // device-resolved steps: the step's distinct experts D, read on the device
-  const int D = a.n_dev ? *a.n_dev : a.o_lo + a.n_exp;
-  const bool res = a.x_res && (!a.res_last || (a.o_lo < D && D <= a.o_lo + a.n_exp));
-  float o_prev = 0.f;
-  uint32_t x_prev = 0;
-  if (mine) {
-    if (a.accumulate) o_prev = a.out[(size_t)my_t * H + r0 + my_r];
-    if (res) x_prev = a.x_res[(size_t)my_t * H + r0 + my_r];
-  }
-  const int n_exp = min(a.n_exp, D - a.o_lo);  // none past the step's last expert
-  if (wid < n_exp) load_expert(slot_cur, cur);
-  for (int e = wid; e < n_exp; e += 8) {
-    int slot_nxt = 0;
-    if (e + 8 < n_exp) {
-      slot_nxt = a.order_slot[a.o_lo + e + 8];
-      load_expert(slot_nxt, nxt);
-    }
-    const int o = a.o_lo + e;
-    const uint8_t* rec = a.slots + (size_t)slot_cur * a.stride;
-    float sc[RW][NJ], zc[RW][NJ];
     if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
-      const float* sd = (const float*)(rec + L.sd);
+      const uint32_t* sd = (const uint32_t*)(rec + L.sd);
       const int nb = I / 128;
 #pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int c = min(lane + kWave * j, nch - 1);
-          sc[r][j] = sd[(min(r0 + r, H - 1) / 128) * nb + (c * CV2) / 128];
-        }
+      for (int j = 0; j < NJ; ++j) {
+        const int c = min(lane + kWave * j, nch - 1);
+        s.sc[0][j] = sd[(min(r0, H - 1) / 128) * nb + (c * CV2) / 128];
+      }
     } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
       const uint16_t* sd = (const uint16_t*)(rec + L.sd);
       const uint16_t* zd = (const uint16_t*)(rec + L.zd);
@@ -160,8 +169,7 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
         for (int j = 0; j < NJ; ++j) {
           const int g = min(lane + kWave * j, nch - 1) * CV2 / 128;
           const size_t row = (size_t)min(r0 + r, H - 1);
-          sc[r][j] = half_to_float(sd[row * ng + g]);
-          zc[r][j] = half_to_float(zd[row * ng + g]);
+          s.sc[r][j] = (uint32_t)sd[row * ng + g] | ((uint32_t)zd[row * ng + g] << 16);
         }
     } else if constexpr (F == MOE_FMT_MXFP4_B32) {
       const uint8_t* sd = rec + L.sd;  // one scale byte per 32 weights = 4 chunks
@@ -171,66 +179,103 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int c = min(lane + kWave * j, nch - 1);
-          sc[r][j] = e8m0_to_float(sd[(size_t)min(r0 + r, H - 1) * nb + (c * CV2) / 32]);
+          s.sc[r][j] = sd[(size_t)min(r0 + r, H - 1) * nb + (c * CV2) / 32];
         }
     }
-    // one token: every expert has exactly one pair, at CSR position o
-    const int p0 = a.T == 1 ? o : a.pair_off[o], p1 = a.T == 1 ? o + 1 : a.pair_off[o + 1];
-    for (int q = p0; q < p1; ++q) {
-      const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
-      const float wq = a.pair_w[q];
-      float hv[NJ][CV2];
+    load_pair(p0, s.hv, s.t, s.wq);
+  };
+  // one pair: the RW rows dotted with its h, reduced over the wavefront and
+  // added, times the router weight, into token t's lane
+  auto do_pair = [&](Stage& s) {
+    float hsum[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      hsum[j] = 0.f;
+      if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+#pragma unroll
+        for (int v = 0; v < CV2; ++v) hsum[j] += s.hv[j][v];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float y = 0.f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int c = lane + kWave * j;
-        if (c < nch) {
+        const float hs = hsum[j];
+        float unused = 0.f;
 #pragma unroll
-          for (int v = 0; v < CV2; v += 4) {
-            const float4 f = *(const float4*)(a.h + (size_t)q * I + c * CV2 + v);
-            hv[j][v] = f.x; hv[j][v + 1] = f.y; hv[j][v + 2] = f.z; hv[j][v + 3] = f.w;
-          }
+        for (int n = 0; n < NW; ++n)  // no hoisting of conversions (as in the up kernel)
+          asm volatile("" : "+v"(s.w[r][j][n]));
+        const float d = dot2<F>(s.w[r][j], s.hv[j], &unused);
+        if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
+          y = fmaf(d, __uint_as_float(s.sc[0][j]), y);
+        } else if constexpr (F == MOE_FMT_MXFP4_B32) {
+          y = fmaf(d, e8m0_to_float((uint8_t)s.sc[r][j]), y);
+        } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
+          const float sv = half_to_float((uint16_t)s.sc[r][j]), zv = half_to_float((uint16_t)(s.sc[r][j] >> 16));
+          y = fmaf(sv, d - zv * hs, y);
         } else {
-#pragma unroll
-          for (int v = 0; v < CV2; ++v) hv[j][v] = 0.f;
+          y += d;
         }
       }
-      float hsum[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        hsum[j] = 0.f;
-        if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
-#pragma unroll
-          for (int v = 0; v < CV2; ++v) hsum[j] += hv[j][v];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        float y = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const float hs = hsum[j];
-          float unused = 0.f;
-#pragma unroll
-          for (int n = 0; n < NW; ++n)  // no hoisting of conversions (as in the up kernel)
-            asm volatile("" : "+v"(cur[r][j][n]));
-          const float d = dot2<F>(cur[r][j], hv[j], &unused);
-          if constexpr (F == MOE_FMT_FP8_E4M3_B128 || F == MOE_FMT_MXFP4_B32) y = fmaf(d, sc[r][j], y);
-          else if constexpr (F == MOE_FMT_INT4_ASYM_G128) y = fmaf(sc[r][j], d - zc[r][j] * hs, y);
-          else y += d;
-        }
-        y = wave_sum(y);
-        if (lane == t) acc[r] = fmaf(wq, y, acc[r]);
-      }
+      y = wave_sum(y);
+      if (lane == s.t) acc[r] = fmaf(s.wq, y, acc[r]);
     }
-    if (e + 8 < n_exp) {
+  };
+
+  // Expert i of this wavefront (wave-order position o_lo + wid + 8 i): its
+  // slot and CSR pair range [p0, p1) in lane i % 64 of register i / 64 (a
+  // wave holds at most MOE_MAX_EXPERTS = 1024 experts, 128 per wavefront).
+  // Positions are clamped into the launch's range, whose entries the arrays
+  // hold; the values of positions past the step's last expert are never
+  // used. One token: expert o's one pair is at o.
+  const int pos_max = max(min(a.o_lo + a.n_exp, a.E) - 1, 0);
+  int m_slot[2] = {0, 0}, m_p0[2] = {0, 0}, m_p1[2] = {0, 0};
 #pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int n = 0; n < NW; ++n) cur[r][j][n] = nxt[r][j][n];
-      slot_cur = slot_nxt;
+  for (int c = 0; c < 2; ++c) {
+    if (c == 1 && a.n_exp <= 8 * kWave) break;  // uniform
+    const int pos = min(a.o_lo + wid + 8 * (c * kWave + lane), pos_max);
+    m_slot[c] = a.order_slot[pos];
+    if (T == 1) {
+      m_p0[c] = pos;
+      m_p1[c] = pos + 1;
+    } else {
+      m_p0[c] = a.pair_off[pos];
+      m_p1[c] = a.pair_off[pos + 1];
     }
+  }
+  auto meta = [&](const int (&m)[2], int i) {
+    return __builtin_amdgcn_readlane((i >> 6) ? m[1] : m[0], i & (kWave - 1));
+  };
+  // The final value of each (token, row) this thread stores (at most one: T *
+  // RW <= 256 < 512 threads): its previous out and x_res values are loaded now,
+  // so their latency overlaps the weight stream instead of ending the kernel.
+  const int my_t = threadIdx.x / RW, my_r = threadIdx.x % RW;
+  const bool mine = (int)threadIdx.x < T * RW && r0 + my_r < H;
+  // device-resolved steps: the step's distinct experts D, read on the device
+  // (in the same round trip as the metadata above)
+  const int D = a.n_dev ? *a.n_dev : a.o_lo + a.n_exp;
+  const bool res = a.x_res && (!a.res_last || (a.o_lo < D && D <= a.o_lo + a.n_exp));
+  float o_prev = 0.f;
+  uint32_t x_prev = 0;
+  if (mine) {
+    if (a.accumulate) o_prev = a.out[(size_t)my_t * H + r0 + my_r];
+    if (res) x_prev = a.x_res[(size_t)my_t * H + r0 + my_r];
+  }
+  const int n_exp = min(a.n_exp, D - a.o_lo);  // none past the step's last expert
+  Stage cur, nxt;
+  if (wid < n_exp) load_stage(meta(m_slot, 0), meta(m_p0, 0), cur);
+  int i = 0;
+  for (int e = wid; e < n_exp; e += 8, ++i) {
+    const int p0 = meta(m_p0, i), p1 = meta(m_p1, i);
+    if (MULTI && e + 8 < n_exp) load_stage(meta(m_slot, i + 1), meta(m_p0, i + 1), nxt);
+    if (p1 > p0) do_pair(cur);
+    for (int q = p0 + 1; q < p1; ++q) {  // later pairs, into the first's registers
+      load_pair(q, cur.hv, cur.t, cur.wq);
+      do_pair(cur);
+    }
+    if (!MULTI) break;  // the launch holds at most 8 experts: one per wavefront
+    if (e + 8 < n_exp) cur = nxt;
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r) part[wid][lane][r] = acc[r];
@@ -252,9 +297,9 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
   }
 }
 
-template <int F, int NJ, int RW>
+template <int F, int NJ, int RW, bool MULTI>
 __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
-  ffn_down_body<F, NJ, RW>(a, blockIdx.x);
+  ffn_down_body<F, NJ, RW, MULTI>(a, blockIdx.x);
 }
 
 // The down launch of a stack step with lookahead: workgroups 0 .. kCopyBlocks-1
@@ -263,7 +308,7 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
 // run this layer's down projection exactly as ffn_down_kernel does.
 constexpr int kCopyBlocks = 64;
 
-template <int F, int NJ, int RW>
+template <int F, int NJ, int RW, bool MULTI>
 __global__ __launch_bounds__(512) void down_copy_next_kernel(FfnArgs a, NextStep n) {
   const int b = blockIdx.x;
   if (b < kCopyBlocks) {
@@ -276,7 +321,7 @@ __global__ __launch_bounds__(512) void down_copy_next_kernel(FfnArgs a, NextStep
     }
     return;
   }
-  ffn_down_body<F, NJ, RW>(a, b - kCopyBlocks);
+  ffn_down_body<F, NJ, RW, MULTI>(a, b - kCopyBlocks);
 }
 
 // output rows per down workgroup, chosen by measurement
@@ -299,38 +344,48 @@ hipError_t up_dispatch(const FfnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int F>
-hipError_t down_copy_dispatch(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+// The down kernels come in two variants: launches of at most 8 experts (one
+// per wavefront: no prefetch of a next expert, fewer registers) and larger ones.
+template <int F, bool MULTI>
+hipError_t down_copy_dispatch_m(const FfnArgs& a, const NextStep& n, hipStream_t s) {
   constexpr int kRW = rw<F>();
   const int nj = (a.I / Fmt<F>::CV2 + kWave - 1) / kWave;
   const dim3 grid(kCopyBlocks + (a.H + kRW - 1) / kRW), block(512);
   switch (nj) {
-    case 1: launch_k(down_copy_next_kernel<F, 1, kRW>, grid, block, s, a.ev0, a.ev1, a, n); break;
-    case 2: launch_k(down_copy_next_kernel<F, 2, kRW>, grid, block, s, a.ev0, a.ev1, a, n); break;
-    case 3: launch_k(down_copy_next_kernel<F, 3, kRW>, grid, block, s, a.ev0, a.ev1, a, n); break;
-    case 4: launch_k(down_copy_next_kernel<F, 4, kRW>, grid, block, s, a.ev0, a.ev1, a, n); break;
-    case 6: launch_k(down_copy_next_kernel<F, 6, kRW>, grid, block, s, a.ev0, a.ev1, a, n); break;
-    case 8: launch_k(down_copy_next_kernel<F, 8, kRW>, grid, block, s, a.ev0, a.ev1, a, n); break;
+    case 1: launch_k(down_copy_next_kernel<F, 1, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a, n); break;
+    case 2: launch_k(down_copy_next_kernel<F, 2, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a, n); break;
+    case 3: launch_k(down_copy_next_kernel<F, 3, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a, n); break;
+    case 4: launch_k(down_copy_next_kernel<F, 4, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a, n); break;
+    case 6: launch_k(down_copy_next_kernel<F, 6, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a, n); break;
+    case 8: launch_k(down_copy_next_kernel<F, 8, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a, n); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-
 template <int F>
-hipError_t down_dispatch(const FfnArgs& a, hipStream_t s) {
+hipError_t down_copy_dispatch(const FfnArgs& a, const NextStep& n, hipStream_t s) {
+  return a.n_exp > 8 ? down_copy_dispatch_m<F, true>(a, n, s) : down_copy_dispatch_m<F, false>(a, n, s);
+}
+
+template <int F, bool MULTI>
+hipError_t down_dispatch_m(const FfnArgs& a, hipStream_t s) {
   constexpr int kRW = rw<F>();
   const int nj = (a.I / Fmt<F>::CV2 + kWave - 1) / kWave;
   const dim3 grid((a.H + kRW - 1) / kRW), block(512);
   switch (nj) {
-    case 1: launch_k(ffn_down_kernel<F, 1, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
-    case 2: launch_k(ffn_down_kernel<F, 2, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
-    case 3: launch_k(ffn_down_kernel<F, 3, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
-    case 4: launch_k(ffn_down_kernel<F, 4, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
-    case 6: launch_k(ffn_down_kernel<F, 6, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
-    case 8: launch_k(ffn_down_kernel<F, 8, kRW>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 1: launch_k(ffn_down_kernel<F, 1, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 2: launch_k(ffn_down_kernel<F, 2, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 3: launch_k(ffn_down_kernel<F, 3, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 4: launch_k(ffn_down_kernel<F, 4, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 6: launch_k(ffn_down_kernel<F, 6, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a); break;
+    case 8: launch_k(ffn_down_kernel<F, 8, kRW, MULTI>, grid, block, s, a.ev0, a.ev1, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <int F>
+hipError_t down_dispatch(const FfnArgs& a, hipStream_t s) {
+  return a.n_exp > 8 ? down_dispatch_m<F, true>(a, s) : down_dispatch_m<F, false>(a, s);
 }
 
 // ------------------------------------------------------------------ dequant
