@@ -227,8 +227,15 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
   // the count's test). The slot's position is clamped into the array and its
   // value used only when the expert exists; without a device count the read
   // goes to the slot map and is ignored.
+  // Several tokens: the expert's CSR pair range is read in the same round
+  // trip (one token: its one pair is at position o).
   int slot = a.order_slot[min(o, a.E - 1)];
   int nd = *(a.n_dev ? a.n_dev : a.order_slot);
+  int p0 = o, p1 = o + 1;
+  if (a.T > 1) {
+    p0 = a.pair_off[min(o, a.E - 1)];
+    p1 = a.pair_off[min(o, a.E - 1) + 1];
+  }
   asm volatile("" : "+s"(slot), "+s"(nd));
   if (a.n_dev && by >= nd - a.o_lo) return;  // device-resolved count: uniform per block
   const uint8_t* rec = a.slots + (size_t)slot * a.stride;
@@ -298,14 +305,17 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
     }
   }
 
-  // one token: every expert has exactly one pair, at CSR position o
-  const int p0 = a.T == 1 ? o : a.pair_off[o], p1 = a.T == 1 ? o + 1 : a.pair_off[o + 1];
+  // the token of each of the expert's pairs (at most one per token, so at
+  // most 64), pair p0 + i in lane i, read beside the weights; one token: 0
+  int tq = 0;
+  if (a.T > 1 && lane < p1 - p0) tq = a.pair_list[p0 + lane] / a.k;
+  auto token_of = [&](int q) { return a.T == 1 ? 0 : __builtin_amdgcn_readlane(tq, q - p0); };
   const XT* xbase = (const XT*)a.x;
   if constexpr (F == MOE_FMT_BF16 && sizeof(XT) == 2) {
     // bf16 weights and activations: dot the packed pairs directly (8 values
     // per 16-byte chunk in 4 words), activations never widened to fp32
     for (int q = p0; q < p1; ++q) {
-      const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
+      const int t = token_of(q);
       if (q > p0) __syncthreads();  // the previous pair's reads of xs are done
       for (int c = threadIdx.x; c < nx16; c += 4 * kWave)
         xs[c] = ((const uint4*)(xbase + (size_t)t * H))[c];
@@ -339,8 +349,7 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
     return;
   }
   for (int q = p0; q < p1; ++q) {
-    // with one token every pair is token 0: no dependent pair-list load
-    const int t = a.T == 1 ? 0 : a.pair_list[q] / a.k;
+    const int t = token_of(q);
     if (q > p0) __syncthreads();  // the previous pair's reads of xs are done
     for (int c = threadIdx.x; c < nx16; c += 4 * kWave) xs[c] = ((const uint4*)(xbase + (size_t)t * H))[c];
     __syncthreads();
