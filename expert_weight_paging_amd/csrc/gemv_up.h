@@ -429,11 +429,12 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
   }
 }
 
-// h rows per wavefront (up), chosen by measurement on the 128-expert layer
-// (8 experts per launch): two h rows per wavefront for the 4- and 8-bit
-// formats, one for bf16 and f32.
+// h rows per wavefront (up), chosen by measurement on the cache-cold batch-1
+// layer (8 experts per launch): two for int4 (6.4 against 6.8 us with one),
+// one for the other formats (MXFP4 7.0 against 7.2 us with two, FP8 7.24
+// against 7.30).
 template <int F> constexpr int rpw() {
-  return (F == MOE_FMT_INT4_ASYM_G128 || F == MOE_FMT_MXFP4_B32 || F == MOE_FMT_FP8_E4M3_B128) ? 2 : 1;
+  return F == MOE_FMT_INT4_ASYM_G128 ? 2 : 1;
 }
 
 }  // namespace gemv
