@@ -72,6 +72,42 @@ def test_largest_e_and_top_k():
     p.close()
 
 
+def test_gemv_launch_past_512_experts():
+    """A GEMV wave of about 650 distinct experts (E = K = 1024, 32 tokens of
+    top-32): each down wavefront takes more than 64 experts, so the kernel's
+    per-lane expert metadata needs its second register; ties included."""
+    E, k, T = 1024, 32, 32
+    say("case: E=K=1024 k=32 B=32, one wave of ~650 experts")
+    p = PairedLayer(E, k, 64, 32, E, gen.F32, _tiny_fill(E, 64, 32, seed=11), max_tokens=T)
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((3, T, E)).astype(np.float32)
+    logits[:, :, :40] = np.round(logits[:, :, :40])
+    x = rng.standard_normal((3, T, 64)).astype(np.float32)
+    seen = []
+
+    def count(pl, t, info):
+        seen.append((info["num_distinct"], info["num_hits"]))
+    p.run(logits, x, check_state_every=1, on_step=count)
+    # the first step (cold table) is one launch of all its experts
+    assert seen[0][1] == 0 and seen[0][0] > 8 * 64, seen
+    p.close()
+
+
+@pytest.mark.parametrize("fmt", [gen.F32, gen.FP8, gen.INT4])
+def test_one_token_more_than_8_experts(fmt):
+    """One token of top-16: 16 experts in one launch, two per down wavefront
+    (the kernel variant that prefetches the next expert), on one token."""
+    E, k, K, H, I = 64, 16, 32, 256, 128
+    say("case: E=64 k=16 K=32 B=1 fmt=%d" % fmt)
+    p = PairedLayer(E, k, H, I, K, fmt, _tiny_fill(E, H, I, fmt=fmt, seed=13), max_tokens=1)
+    rng = np.random.default_rng(14)
+    logits = rng.standard_normal((12, 1, E)).astype(np.float32)
+    v = rng.standard_normal((12, 1, H)).astype(np.float32)
+    x = v if fmt == gen.F32 else gen.f32_to_bf16_bits(v)
+    p.run(logits, x, check_state_every=4)
+    p.close()
+
+
 def test_separate_streams_and_nan_canary():
     """Compute, copy and route on three streams; before each page-in the victim
     slots are filled with NaN on the copy stream. A forward that read a slot
