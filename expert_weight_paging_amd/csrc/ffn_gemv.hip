@@ -47,7 +47,10 @@ __device__ inline void load_w2(const uint8_t* p, uint32_t* w) {
   }
 }
 
-template <int F>
+// BYTES (int4): convert the codes from even and odd nibble bytes (one
+// instruction per code, two more registers) instead of one bit-field
+// extract and conversion per code; the same products in the same order.
+template <int F, bool BYTES>
 __device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
   float acc = 0.f;
   if constexpr (F == MOE_FMT_F32) {
@@ -66,6 +69,15 @@ __device__ inline float dot2(const uint32_t* w, const float* h, float* hsum) {
     acc = fmaf(b.y, h[3], acc);
   } else if constexpr (F == MOE_FMT_MXFP4_B32) {
     acc = dot_e2m1x8(w[0], h, acc);
+  } else if constexpr (BYTES) {
+    // int4 codes in index order (the low nibble of byte b is code 2b)
+    uint32_t ev = w[0] & 0x0F0F0F0Fu, od = (w[0] >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(ev), "+v"(od));  // keeps the byte conversions (not a bit-field extract per code)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc = fmaf((float)((ev >> (8 * b)) & 0xFFu), h[2 * b], acc);
+      acc = fmaf((float)((od >> (8 * b)) & 0xFFu), h[2 * b + 1], acc);
+    }
   } else {
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc = fmaf((float)((w[0] >> (4 * n)) & 0xFu), h[n], acc);
@@ -206,7 +218,7 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
 #pragma unroll
         for (int n = 0; n < NW; ++n)  // no hoisting of conversions (as in the up kernel)
           asm volatile("" : "+v"(s.w[r][j][n]));
-        const float d = dot2<F>(s.w[r][j], s.hv[j], &unused);
+        const float d = dot2<F, !MULTI>(s.w[r][j], s.hv[j], &unused);  // the prefetching variant keeps its registers
         if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
           y = fmaf(d, __uint_as_float(s.sc[0][j]), y);
         } else if constexpr (F == MOE_FMT_MXFP4_B32) {
