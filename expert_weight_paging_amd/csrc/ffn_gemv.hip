@@ -218,11 +218,13 @@ __device__ __forceinline__ void ffn_down_body(const FfnArgs& a, int bx) {
 #pragma unroll
         for (int n = 0; n < NW; ++n)  // no hoisting of conversions (as in the up kernel)
           asm volatile("" : "+v"(s.w[r][j][n]));
+        if constexpr (F == MOE_FMT_MXFP4_B32) {  // the scale applied by the conversions
+          y += dot_e2m1x8_scaled(s.w[r][j][0], s.hv[j], e8m0_to_float((uint8_t)s.sc[r][j]), 0.f);
+          continue;
+        }
         const float d = dot2<F, !MULTI>(s.w[r][j], s.hv[j], &unused);  // the prefetching variant keeps its registers
         if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
           y = fmaf(d, __uint_as_float(s.sc[0][j]), y);
-        } else if constexpr (F == MOE_FMT_MXFP4_B32) {
-          y = fmaf(d, e8m0_to_float((uint8_t)s.sc[r][j]), y);
         } else if constexpr (F == MOE_FMT_INT4_ASYM_G128) {
           const float sv = half_to_float((uint16_t)s.sc[r][j]), zv = half_to_float((uint16_t)(s.sc[r][j] >> 16));
           y = fmaf(sv, d - zv * hs, y);

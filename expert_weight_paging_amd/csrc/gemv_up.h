@@ -101,6 +101,28 @@ __device__ inline float dot_e2m1x8(uint32_t w, const float* x, float acc) {
   return acc;
 }
 
+// The same sum with the block's E8M0 scale s = 2^(e - 127) applied by the
+// conversion (gfx950 v_cvt_scalef32_pk_f32_fp4: selector b converts byte b,
+// low nibble first, and multiplies by 2 to the exponent of its f32 scale
+// operand, exactly): codes times s, in index order. In the normal range each
+// step is the unscaled step times s, so the result is the raw sum times s,
+// bit for bit.
+__device__ inline float dot_e2m1x8_scaled(uint32_t w, const float* x, float s, float acc) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
+  acc = fmaf(a.x, x[0], acc);
+  acc = fmaf(a.y, x[1], acc);
+  acc = fmaf(b.x, x[2], acc);
+  acc = fmaf(b.y, x[3], acc);
+  acc = fmaf(c.x, x[4], acc);
+  acc = fmaf(c.y, x[5], acc);
+  acc = fmaf(d.x, x[6], acc);
+  acc = fmaf(d.y, x[7], acc);
+  return acc;
+}
+
 // Load CV1 activations starting at column col, as float.
 template <int F, typename XT>
 __device__ inline void load_x(const XT* x, int col, float* v) {
@@ -407,10 +429,23 @@ __device__ __forceinline__ void ffn_up_body(const FfnArgs& a, int bx, int by) {
           g = fmaf(sg[r][j], dg - (zg[r][j] + 128.f) * xp[j].sum, g);
           u = fmaf(su[r][j], du - (zu[r][j] + 128.f) * xp[j].sum, u);
         } else {
+          if constexpr (F == MOE_FMT_MXFP4_B32) {  // scales applied by the conversions
+            const uint32_t gv[4] = {wg[r][j].x, wg[r][j].y, wg[r][j].z, wg[r][j].w};
+            const uint32_t uv[4] = {wu[r][j].x, wu[r][j].y, wu[r][j].z, wu[r][j].w};
+            float dg = 0.f, du = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              dg = dot_e2m1x8_scaled(gv[i], xv[j] + 8 * i, sg[r][j], dg);
+              du = dot_e2m1x8_scaled(uv[i], xv[j] + 8 * i, su[r][j], du);
+            }
+            g += dg;
+            u += du;
+            continue;
+          }
           float xs = 0.f;
           const float dg = dot1<F>(wg[r][j], xv[j], &xs);
           const float du = dot1<F>(wu[r][j], xv[j], &xs);
-          if constexpr (F == MOE_FMT_FP8_E4M3_B128 || F == MOE_FMT_MXFP4_B32) {
+          if constexpr (F == MOE_FMT_FP8_E4M3_B128) {
             g = fmaf(dg, sg[r][j], g);
             u = fmaf(du, su[r][j], u);
           } else {
