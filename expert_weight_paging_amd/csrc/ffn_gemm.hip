@@ -81,17 +81,20 @@ __device__ inline bf16x8 fp8x8_to_bf16(uint2 q, float s) {
 }
 
 // Eight E2M1 codes (one word, code 2b in the low nibble of byte b) to bf16
-// operands: each exact in e4m3 and then in fp32, times the block's E8M0 scale
-// in fp32, rounded to nearest even; the same arithmetic as the decode kernels'
-// expansion of MXFP4 records.
+// operands: each code times the block's E8M0 scale s = 2^(e - 127), by
+// gfx950's scaled conversion (selector b converts byte b, low nibble first,
+// times 2 to the exponent of s). A code has at most two significant bits, so
+// the product is exact in bf16: the same values as the expansion of MXFP4
+// records (exact product in fp32, rounded to nearest even).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline bf16x8 fp4x8_to_bf16(uint32_t q, float s) {
-  uint32_t ev, od;
-  gemv::e2m1x8_to_e4m3(q, &ev, &od);
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 3);
   bf16x8 r;
-  r[0] = (__bf16)(a.x * s); r[1] = (__bf16)(c.x * s); r[2] = (__bf16)(a.y * s); r[3] = (__bf16)(c.y * s);
-  r[4] = (__bf16)(b.x * s); r[5] = (__bf16)(d.x * s); r[6] = (__bf16)(b.y * s); r[7] = (__bf16)(d.y * s);
+  r[0] = a.x; r[1] = a.y; r[2] = b.x; r[3] = b.y;
+  r[4] = c.x; r[5] = c.y; r[6] = d.x; r[7] = d.y;
   return r;
 }
 
